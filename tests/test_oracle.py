@@ -1,0 +1,230 @@
+"""Pins for the CPU oracle, each against something other than the oracle itself:
+closed forms from the pages' generator, a hand-derived worked example, the
+pages' printed tile_dot values, finite differences, identities that hold at any
+size, special cases with a textbook answer, and an independent algorithm."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from golden.fixtures import load
+
+
+# ---------------------------------------------------------------- forward ----
+
+@pytest.mark.parametrize("n", [2, 16, 512])
+def test_closed_form_factor_is_E(n):
+    # jaxmg docs, "Cholesky factorization": A = E E^T must factor to E.
+    A, E = workloads.closed_form(n)
+    L, info = oracle.potrf(A)
+    assert info == 0
+    assert np.max(np.abs(L - E)) <= 1e-14
+    # entries off the two bands are exactly zero (and so is the strict upper triangle)
+    band = np.tril(np.ones((n, n), bool)) & ~np.tril(np.ones((n, n), bool), -2)
+    assert np.all(L[~band] == 0.0)
+
+
+def test_n2_worked_example_forward_exact():
+    g = load("n2_worked_example.txt")
+    L, info = oracle.potrf(g["A"].reshape(2, 2))
+    assert info == 0
+    assert np.array_equal(L, g["L"].reshape(2, 2))
+
+
+def test_n2_generator_matches_fixture():
+    A, E = workloads.closed_form(2)
+    g = load("n2_worked_example.txt")
+    assert np.array_equal(A, g["A"].reshape(2, 2))
+    assert np.array_equal(E, g["L"].reshape(2, 2))
+
+
+@pytest.mark.parametrize("n,seed", [(1, 3), (7, 4), (64, 5), (300, 6)])
+def test_residual_random_spd(n, seed):
+    A = workloads.gram_spd(n, seed=seed, shift=1.0)
+    L, info = oracle.potrf(A)
+    assert info == 0
+    assert np.all(np.triu(L, 1) == 0.0)
+    assert np.all(np.diag(L) > 0)
+    res = np.linalg.norm(L @ L.T - A) / np.linalg.norm(A)
+    assert res <= 1e-13
+
+
+def test_diagonal_matrix_gives_sqrt_exactly():
+    d = np.array([4.0, 2.0, 9.0, 1e-300, 3.5, 1e300])
+    L, info = oracle.potrf(np.diag(d))
+    assert info == 0
+    assert np.array_equal(L, np.diag(np.sqrt(d)))
+
+
+def test_scalar_case():
+    L, info = oracle.potrf(np.array([[6.25]]))
+    assert info == 0 and L[0, 0] == 2.5
+
+
+def test_only_lower_triangle_is_read():
+    A = workloads.gram_spd(20, seed=7)
+    B = A.copy()
+    B[np.triu_indices(20, 1)] = np.nan
+    La, _ = oracle.potrf(A)
+    Lb, _ = oracle.potrf(B)
+    assert np.array_equal(La, Lb)
+
+
+@pytest.mark.parametrize("n", [3, 17, 64])
+def test_matches_numpy_cholesky(n):
+    # third-party sanity check (LAPACK through NumPy), forward only
+    A = workloads.gram_spd(n, seed=11, shift=0.5)
+    L, info = oracle.potrf(A)
+    assert info == 0
+    ref = np.linalg.cholesky(A)
+    assert np.max(np.abs(L - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("n,col,val", [(6, 3, -1.0), (6, 0, 0.0), (5, 4, np.nan), (9, 8, -2.0)])
+def test_info_first_failing_column(n, col, val):
+    A = workloads.spd_with_bad_pivot(n, col, val)
+    _, info = oracle.potrf(A)
+    assert info == col + 1
+
+
+def test_info_exact_zero_pivot():
+    _, info = oracle.potrf(np.array([[1.0, 1.0], [1.0, 1.0]]))
+    assert info == 2
+
+
+def test_batched_equals_single():
+    A = workloads.batched_spd(9, 12, seed=2, dtype=np.float64)
+    A[4, 5, 5] = -3.0
+    Lb, info = oracle.potrf(A)
+    for b in range(9):
+        L1, i1 = oracle.potrf(A[b])
+        assert i1 == info[b]
+        if i1 == 0:
+            assert np.array_equal(L1, Lb[b])
+    assert info[4] == 6 and np.count_nonzero(info) == 1
+
+
+# ---------------------------------------------------------------- adjoint ----
+
+def _f(A, adjL):
+    L, info = oracle.potrf(A)
+    assert info == 0
+    return float(np.sum(np.tril(adjL) * L))
+
+
+@pytest.mark.parametrize("n,seed", [(1, 0), (2, 1), (5, 2), (8, 3)])
+def test_adjoint_central_finite_differences(n, seed):
+    # f(A) = <adj_L, chol(A)>; perturb each lower entry the forward reads.
+    A = workloads.gram_spd(n, seed=seed, shift=1.0)
+    adjL = workloads.lower_normal(n, seed=seed + 100)
+    L, _ = oracle.potrf(A)
+    G = oracle.potrf_adjoint(L, adjL)
+    fd = np.zeros_like(A)
+    for i in range(n):
+        for j in range(i + 1):
+            h = 1e-5 * max(1.0, abs(A[i, j]))
+            Ap = A.copy(); Ap[i, j] += h
+            Am = A.copy(); Am[i, j] -= h
+            fd[i, j] = (_f(Ap, adjL) - _f(Am, adjL)) / (2 * h)
+    scale = max(1.0, np.max(np.abs(fd)))
+    assert np.max(np.abs(np.tril(G) - fd)) <= 1e-7 * scale
+    assert np.all(np.triu(G, 1) == 0.0)
+
+
+@pytest.mark.parametrize("key,pos", [("G_e00", (0, 0)), ("G_e10", (1, 0)), ("G_e11", (1, 1))])
+def test_n2_worked_example_adjoint_exact(key, pos):
+    g = load("n2_worked_example.txt")
+    L = g["L"].reshape(2, 2)
+    adjL = np.zeros((2, 2)); adjL[pos] = 1.0
+    G = oracle.potrf_adjoint(L, adjL)
+    got = np.array([G[0, 0], G[1, 0], G[1, 1]])
+    assert np.array_equal(got, g[key])
+
+
+def test_scalar_adjoint():
+    # N = 1: L = sqrt(a), dL/da = 1 / (2 L); pins the diagonal halving of Phi.
+    G = oracle.potrf_adjoint(np.array([[2.5]]), np.array([[3.0]]))
+    assert G[0, 0] == 3.0 / 5.0
+
+
+@pytest.mark.parametrize("n", [10, 50])
+def test_adjL_equal_L_gives_half_identity(n):
+    # <L, L> = tr(A), so the gradient of (1/2)||L||^2 in the lower entries is I / 2.
+    A = workloads.gram_spd(n, seed=21)
+    L, _ = oracle.potrf(A)
+    G = oracle.potrf_adjoint(L, L)
+    assert np.max(np.abs(G - 0.5 * np.eye(n))) <= 1e-13
+
+
+@pytest.mark.parametrize("n,p,q", [(12, 7, 3), (12, 11, 0), (40, 25, 24), (40, 13, 13)])
+def test_symmetric_pair_invariant(n, p, q):
+    # adj_L = tril(2 W L), W symmetric  =>  G = Phi(2 W).  With W = e_p e_q^T + e_q e_p^T
+    # (p > q) that is 2 e_p e_q^T; with p == q and W = e_p e_p^T it is e_p e_p^T.
+    A = workloads.gram_spd(n, seed=22)
+    L, _ = oracle.potrf(A)
+    W = np.zeros((n, n))
+    W[p, q] = 1.0
+    W[q, p] = 1.0
+    adjL = np.tril(2.0 * W @ L)
+    G = oracle.potrf_adjoint(L, adjL)
+    expect = np.zeros((n, n))
+    expect[p, q] = 2.0 if p != q else 1.0
+    assert np.max(np.abs(G - expect)) <= 1e-12
+
+
+def test_adjoint_is_linear_in_adjL():
+    n = 30
+    A = workloads.gram_spd(n, seed=23)
+    L, _ = oracle.potrf(A)
+    x = workloads.lower_normal(n, seed=24)
+    y = workloads.lower_normal(n, seed=25)
+    gx = oracle.potrf_adjoint(L, x)
+    gy = oracle.potrf_adjoint(L, y)
+    gxy = oracle.potrf_adjoint(L, 2.0 * x - 3.0 * y)
+    assert np.max(np.abs(gxy - (2.0 * gx - 3.0 * gy))) <= 1e-12 * np.max(np.abs(gxy))
+
+
+def test_upper_of_adjL_ignored_and_upper_of_adjA_untouched():
+    n = 15
+    A = workloads.gram_spd(n, seed=26)
+    L, _ = oracle.potrf(A)
+    adjL = np.random.default_rng(27).standard_normal((n, n))
+    base = np.random.default_rng(28).standard_normal((n, n))
+    g1 = oracle.potrf_adjoint(L, adjL, base, accumulate=True)
+    g2 = oracle.potrf_adjoint(L, np.tril(adjL), base, accumulate=True)
+    assert np.array_equal(g1, g2)
+    assert np.array_equal(np.triu(g1, 1), np.triu(base, 1))
+    g0 = oracle.potrf_adjoint(L, adjL, base, accumulate=False)
+    assert np.array_equal(np.tril(g1), np.tril(g0) + np.tril(base)) or \
+        np.max(np.abs(np.tril(g1) - np.tril(g0) - np.tril(base))) <= 1e-13 * np.max(np.abs(g1))
+    assert np.array_equal(np.triu(g0, 1), np.triu(base, 1))
+
+
+@pytest.mark.parametrize("n,seed", [(1, 30), (9, 31), (64, 32), (256, 33)])
+def test_formula_matches_independent_sweep(n, seed):
+    A = workloads.gram_spd(n, seed=seed, shift=1.0)
+    adjL = workloads.lower_normal(n, seed=seed + 1)
+    L, _ = oracle.potrf(A)
+    g_formula = oracle.potrf_adjoint(L, adjL, method="formula")
+    g_sweep = oracle.potrf_adjoint(L, adjL, method="sweep")
+    assert np.max(np.abs(g_formula - g_sweep)) <= 1e-12 * np.max(np.abs(g_sweep))
+
+
+def test_batched_adjoint_equals_single():
+    A = workloads.batched_spd(5, 10, seed=3, dtype=np.float64)
+    adjL = workloads.lower_normal(10, seed=4, batch=5)
+    L, _ = oracle.potrf(A)
+    Gb = oracle.potrf_adjoint(L, adjL)
+    for b in range(5):
+        assert np.array_equal(Gb[b], oracle.potrf_adjoint(L[b], adjL[b]))
+
+
+# ------------------------------------------------------------- tile_dot ----
+
+def test_tile_dot_values_from_warp_1374():
+    g = load("tile_dot_warp1374.txt")
+    assert oracle.dot(g["a"], g["b"]) == g["forward"][0]
+    abar, bbar = oracle.dot_adjoint(g["a"], g["b"], 1.0)
+    assert np.array_equal(abar, g["grad_a"])
+    assert np.array_equal(bbar, g["grad_b"])
+    assert not np.array_equal(abar, g["grad_a_missing_broadcast"])

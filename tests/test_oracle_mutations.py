@@ -1,0 +1,91 @@
+"""Plant plausible mistakes in copies of the oracle's C source (CPU only) and
+check that the pins in ``test_oracle.py`` catch every one of them.  This shows
+the pins are sensitive to a dropped term, a wrong sign, a wrong index or a
+transposed operand anywhere in the oracle."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement).  Each replacement is a mistake that
+# still compiles and still produces finite numbers.
+MUTATIONS = [
+    ("fwd_pivot_sign", "d -= AT(L, ldl, j, k) * AT(L, ldl, j, k);",
+     "d += AT(L, ldl, j, k) * AT(L, ldl, j, k);"),
+    ("fwd_row_index", "s -= AT(L, ldl, i, k) * AT(L, ldl, j, k);",
+     "s -= AT(L, ldl, i, k) * AT(L, ldl, i, k);"),
+    ("fwd_no_divide", "AT(L, ldl, i, j) = s / ljj;", "AT(L, ldl, i, j) = s;"),
+    ("fwd_pivot_no_sqrt", "const double ljj = sqrt(d);", "const double ljj = d;"),
+    ("adj_M_transposed", "const double lki = AT(L, ldl, k, i);",
+     "const double lki = AT(L, ldl, i, k);"),
+    ("adj_M_uses_upper_adjL", "mrow[j] += lki * AT(adjL, ldal, k, j);",
+     "mrow[j] += lki * AT(adjL, ldal, j, k);"),
+    ("adj_phi_no_halving", "M[(size_t)i * n + i] *= 0.5;", "M[(size_t)i * n + i] *= 1.0;"),
+    ("adj_solve1_no_divide", "xi[c] = ri[c] / lii;", "xi[c] = ri[c];"),
+    ("adj_solve1_wrong_sign", "rt[c] -= lit * xi[c];", "rt[c] += lit * xi[c];"),
+    ("adj_solve1_transposed", "const double lit = AT(L, ldl, i, t);",
+     "const double lit = AT(L, ldl, t, i);"),
+    ("adj_solve2_transposed", "rr[k] -= srj * AT(L, ldl, j, k);",
+     "rr[k] -= srj * AT(L, ldl, k, j);"),
+    ("adj_solve2_no_divide", "const double srj = rr[j] / AT(L, ldl, j, j);",
+     "const double srj = rr[j];"),
+    ("adj_sym_half_offdiag", ": S[(size_t)i * n + j] + S[(size_t)j * n + i];",
+     ": 0.5 * (S[(size_t)i * n + j] + S[(size_t)j * n + i]);"),
+    ("adj_sym_lower_only", ": S[(size_t)i * n + j] + S[(size_t)j * n + i];",
+     ": S[(size_t)i * n + j];"),
+    ("adj_diag_doubled", "const double g = (i == j) ? S[(size_t)i * n + i]",
+     "const double g = (i == j) ? 2.0 * S[(size_t)i * n + i]"),
+    ("adj_overwrites_when_accumulating", "AT(adjA, ldaa, i, j) += g;", "AT(adjA, ldaa, i, j) = g;"),
+    ("dot_reversed_index", "y += a[k] * b[k];", "y += a[k] * b[n - 1 - k];"),
+    ("dot_adjoint_swapped", "abar[k] += ybar * b[k];", "abar[k] += ybar * a[k];"),
+]
+
+PINS = [
+    lambda: pins.test_closed_form_factor_is_E(16),
+    pins.test_n2_worked_example_forward_exact,
+    lambda: pins.test_residual_random_spd(64, 5),
+    pins.test_diagonal_matrix_gives_sqrt_exactly,
+    pins.test_scalar_case,
+    lambda: pins.test_adjoint_central_finite_differences(5, 2),
+    lambda: pins.test_n2_worked_example_adjoint_exact("G_e10", (1, 0)),
+    lambda: pins.test_n2_worked_example_adjoint_exact("G_e11", (1, 1)),
+    pins.test_scalar_adjoint,
+    lambda: pins.test_adjL_equal_L_gives_half_identity(10),
+    lambda: pins.test_symmetric_pair_invariant(12, 7, 3),
+    pins.test_upper_of_adjL_ignored_and_upper_of_adjA_untouched,
+    pins.test_tile_dot_values_from_warp_1374,
+]
+
+
+def _caught(lib_path):
+    with oracle._use_library(lib_path):
+        for pin in PINS:
+            try:
+                pin()
+            except Exception:  # an assertion, or any failure the mistake causes
+                return True
+    return False
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path):
+    out = tmp_path / "liboracle_copy.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                    SRC, "-o", str(out), "-lm"], check=True)
+    assert not _caught(str(out))
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(text.replace(old, new))
+    out = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                    str(src), "-o", str(out), "-lm"], check=True)
+    assert _caught(str(out)), f"no pin caught the planted mistake {name}"

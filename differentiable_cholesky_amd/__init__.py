@@ -1,0 +1,24 @@
+"""libchol: Cholesky factor A = L L^T and its reverse-mode adjoint on AMD MI355X.
+
+The computation lives in hand-written HIP kernels behind the C-ABI declared in
+``include/libchol.h``; this package only binds that library (``_lib``) and
+builds it (``build``).  Importing the package loads ``libchol.so`` and fails
+loudly if it has not been built.
+"""
+from ._lib import (  # noqa: F401
+    CHOL_F32,
+    CHOL_F64,
+    CholError,
+    MAX_NB,
+    SMALL_MAX_N,
+    chol_abi_version,
+    chol_potrf,
+    chol_potrf_adjoint,
+    chol_potrf_adjoint_batched,
+    chol_potrf_adjoint_workspace_size,
+    chol_potrf_batched,
+    chol_status_string,
+    chol_wave_dot_fwd_adj,
+    header_entry_points,
+    lib,
+)

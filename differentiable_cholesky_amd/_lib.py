@@ -1,0 +1,211 @@
+"""ctypes binding of libchol (``include/libchol.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C-ABI.  The functions named like the C entry points take
+torch tensors that live on a ROCm device and pass their device pointers,
+leading dimensions and the current torch stream.  There is no CPU fallback:
+if the library is missing or fails to load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libchol.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "libchol.h")
+
+CHOL_F32, CHOL_F64 = 0, 1
+CHOL_OK, CHOL_ERR_INVALID_VALUE, CHOL_ERR_NOT_SUPPORTED, CHOL_ERR_WORKSPACE, CHOL_ERR_HIP = range(5)
+SMALL_MAX_N = 64
+MAX_NB = 128
+
+
+class CholError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libchol.so not built at {LIB_PATH}; run `python -m differentiable_cholesky_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    st = ctypes.c_int
+    lib.chol_potrf.restype = st
+    lib.chol_potrf.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.chol_potrf_batched.restype = st
+    lib.chol_potrf_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp]
+    lib.chol_potrf_adjoint.restype = st
+    lib.chol_potrf_adjoint.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, i32, i64, vp, sz, vp]
+    lib.chol_potrf_adjoint_workspace_size.restype = st
+    lib.chol_potrf_adjoint_workspace_size.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(sz)]
+    lib.chol_potrf_adjoint_batched.restype = st
+    lib.chol_potrf_adjoint_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, vp]
+    lib.chol_wave_dot_fwd_adj.restype = st
+    lib.chol_wave_dot_fwd_adj.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, i32, vp]
+    lib.chol_status_string.restype = ctypes.c_char_p
+    lib.chol_status_string.argtypes = [st]
+    lib.chol_abi_version.restype = ctypes.c_int
+    lib.chol_abi_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def header_entry_points() -> list[str]:
+    """Names of the functions ``include/libchol.h`` declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(chol_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib.chol_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != CHOL_OK:
+        raise CholError(status, status_string(status))
+
+
+# --------------------------------------------------------------- tensors ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return CHOL_F32
+    if t.dtype == torch.float64:
+        return CHOL_F64
+    raise TypeError(f"libchol handles float32 and float64, got {t.dtype}")
+
+
+def _mat(t, name: str):
+    """(pointer, ld) of a 2-D row-major device matrix (last stride 1)."""
+    if t.dim() != 2 or t.shape[0] != t.shape[1]:
+        raise ValueError(f"{name} must be a square 2-D tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return ctypes.c_void_p(t.data_ptr()), max(int(t.stride(0)), int(t.shape[0]), 1)
+
+
+def _bat(t, name: str):
+    """(pointer, ld, stride) of a [batch, n, n] row-major device array."""
+    if t.dim() != 3 or t.shape[1] != t.shape[2]:
+        raise ValueError(f"{name} must be [batch, n, n]")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    n = int(t.shape[1])
+    ld = max(int(t.stride(1)), n, 1)
+    stride = int(t.stride(0)) if t.shape[0] > 1 else ld * n
+    return ctypes.c_void_p(t.data_ptr()), ld, stride
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def chol_potrf(A, L=None, info=None, nb: int = 0, stream=None):
+    """Factor one SPD matrix: returns (L, info).  ``L`` may be ``A`` (in place)."""
+    torch = _torch()
+    if L is None:
+        L = torch.empty_like(A)
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=A.device)
+    pa, lda = _mat(A, "A")
+    pl, ldl = _mat(L, "L")
+    _check(lib.chol_potrf(_dtype_code(A), A.shape[0], pa, lda, pl, ldl, ctypes.c_void_p(info.data_ptr()),
+                          nb, _stream(stream)))
+    return L, info
+
+
+def chol_potrf_batched(A, L=None, info=None, stream=None):
+    """Factor [batch, n, n] SPD matrices (n <= 64): returns (L, info[batch])."""
+    torch = _torch()
+    if L is None:
+        L = torch.empty_like(A)
+    if info is None:
+        info = torch.empty(A.shape[0], dtype=torch.int32, device=A.device)
+    pa, lda, sa = _bat(A, "A")
+    pl, ldl, sl = _bat(L, "L")
+    _check(lib.chol_potrf_batched(_dtype_code(A), A.shape[1], A.shape[0], pa, lda, sa, pl, ldl, sl,
+                                  ctypes.c_void_p(info.data_ptr()), _stream(stream)))
+    return L, info
+
+
+def chol_potrf_adjoint_workspace_size(dtype_code: int, n: int, nb: int = 0, accumulate: bool = True,
+                                      in_place: bool = False) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.chol_potrf_adjoint_workspace_size(dtype_code, n, nb, 1 if accumulate else 0,
+                                                 1 if in_place else 0, ctypes.byref(out)))
+    return int(out.value)
+
+
+def chol_potrf_adjoint(L, adjL, adjA=None, accumulate: bool = True, nb: int = 0, workspace=None,
+                       stream=None):
+    """Adjoint of the factor: lower(adjA) += G (or = G).  Returns adjA.
+    ``adjA`` may be ``adjL`` when ``accumulate`` is False."""
+    torch = _torch()
+    if adjA is None:
+        adjA = torch.zeros_like(L)
+    pl, ldl = _mat(L, "L")
+    pb, ldb = _mat(adjL, "adjL")
+    pa, lda = _mat(adjA, "adjA")
+    code = _dtype_code(L)
+    n = L.shape[0]
+    need = chol_potrf_adjoint_workspace_size(code, n, nb, accumulate, adjA.data_ptr() == adjL.data_ptr())
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=L.device)
+    wptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.chol_potrf_adjoint(code, n, pl, ldl, pb, ldb, pa, lda, 1 if accumulate else 0, nb, wptr,
+                                  wbytes, _stream(stream)))
+    return adjA
+
+
+def chol_potrf_adjoint_batched(L, adjL, adjA=None, accumulate: bool = True, stream=None):
+    torch = _torch()
+    if adjA is None:
+        adjA = torch.zeros_like(L)
+    pl, ldl, sl = _bat(L, "L")
+    pb, ldb, sb = _bat(adjL, "adjL")
+    pa, lda, sa = _bat(adjA, "adjA")
+    _check(lib.chol_potrf_adjoint_batched(_dtype_code(L), L.shape[1], L.shape[0], pl, ldl, sl, pb, ldb, sb,
+                                          pa, lda, sa, 1 if accumulate else 0, _stream(stream)))
+    return adjA
+
+
+def chol_wave_dot_fwd_adj(a, b, ybar, abar=None, bbar=None, staging: int = 0, stream=None):
+    """Returns (y, abar, bbar) of the one-lane-result dot product kernel."""
+    torch = _torch()
+    y = torch.empty(1, dtype=a.dtype, device=a.device)
+    if abar is None:
+        abar = torch.zeros_like(a)
+    if bbar is None:
+        bbar = torch.zeros_like(b)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    _check(lib.chol_wave_dot_fwd_adj(_dtype_code(a), a.numel(), p(a), p(b), p(y), p(ybar), p(abar), p(bbar),
+                                     staging, _stream(stream)))
+    return y, abar, bbar
+
+
+def chol_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def chol_abi_version() -> int:
+    return int(lib.chol_abi_version())

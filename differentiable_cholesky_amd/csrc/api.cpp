@@ -1,0 +1,250 @@
+// libchol C-ABI: argument validation and dispatch to the two kernel families.
+// Every check here runs on the host before anything is launched; a failed
+// check launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/libchol.h"
+
+namespace chol {
+template <typename T>
+chol_status small_potrf(int n, int64_t batch, const T *A, int64_t lda, int64_t sA, T *L, int64_t ldl,
+                        int64_t sL, int32_t *info, int info_mode, int64_t info_base, hipStream_t st);
+template <typename T>
+chol_status small_potrf_adjoint(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
+                                const T *adjL, int64_t ldal, int64_t sAL, T *adjA, int64_t ldaa,
+                                int64_t sAA, int accumulate, hipStream_t st);
+template <typename T>
+chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info, int nb,
+                          hipStream_t st);
+template <typename T>
+chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
+                            int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t st);
+size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb);
+template <typename T>
+chol_status wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar, T *bbar, int staging,
+                     hipStream_t st);
+} // namespace chol
+
+namespace {
+
+const int DEFAULT_NB = 128;
+// Index arithmetic inside the kernels uses 32-bit row/column counts.
+const int64_t MAX_N = (int64_t)1 << 30;
+
+struct Extent {
+    uintptr_t lo, hi; // [lo, hi) in bytes; empty when lo == hi
+};
+
+bool valid_dtype(chol_dtype dt) { return dt == CHOL_F32 || dt == CHOL_F64; }
+size_t esize(chol_dtype dt) { return dt == CHOL_F64 ? 8 : 4; }
+
+Extent extent(const void *p, int64_t n, int64_t ld, int64_t batch, int64_t stride, size_t es)
+{
+    Extent e{(uintptr_t)p, (uintptr_t)p};
+    if (n > 0 && batch > 0)
+        e.hi = e.lo + (size_t)((batch - 1) * stride + (n - 1) * ld + n) * es;
+    return e;
+}
+
+bool overlap(const Extent &a, const Extent &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Output `o` may be exactly the same buffer as input `i` (same base, ld and
+// stride) or disjoint from it; any other overlap is rejected.
+bool alias_ok(const void *i, int64_t ldi, int64_t si, const void *o, int64_t ldo, int64_t so, int64_t n,
+              int64_t batch, size_t es)
+{
+    if (i == o)
+        return ldi == ldo && (batch <= 1 || si == so);
+    return !overlap(extent(i, n, ldi, batch, si, es), extent(o, n, ldo, batch, so, es));
+}
+
+bool ld_ok(int64_t ld, int64_t n) { return ld >= std::max<int64_t>(1, n); }
+bool stride_ok(int64_t stride, int64_t ld, int64_t n, int64_t batch)
+{
+    return batch <= 1 || stride >= ld * n;
+}
+bool nb_ok(int64_t nb) { return nb >= 0 && nb <= CHOL_MAX_NB; }
+
+} // namespace
+
+extern "C" {
+
+int chol_abi_version(void) { return LIBCHOL_ABI_VERSION; }
+
+const char *chol_status_string(chol_status s)
+{
+    switch (s) {
+    case CHOL_OK: return "CHOL_OK";
+    case CHOL_ERR_INVALID_VALUE: return "CHOL_ERR_INVALID_VALUE: an argument is out of range or buffers overlap";
+    case CHOL_ERR_NOT_SUPPORTED: return "CHOL_ERR_NOT_SUPPORTED: size outside what this entry point handles";
+    case CHOL_ERR_WORKSPACE: return "CHOL_ERR_WORKSPACE: workspace missing or too small";
+    case CHOL_ERR_HIP: return "CHOL_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown chol_status";
+}
+
+chol_status chol_potrf(chol_dtype dt, int64_t n, const void *A, int64_t lda, void *L, int64_t ldl,
+                       int32_t *info, int64_t nb, void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n == 0)
+        return CHOL_OK;
+    if (!A || !L || !ld_ok(lda, n) || !ld_ok(ldl, n))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    if (!alias_ok(A, lda, 0, L, ldl, 0, n, 1, es))
+        return CHOL_ERR_INVALID_VALUE;
+    if (info && overlap(extent(info, 1, 1, 1, 0, 4), extent(L, n, ldl, 1, 0, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    if (dt == CHOL_F64) {
+        if (n <= CHOL_SMALL_MAX_N)
+            return chol::small_potrf<double>((int)n, 1, (const double *)A, lda, 0, (double *)L, ldl, 0, info, 0, 0, st);
+        return chol::blocked_potrf<double>(n, (const double *)A, lda, (double *)L, ldl, info, b, st);
+    }
+    if (n <= CHOL_SMALL_MAX_N)
+        return chol::small_potrf<float>((int)n, 1, (const float *)A, lda, 0, (float *)L, ldl, 0, info, 0, 0, st);
+    return chol::blocked_potrf<float>(n, (const float *)A, lda, (float *)L, ldl, info, b, st);
+}
+
+chol_status chol_potrf_batched(chol_dtype dt, int64_t n, int64_t batch, const void *A, int64_t lda,
+                               int64_t strideA, void *L, int64_t ldl, int64_t strideL, int32_t *info,
+                               void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || batch < 0)
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > CHOL_SMALL_MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    if (n == 0 || batch == 0)
+        return CHOL_OK;
+    if (!A || !L || !ld_ok(lda, n) || !ld_ok(ldl, n) || !stride_ok(strideA, lda, n, batch) ||
+        !stride_ok(strideL, ldl, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    if (batch > ((int64_t)1 << 31) - 1)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    if (!alias_ok(A, lda, strideA, L, ldl, strideL, n, batch, es))
+        return CHOL_ERR_INVALID_VALUE;
+    if (info && overlap(extent(info, 1, 1, batch, 1, 4), extent(L, n, ldl, batch, strideL, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    if (dt == CHOL_F64)
+        return chol::small_potrf<double>((int)n, batch, (const double *)A, lda, strideA, (double *)L, ldl,
+                                         strideL, info, 0, 0, st);
+    return chol::small_potrf<float>((int)n, batch, (const float *)A, lda, strideA, (float *)L, ldl, strideL,
+                                    info, 0, 0, st);
+}
+
+chol_status chol_potrf_adjoint_workspace_size(chol_dtype dt, int64_t n, int64_t nb, int accumulate,
+                                              int in_place, size_t *bytes)
+{
+    if (!bytes || !valid_dtype(dt) || n < 0 || !nb_ok(nb) || (in_place && accumulate))
+        return CHOL_ERR_INVALID_VALUE;
+    *bytes = 0;
+    if (n <= CHOL_SMALL_MAX_N)
+        return CHOL_OK;
+    if (n > MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    *bytes = chol::blocked_adjoint_workspace(n, nb ? (int)nb : DEFAULT_NB, esize(dt), accumulate != 0);
+    return CHOL_OK;
+}
+
+chol_status chol_potrf_adjoint(chol_dtype dt, int64_t n, const void *L, int64_t ldl, const void *adjL,
+                               int64_t ldal, void *adjA, int64_t ldaa, int accumulate, int64_t nb,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n == 0)
+        return CHOL_OK;
+    if (!L || !adjL || !adjA || !ld_ok(ldl, n) || !ld_ok(ldal, n) || !ld_ok(ldaa, n))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    const bool in_place = adjA == adjL;
+    if (in_place && accumulate)
+        return CHOL_ERR_INVALID_VALUE;
+    if (!alias_ok(adjL, ldal, 0, adjA, ldaa, 0, n, 1, es))
+        return CHOL_ERR_INVALID_VALUE;
+    if (overlap(extent(L, n, ldl, 1, 0, es), extent(adjA, n, ldaa, 1, 0, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    if (n <= CHOL_SMALL_MAX_N) {
+        if (dt == CHOL_F64)
+            return chol::small_potrf_adjoint<double>((int)n, 1, (const double *)L, ldl, 0, (const double *)adjL,
+                                                     ldal, 0, (double *)adjA, ldaa, 0, accumulate, st);
+        return chol::small_potrf_adjoint<float>((int)n, 1, (const float *)L, ldl, 0, (const float *)adjL, ldal,
+                                                0, (float *)adjA, ldaa, 0, accumulate, st);
+    }
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    const size_t need = chol::blocked_adjoint_workspace(n, b, es, accumulate != 0);
+    if (!workspace || workspace_bytes < need)
+        return CHOL_ERR_WORKSPACE;
+    const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlap(ws, extent(L, n, ldl, 1, 0, es)) || overlap(ws, extent(adjL, n, ldal, 1, 0, es)) ||
+        overlap(ws, extent(adjA, n, ldaa, 1, 0, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    if (dt == CHOL_F64)
+        return chol::blocked_adjoint<double>(n, (const double *)L, ldl, (const double *)adjL, ldal,
+                                             (double *)adjA, ldaa, accumulate, b, workspace, st);
+    return chol::blocked_adjoint<float>(n, (const float *)L, ldl, (const float *)adjL, ldal, (float *)adjA,
+                                        ldaa, accumulate, b, workspace, st);
+}
+
+chol_status chol_potrf_adjoint_batched(chol_dtype dt, int64_t n, int64_t batch, const void *L, int64_t ldl,
+                                       int64_t strideL, const void *adjL, int64_t ldal, int64_t strideAL,
+                                       void *adjA, int64_t ldaa, int64_t strideAA, int accumulate,
+                                       void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || batch < 0)
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > CHOL_SMALL_MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    if (n == 0 || batch == 0)
+        return CHOL_OK;
+    if (!L || !adjL || !adjA || !ld_ok(ldl, n) || !ld_ok(ldal, n) || !ld_ok(ldaa, n) ||
+        !stride_ok(strideL, ldl, n, batch) || !stride_ok(strideAL, ldal, n, batch) ||
+        !stride_ok(strideAA, ldaa, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    if (batch > ((int64_t)1 << 31) - 1)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    if (adjA == adjL && accumulate)
+        return CHOL_ERR_INVALID_VALUE;
+    if (!alias_ok(adjL, ldal, strideAL, adjA, ldaa, strideAA, n, batch, es))
+        return CHOL_ERR_INVALID_VALUE;
+    if (overlap(extent(L, n, ldl, batch, strideL, es), extent(adjA, n, ldaa, batch, strideAA, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    if (dt == CHOL_F64)
+        return chol::small_potrf_adjoint<double>((int)n, batch, (const double *)L, ldl, strideL,
+                                                 (const double *)adjL, ldal, strideAL, (double *)adjA, ldaa,
+                                                 strideAA, accumulate, st);
+    return chol::small_potrf_adjoint<float>((int)n, batch, (const float *)L, ldl, strideL, (const float *)adjL,
+                                            ldal, strideAL, (float *)adjA, ldaa, strideAA, accumulate, st);
+}
+
+chol_status chol_wave_dot_fwd_adj(chol_dtype dt, int64_t n, const void *a, const void *b, void *y,
+                                  const void *ybar, void *abar, void *bbar, int staging, void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || n > 64 || (staging != 0 && staging != 1))
+        return CHOL_ERR_INVALID_VALUE;
+    if (!y || !ybar || (n > 0 && (!a || !b || !abar || !bbar)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    if (dt == CHOL_F64)
+        return chol::wave_dot<double>((int)n, (const double *)a, (const double *)b, (double *)y,
+                                      (const double *)ybar, (double *)abar, (double *)bbar, staging, st);
+    return chol::wave_dot<float>((int)n, (const float *)a, (const float *)b, (float *)y, (const float *)ybar,
+                                 (float *)abar, (float *)bbar, staging, st);
+}
+
+} // extern "C"

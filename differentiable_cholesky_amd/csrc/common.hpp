@@ -1,0 +1,50 @@
+// Shared device helpers for libchol's gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/libchol.h"
+
+namespace chol {
+
+// ---------------------------------------------------------------- math ----
+// Division and square root use HIP's IEEE routines for both precisions.
+template <typename T> __device__ __forceinline__ T dsqrt(T x);
+template <> __device__ __forceinline__ float dsqrt<float>(float x) { return __fsqrt_rn(x); }
+template <> __device__ __forceinline__ double dsqrt<double>(double x) { return __dsqrt_rn(x); }
+
+template <typename T> __device__ __forceinline__ T drcp(T x);
+template <> __device__ __forceinline__ float drcp<float>(float x) { return __fdiv_rn(1.0f, x); }
+template <> __device__ __forceinline__ double drcp<double>(double x) { return __drcp_rn(x); }
+
+// ---------------------------------------------------------------- MFMA ----
+// One 16x16x4 matrix-core step: acc(16x16) += a(16x4) * b(4x16).
+// Operand layout of v_mfma_{f32,f64}_16x16x4 on a 64-lane wavefront:
+//   a: lane l holds A[l % 16][l / 16]      (row, k)
+//   b: lane l holds B[l / 16][l % 16]      (k, col)
+//   acc[v]: lane l holds C[4 * (l / 16) + v][l % 16]
+typedef double d4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Acc;
+template <> struct Acc<double> { typedef d4_t type; };
+template <> struct Acc<float> { typedef f4_t type; };
+
+__device__ __forceinline__ d4_t mfma16x16x4(double a, double b, d4_t c)
+{
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4_t mfma16x16x4(float a, float b, f4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------ launch checking ----
+#define CHOL_LAUNCH_CHECK()                                  \
+    do {                                                     \
+        if (hipGetLastError() != hipSuccess)                 \
+            return CHOL_ERR_HIP;                             \
+    } while (0)
+
+} // namespace chol

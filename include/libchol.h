@@ -1,0 +1,180 @@
+/*
+ * libchol -- Cholesky factorisation A = L L^T of symmetric positive-definite
+ * matrices and its reverse-mode adjoint, on one AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: the pages this library follows):
+ *   - jaxmg documentation, "Cholesky factorization" (potrf example): the
+ *     factor is the lower-triangular L with A = L L^T; no solve is performed;
+ *     the example validates against an expected factor whose strict upper
+ *     triangle is zero; its input may be donated so the factor overwrites it
+ *     ("Common setup", "Compute the factor" and the donation warning), and the
+ *     lower-level entry returns a status next to the factor ("Advanced:
+ *     control the outer jax.jit"); the tile size T_A is a parameter.
+ *   - Warp issue #1316, "[REQ] Add adjoint for out-of-place tile Cholesky
+ *     factorization", resolution comment: the adjoint is Murray's (2016)
+ *     symmetric-matrix derivative -- form Phi(L^T adj_L), apply two triangular
+ *     solves against L, and accumulate into the lower triangle of the gradient
+ *     of A.
+ *
+ * Conventions shared by every entry point
+ *   - Row-major storage: element (i, j) of a matrix with leading dimension ld
+ *     is at p[i * ld + j].  Batched arrays add stride * b for element b.
+ *   - "Lower" means i >= j.  Only the lower triangle of A and of adj_L is read.
+ *     L's strict upper triangle is written as zero.  adj_A's strict upper
+ *     triangle is never written.
+ *   - Phi(X) is the lower triangle of X with its diagonal halved.  The adjoint
+ *     written to adj_A is G = Phi(S + S^T), S = L^{-T} Phi(L^T adj_L) L^{-1}:
+ *     the exact gradient with respect to the lower entries the factorisation
+ *     reads (for f(A) = <adj_L, chol(A)>, G_ij = df/dA_ij for i >= j).
+ *   - dtype selects fp32 or fp64 for every floating-point array of the call.
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     keeps no reference after a call returns and allocates no device memory
+ *     in these calls (the blocked adjoint takes a caller workspace).
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *     is the null stream).  Nothing is synchronised with the host.
+ *   - Numerical failure is not an error code: info[b] is set on the device to
+ *     0 on success, else to 1 + the first column j whose pivot
+ *     d = A_jj - sum_k L_jk^2 fails d > 0 (NaN fails); the factor's columns
+ *     >= j are then unspecified.  The adjoint does not check its inputs.
+ *   - Argument errors are detected on the host before anything is launched:
+ *     n < 0, batch < 0, ld < max(1, n), a batch stride smaller than ld * n,
+ *     a NULL data pointer with n > 0 (and batch > 0), an unknown dtype, an
+ *     out-of-range tile size, or input and output buffers that overlap without
+ *     being exactly the same buffer with the same leading dimension and stride.
+ *     These return CHOL_ERR_INVALID_VALUE and launch nothing.  A HIP launch
+ *     failure returns CHOL_ERR_HIP.  n == 0 or batch == 0 is a no-op.
+ *   - Thread safety: calls from several host threads are safe; calls that share
+ *     output buffers or a workspace on concurrent streams race on that memory.
+ */
+#ifndef LIBCHOL_H
+#define LIBCHOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIBCHOL_ABI_VERSION 1
+
+/* Largest matrix edge handled by the batched small-tile kernels. */
+#define CHOL_SMALL_MAX_N 64
+/* Largest diagonal tile of the blocked factorisation (one workgroup keeps it in LDS). */
+#define CHOL_MAX_NB 128
+
+typedef enum { CHOL_F32 = 0, CHOL_F64 = 1 } chol_dtype;
+
+typedef enum {
+    CHOL_OK = 0,
+    CHOL_ERR_INVALID_VALUE = 1,
+    CHOL_ERR_NOT_SUPPORTED = 2,
+    CHOL_ERR_WORKSPACE = 3,
+    CHOL_ERR_HIP = 4
+} chol_status;
+
+/*
+ * chol_potrf -- factor one n x n SPD matrix.
+ *   A      [in]  device, n x n, leading dimension lda; lower triangle read.
+ *   L      [out] device, n x n, leading dimension ldl.  L == A with ldl == lda
+ *                factors in place (the jaxmg "donated input" case) and gives
+ *                bitwise the same L as the out-of-place call.
+ *   info   [out] device int32[1], or NULL if not wanted.
+ *   nb     tile size of the blocked algorithm (the page's T_A): 0 picks the
+ *          default (128); otherwise 1 <= nb <= CHOL_MAX_NB.  Matrices with
+ *          n <= CHOL_SMALL_MAX_N use the small-tile kernel and ignore nb.
+ * For n > CHOL_SMALL_MAX_N the call runs the blocked right-looking
+ * factorisation: per tile column a diagonal factor in LDS, a panel solve, and
+ * a lower-triangular trailing update on the matrix cores.
+ */
+chol_status chol_potrf(chol_dtype dtype, int64_t n,
+                       const void *A, int64_t lda,
+                       void *L, int64_t ldl,
+                       int32_t *info, int64_t nb, void *stream);
+
+/*
+ * chol_potrf_batched -- factor `batch` independent n x n SPD matrices,
+ * n <= CHOL_SMALL_MAX_N (larger n returns CHOL_ERR_NOT_SUPPORTED).
+ * Matrix b is at A + b * strideA (elements); likewise for L.  L == A with equal
+ * ld and stride is in place.  info: device int32[batch] or NULL.
+ * (Warp issue #1316 resolution comment: one tile Cholesky per block, loaded,
+ * factored and stored.)
+ */
+chol_status chol_potrf_batched(chol_dtype dtype, int64_t n, int64_t batch,
+                               const void *A, int64_t lda, int64_t strideA,
+                               void *L, int64_t ldl, int64_t strideL,
+                               int32_t *info, void *stream);
+
+/*
+ * chol_potrf_adjoint -- reverse-mode adjoint of chol_potrf for one matrix.
+ *   L      [in]  device, the factor (lower triangle read; diagonal must be
+ *                nonzero).
+ *   adjL   [in]  device, the upstream gradient dLoss/dL; lower triangle read.
+ *   adjA   [in/out] device; its lower triangle receives G:
+ *                accumulate != 0 : lower(adjA) += G   (gradient-buffer semantics)
+ *                accumulate == 0 : lower(adjA)  = G
+ *                adjA == adjL (same ld) is allowed only with accumulate == 0;
+ *                adj_L is then overwritten with G.
+ *   nb     tile size (0 = default 128, else 1..CHOL_MAX_NB); ignored for
+ *          n <= CHOL_SMALL_MAX_N.
+ *   workspace, workspace_bytes: device scratch of at least the size
+ *          chol_potrf_adjoint_workspace_size reports for the same arguments
+ *          (NULL / 0 allowed when it reports 0).  Too small returns
+ *          CHOL_ERR_WORKSPACE.
+ * The blocked form walks the tile columns in reverse order: the adjoint of the
+ * trailing update (a symmetric product on the matrix cores), the adjoint of
+ * the panel solve, and the formula above on each diagonal tile.
+ */
+chol_status chol_potrf_adjoint(chol_dtype dtype, int64_t n,
+                               const void *L, int64_t ldl,
+                               const void *adjL, int64_t ldal,
+                               void *adjA, int64_t ldaa,
+                               int accumulate, int64_t nb,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Bytes of workspace chol_potrf_adjoint needs for these arguments.
+ * in_place != 0 means adjA == adjL. */
+chol_status chol_potrf_adjoint_workspace_size(chol_dtype dtype, int64_t n, int64_t nb,
+                                              int accumulate, int in_place,
+                                              size_t *bytes);
+
+/*
+ * chol_potrf_adjoint_batched -- adjoint for `batch` independent matrices,
+ * n <= CHOL_SMALL_MAX_N, no workspace.  Strides and in-place rules as in
+ * chol_potrf_batched / chol_potrf_adjoint.
+ */
+chol_status chol_potrf_adjoint_batched(chol_dtype dtype, int64_t n, int64_t batch,
+                                       const void *L, int64_t ldl, int64_t strideL,
+                                       const void *adjL, int64_t ldal, int64_t strideAL,
+                                       void *adjA, int64_t ldaa, int64_t strideAA,
+                                       int accumulate, void *stream);
+
+/*
+ * chol_wave_dot_fwd_adj -- diagnostic kernel for the reduction/broadcast
+ * pattern the small-tile kernels rely on (Warp issue #1374, "adj_tile_dot is
+ * missing a block-wide broadcast of adj_ret": a dot product whose result only
+ * one lane writes must still hand the upstream gradient to every lane in the
+ * reverse pass).  One 64-lane wavefront loads a and b (n <= 64 elements each,
+ * fp32 or fp64), reduces y = a.b, and only lane 0 writes y[0].  In the
+ * reverse pass only lane 0 reads ybar[0]; it is broadcast to every lane,
+ * which then writes abar[k] += ybar*b[k] and bbar[k] += ybar*a[k] for the
+ * elements it owns.  `staging` 0 keeps a and b in registers, 1 stages them
+ * through LDS.
+ */
+chol_status chol_wave_dot_fwd_adj(chol_dtype dtype, int64_t n,
+                                  const void *a, const void *b, void *y,
+                                  const void *ybar, void *abar, void *bbar,
+                                  int staging, void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *chol_status_string(chol_status status);
+
+/* LIBCHOL_ABI_VERSION of the loaded library. */
+int chol_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCHOL_H */

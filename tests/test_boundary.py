@@ -1,0 +1,131 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host before launching
+anything.  No call here reaches a kernel launch."""
+import ctypes
+
+import pytest
+
+dc = pytest.importorskip("differentiable_cholesky_amd")
+from differentiable_cholesky_amd import _lib  # noqa: E402
+
+lib = _lib.lib
+F32, F64 = _lib.CHOL_F32, _lib.CHOL_F64
+OK, INVALID, NOTSUP, WS = (_lib.CHOL_OK, _lib.CHOL_ERR_INVALID_VALUE, _lib.CHOL_ERR_NOT_SUPPORTED,
+                           _lib.CHOL_ERR_WORKSPACE)
+
+# fake, never dereferenced device addresses (every call below fails validation first)
+P1 = ctypes.c_void_p(0x10000000)
+P2 = ctypes.c_void_p(0x20000000)
+P3 = ctypes.c_void_p(0x30000000)
+NUL = ctypes.c_void_p(0)
+
+
+def test_abi_version():
+    assert lib.chol_abi_version() == 1
+
+
+def test_every_declared_entry_point_is_exported():
+    names = _lib.header_entry_points()
+    assert set(names) >= {"chol_potrf", "chol_potrf_batched", "chol_potrf_adjoint",
+                          "chol_potrf_adjoint_batched", "chol_potrf_adjoint_workspace_size",
+                          "chol_status_string", "chol_abi_version", "chol_wave_dot_fwd_adj"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert lib.chol_status_string(s).startswith(b"CHOL_")
+    assert b"unknown" in lib.chol_status_string(99)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((7, 10, P1, 10, P2, 10, NUL, 0, NUL), INVALID),          # bad dtype
+    ((F64, -1, P1, 10, P2, 10, NUL, 0, NUL), INVALID),        # n < 0
+    ((F64, 0, NUL, 0, NUL, 0, NUL, 0, NUL), OK),              # empty: no-op
+    ((F64, 10, NUL, 10, P2, 10, NUL, 0, NUL), INVALID),       # null A
+    ((F64, 10, P1, 10, NUL, 10, NUL, 0, NUL), INVALID),       # null L
+    ((F64, 10, P1, 9, P2, 10, NUL, 0, NUL), INVALID),         # lda < n
+    ((F64, 10, P1, 10, P2, 9, NUL, 0, NUL), INVALID),         # ldl < n
+    ((F64, 100, P1, 100, P2, 100, NUL, -1, NUL), INVALID),    # nb < 0
+    ((F64, 100, P1, 100, P2, 100, NUL, 129, NUL), INVALID),   # nb > max
+    ((F64, 10, P1, 10, ctypes.c_void_p(0x10000000 + 8), 10, NUL, 0, NUL), INVALID),  # partial overlap
+    ((F64, 10, P1, 10, P1, 12, NUL, 0, NUL), INVALID),        # same buffer, different ld
+    ((F64, 10, P1, 10, P2, 10, ctypes.c_void_p(0x20000000 + 16), 0, NUL), INVALID),  # info inside L
+])
+def test_potrf_argument_errors(args, expect):
+    assert lib.chol_potrf(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((F32, 65, 4, P1, 65, 65 * 65, P2, 65, 65 * 65, NUL, NUL), NOTSUP),     # n > 64
+    ((F32, 8, -1, P1, 8, 64, P2, 8, 64, NUL, NUL), INVALID),                 # batch < 0
+    ((F32, 8, 0, NUL, 8, 64, NUL, 8, 64, NUL, NUL), OK),                     # empty batch
+    ((F32, 8, 4, P1, 8, 63, P2, 8, 64, NUL, NUL), INVALID),                  # strideA < ld*n
+    ((F32, 8, 4, P1, 8, 64, P2, 7, 64, NUL, NUL), INVALID),                  # ldl < n
+    ((F32, 8, 4, P1, 8, 64, ctypes.c_void_p(0x10000000 + 4 * 100), 8, 64, NUL, NUL), INVALID),  # overlap
+    ((F32, 8, 4, P1, 8, 64, P1, 8, 72, NUL, NUL), INVALID),                  # in place, different stride
+])
+def test_batched_argument_errors(args, expect):
+    assert lib.chol_potrf_batched(*args) == expect
+
+
+def _ws(dt, n, nb, acc, inplace):
+    out = ctypes.c_size_t(123)
+    st = lib.chol_potrf_adjoint_workspace_size(dt, n, nb, acc, inplace, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_query():
+    assert _ws(F64, 64, 0, 1, 0) == (OK, 0)
+    st, b = _ws(F64, 1000, 0, 1, 0)
+    assert st == OK and b >= 1000 * 1000 * 8
+    st, b0 = _ws(F64, 1000, 0, 0, 0)
+    assert st == OK and 0 < b0 and b - b0 >= 1000 * 1000 * 8   # the n x n gradient copy
+    st, b1 = _ws(F64, 1000, 0, 0, 1)
+    assert st == OK and b1 == b0
+    assert _ws(F64, 1000, 0, 1, 1)[0] == INVALID              # in place needs accumulate == 0
+    assert _ws(F32, 1000, 200, 1, 0)[0] == INVALID            # nb too large
+    assert lib.chol_potrf_adjoint_workspace_size(F64, 10, 0, 1, 0, None) == INVALID
+
+
+def test_adjoint_argument_errors():
+    n = 1000
+    # in place with accumulate
+    assert lib.chol_potrf_adjoint(F64, n, P1, n, P2, n, P2, n, 1, 0, P3, 1 << 40, NUL) == INVALID
+    # adjA overlapping L
+    assert lib.chol_potrf_adjoint(F64, n, P1, n, P2, n, ctypes.c_void_p(0x10000000 + 8 * 5), n, 0, 0, P3,
+                                  1 << 40, NUL) == INVALID
+    # missing / small workspace
+    assert lib.chol_potrf_adjoint(F64, n, P1, n, P2, n, P3, n, 1, 0, NUL, 0, NUL) == WS
+    st, need = _ws(F64, n, 0, 1, 0)
+    big = ctypes.c_void_p(0x7000000000)
+    assert lib.chol_potrf_adjoint(F64, n, P1, n, P2, n, P3, n, 1, 0, big, need - 1, NUL) == WS
+    # workspace overlapping an operand
+    assert lib.chol_potrf_adjoint(F64, n, P1, n, P2, n, P3, n, 1, 0, P2, need, NUL) == INVALID
+    # bad ld / null
+    assert lib.chol_potrf_adjoint(F64, n, P1, n - 1, P2, n, P3, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrf_adjoint(F64, n, NUL, n, P2, n, P3, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrf_adjoint(F64, 0, NUL, 0, NUL, 0, NUL, 0, 1, 0, NUL, 0, NUL) == OK
+
+
+def test_adjoint_batched_argument_errors():
+    assert lib.chol_potrf_adjoint_batched(F32, 65, 2, P1, 65, 65 * 65, P2, 65, 65 * 65, P3, 65, 65 * 65, 1,
+                                          NUL) == NOTSUP
+    assert lib.chol_potrf_adjoint_batched(F32, 8, 2, P1, 8, 64, P2, 8, 64, P2, 8, 64, 1, NUL) == INVALID
+    assert lib.chol_potrf_adjoint_batched(F32, 8, 2, P1, 8, 64, P2, 8, 64, ctypes.c_void_p(0x10000000 + 40),
+                                          8, 64, 0, NUL) == INVALID
+    assert lib.chol_potrf_adjoint_batched(F32, 8, 0, NUL, 8, 64, NUL, 8, 64, NUL, 8, 64, 1, NUL) == OK
+
+
+def test_wave_dot_argument_errors():
+    assert lib.chol_wave_dot_fwd_adj(F32, 65, P1, P2, P3, P1, P2, P3, 0, NUL) == INVALID
+    assert lib.chol_wave_dot_fwd_adj(F32, 16, P1, P2, P3, P1, P2, P3, 2, NUL) == INVALID
+    assert lib.chol_wave_dot_fwd_adj(F32, 16, NUL, P2, P3, P1, P2, P3, 0, NUL) == INVALID
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    A = torch.eye(4, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        dc.chol_potrf(A, L=A.clone(), info=torch.zeros(1, dtype=torch.int32))

@@ -301,14 +301,14 @@ k_gemm(GemmArgs<T> p)
         }
     }
 
-    // epilogue: acc[i][j][v] -> C[row][col], row = 4*(lane/16) + v within the 16x16 tile
+    // epilogue: acc[i][j][v] -> C[row][col] (row within the 16x16 tile per the MFMA output layout)
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = r0 + wm * WM + i * 16 + 4 * (lane / 16) + v;
+                const int row = r0 + wm * WM + i * 16 + Acc<T>::row(lane, v);
                 const int col = c0 + wn * WN + j * 16 + lane % 16;
                 if (row >= p.M || col >= p.N)
                     continue;

@@ -20,16 +20,24 @@ template <> __device__ __forceinline__ double drcp<double>(double x) { return __
 
 // ---------------------------------------------------------------- MFMA ----
 // One 16x16x4 matrix-core step: acc(16x16) += a(16x4) * b(4x16).
-// Operand layout of v_mfma_{f32,f64}_16x16x4 on a 64-lane wavefront:
+// Operand layout of v_mfma_{f32,f64}_16x16x4 on a 64-lane wavefront (checked
+// on gfx950 with one-hot inputs):
 //   a: lane l holds A[l % 16][l / 16]      (row, k)
 //   b: lane l holds B[l / 16][l % 16]      (k, col)
-//   acc[v]: lane l holds C[4 * (l / 16) + v][l % 16]
+//   acc[v], f32: lane l holds C[4 * (l / 16) + v][l % 16]
+//   acc[v], f64: lane l holds C[(l / 16) + 4 * v][l % 16]
 typedef double d4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 template <typename T> struct Acc;
-template <> struct Acc<double> { typedef d4_t type; };
-template <> struct Acc<float> { typedef f4_t type; };
+template <> struct Acc<double> {
+    typedef d4_t type;
+    static __device__ __forceinline__ int row(int lane, int v) { return lane / 16 + 4 * v; }
+};
+template <> struct Acc<float> {
+    typedef f4_t type;
+    static __device__ __forceinline__ int row(int lane, int v) { return 4 * (lane / 16) + v; }
+};
 
 __device__ __forceinline__ d4_t mfma16x16x4(double a, double b, d4_t c)
 {

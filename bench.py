@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X; prints ONE JSON line on stdout.
+
+A step is one pass over both kernel families on their benchmark inputs:
+  * batched fp32: 65536 matrices of 32 x 32, A_b = B_b B_b^T / 32 + I, factor
+    (chol_potrf_batched) then adjoint with accumulate (chol_potrf_adjoint_batched);
+  * blocked fp64: one 16384 x 16384 matrix A = G G^T / 16384 + 0.1 I, factor
+    (chol_potrf, nb = 128) then adjoint with accumulate (chol_potrf_adjoint).
+All inputs are built from seeds and resident in HBM before timing starts.
+
+value  = fp64 N=16384 factor+adjoint rate, counting N^3/3 + 2N^3/3 flops, GFLOP/s.
+batched.value = fp32 N=32 factor+adjoint rate, matrices/s.
+roofline = the kernel family with the largest summed time in the timed region:
+  algorithmic work per launch / average launch time, from HIP events recorded
+  by the library on the stream each kernel runs on (chol_profile_start/stop).
+cpu_baseline = the plain CPU oracle on a bounded sample of the same inputs.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "potrf fwd+adjoint GFLOP/s (fp64 N=16384) and batched matrices/s (fp32 N=32)"
+PEAK_FP64_TFLOPS = 78.6
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+FAMILIES = ["small_factor", "small_adjoint", "diag_factor", "diag_inverse", "panel_solve",
+            "trailing_update", "adj_trailing", "adj_panel", "adj_diag_update", "adj_diag", "elementwise"]
+BYTE_FAMILIES = {"small_factor", "small_adjoint", "elementwise"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def profile_stop(lib):
+    k = len(FAMILIES)
+    cnt = (ctypes.c_int64 * k)()
+    ms = (ctypes.c_double * k)()
+    work = (ctypes.c_double * k)()
+    lib.chol_profile_stop.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    st = lib.chol_profile_stop(k, ctypes.byref(cnt), ctypes.byref(ms), ctypes.byref(work))
+    if st != 0:
+        raise RuntimeError("chol_profile_stop failed")
+    return {FAMILIES[i]: {"launches": int(cnt[i]), "ms": float(ms[i]), "work": float(work[i])}
+            for i in range(k) if cnt[i] > 0}
+
+
+def roofline_of(fam: str, rec: dict, dtype_peak_tflops: float):
+    avg_s = rec["ms"] / rec["launches"] / 1e3
+    per_launch = rec["work"] / rec["launches"]
+    if fam in BYTE_FAMILIES:
+        achieved = per_launch / avg_s / 1e9
+        return {"kernel": fam, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "launches": rec["launches"], "avg_launch_us": round(avg_s * 1e6, 2)}
+    achieved = per_launch / avg_s / 1e12
+    return {"kernel": fam, "bound": "mfma", "achieved": round(achieved, 2), "peak": dtype_peak_tflops,
+            "unit": "TFLOP/s", "frac": round(achieved / dtype_peak_tflops, 4), "traffic": None,
+            "launches": rec["launches"], "avg_launch_us": round(avg_s * 1e6, 2)}
+
+
+def cpu_baseline(A_gpu, adjL_host, Ab_host, adjLb_host, ns: int):
+    import oracle
+    threads = oracle.max_threads()
+    A = A_gpu[:ns, :ns].cpu().numpy()
+    t = time.perf_counter()
+    L, info = oracle.potrf(A)
+    oracle.potrf_adjoint(L, adjL_host[:ns, :ns])
+    tb = time.perf_counter() - t
+    gflops = (ns ** 3 / 3 + 2 * ns ** 3 / 3) / tb / 1e9
+    t = time.perf_counter()
+    Lb, _ = oracle.potrf(Ab_host)
+    oracle.potrf_adjoint(Lb, adjLb_host, np.zeros_like(Lb))
+    tm = time.perf_counter() - t
+    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"leading {ns}x{ns} block of the same fp64 A (factor + adjoint, rate with "
+                      f"{ns}^3/3 + 2*{ns}^3/3 flops) and all {Ab_host.shape[0]} batched 32x32 matrices",
+            "seconds": round(tb + tm, 2),
+            "batched": {"value": round(Ab_host.shape[0] / tm, 1), "unit": "matrices/s"}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--n", type=int, default=16384)
+    ap.add_argument("--nb", type=int, default=128)
+    ap.add_argument("--batch", type=int, default=65536)
+    ap.add_argument("--batch-n", type=int, default=32)
+    ap.add_argument("--cpu-sample-n", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import differentiable_cholesky_amd as dc
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    n, nb, batch, bn = args.n, args.nb, args.batch, args.batch_n
+
+    log(f"bench: building inputs (n={n}, batch={batch}x{bn})")
+    A = workloads.gram_spd(n, seed=workloads.SEED_MATRIX, shift=0.1, device=dev)
+    adjL_h = workloads.lower_normal(n, seed=workloads.SEED_ADJ)
+    adjL = torch.from_numpy(adjL_h).to(dev)
+    L = torch.empty_like(A)
+    adjA = torch.zeros_like(A)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws_bytes = dc.chol_potrf_adjoint_workspace_size(dc.CHOL_F64, n, nb, True, False)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    Ab_h = workloads.batched_spd(batch, bn, seed=workloads.SEED_MATRIX, dtype=np.float32)
+    adjLb_h = workloads.lower_normal(bn, seed=workloads.SEED_ADJ, batch=batch, dtype=np.float32)
+    Ab = torch.from_numpy(Ab_h).to(dev)
+    adjLb = torch.from_numpy(adjLb_h).to(dev)
+    Lb = torch.empty_like(Ab)
+    adjAb = torch.zeros_like(Ab)
+    infob = torch.zeros(batch, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def step(times=None):
+        ev[0].record()
+        dc.chol_potrf_batched(Ab, Lb, infob)
+        dc.chol_potrf_adjoint_batched(Lb, adjLb, adjAb, accumulate=True)
+        ev[1].record()
+        dc.chol_potrf(A, L, info, nb=nb)
+        dc.chol_potrf_adjoint(L, adjL, adjA, accumulate=True, nb=nb, workspace=ws)
+        ev[2].record()
+        if times is not None:
+            torch.cuda.synchronize()
+            times.append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])))
+
+    log(f"bench: {args.warmup} warmup steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0 and int(infob.abs().sum().item()) == 0
+
+    log(f"bench: {args.steps} timed steps")
+    times = []
+    dc.lib.chol_profile_start()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(times)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = profile_stop(dc.lib)
+
+    t_small = sum(t[0] for t in times) / 1e3
+    t_block = sum(t[1] for t in times) / 1e3
+    flops = n ** 3 / 3 + 2 * n ** 3 / 3
+    gflops = flops * args.steps / t_block / 1e9
+    mats = batch * args.steps / t_small
+
+    blocked = {k: v for k, v in kern.items() if k not in ("small_factor", "small_adjoint")}
+    dom = max(blocked, key=lambda k: blocked[k]["ms"])
+    roof = roofline_of(dom, kern[dom], PEAK_FP64_TFLOPS)
+    small_dom = max(("small_factor", "small_adjoint"), key=lambda k: kern[k]["ms"])
+    roof_b = {k: roofline_of(k, kern[k], PEAK_FP32_TFLOPS) for k in ("small_factor", "small_adjoint")}
+    algo_bytes = batch * (2 + 4) * (bn * (bn + 1) // 2) * 4
+    roof_b["combined"] = {"bound": "hbm", "achieved": round(algo_bytes * args.steps / t_small / 1e9, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(algo_bytes * args.steps / t_small / 1e9 / PEAK_HBM_GBS, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(gflops, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"fp64 N={n} blocked potrf+adjoint (A=GG^T/N+0.1I, nb={nb}) plus "
+                               f"fp32 {batch}x{bn}x{bn} batched potrf+adjoint (A=BB^T/{bn}+I)",
+                   "n": n, "nb": nb, "batch": batch, "batch_n": bn, "accumulate": True},
+        "fraction_of_fp64_peak": round(gflops / 1e3 / PEAK_FP64_TFLOPS, 4),
+        "blocked_ms": {"total": round(t_block * 1e3 / args.steps, 3)},
+        "batched": {"value": round(mats, 1), "unit": "matrices/s", "dtype": "f32",
+                    "ms": round(t_small * 1e3 / args.steps, 4),
+                    "fraction_of_hbm_roofline": roof_b["combined"]["frac"],
+                    "algorithmic_bytes_per_matrix": (2 + 4) * (bn * (bn + 1) // 2) * 4},
+        "roofline": roof,
+        "roofline_batched": roof_b,
+        "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"] / args.steps, 4)}
+                    for k, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: CPU oracle baseline (sample n={args.cpu_sample_n})")
+        out["cpu_baseline"] = cpu_baseline(A, adjL_h, Ab_h, adjLb_h, min(args.cpu_sample_n, n))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -50,6 +50,10 @@ def _load() -> ctypes.CDLL:
     lib.chol_status_string.argtypes = [st]
     lib.chol_abi_version.restype = ctypes.c_int
     lib.chol_abi_version.argtypes = []
+    lib.chol_profile_start.restype = st
+    lib.chol_profile_start.argtypes = []
+    lib.chol_profile_stop.restype = st
+    lib.chol_profile_stop.argtypes = [ctypes.c_int32, vp, vp, vp]
     return lib
 
 

@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "../../include/libchol.h"
+#include "profile.hpp"
 
 namespace chol {
 template <typename T>
@@ -135,6 +136,7 @@ chol_status chol_potrf_batched(chol_dtype dt, int64_t n, int64_t batch, const vo
     if (info && overlap(extent(info, 1, 1, batch, 1, 4), extent(L, n, ldl, batch, strideL, es)))
         return CHOL_ERR_INVALID_VALUE;
     hipStream_t st = (hipStream_t)stream;
+    chol::prof::Scope ps(CHOL_K_SMALL_FACTOR, st, 2.0 * batch * ((double)n * (n + 1) / 2) * es);
     if (dt == CHOL_F64)
         return chol::small_potrf<double>((int)n, batch, (const double *)A, lda, strideA, (double *)L, ldl,
                                          strideL, info, 0, 0, st);
@@ -224,6 +226,8 @@ chol_status chol_potrf_adjoint_batched(chol_dtype dt, int64_t n, int64_t batch, 
     if (overlap(extent(L, n, ldl, batch, strideL, es), extent(adjA, n, ldaa, batch, strideAA, es)))
         return CHOL_ERR_INVALID_VALUE;
     hipStream_t st = (hipStream_t)stream;
+    chol::prof::Scope ps(CHOL_K_SMALL_ADJOINT, st,
+                         (accumulate ? 4.0 : 3.0) * batch * ((double)n * (n + 1) / 2) * es);
     if (dt == CHOL_F64)
         return chol::small_potrf_adjoint<double>((int)n, batch, (const double *)L, ldl, strideL,
                                                  (const double *)adjL, ldal, strideAL, (double *)adjA, ldaa,

@@ -25,6 +25,7 @@
 #include <cmath>
 
 #include "common.hpp"
+#include "profile.hpp"
 
 namespace chol {
 
@@ -68,6 +69,10 @@ k_tri(int64_t n, const T *src, int64_t lds, T *dst, int64_t ldd)
 template <typename T, int MODE>
 static chol_status tri_op(int64_t n, const T *src, int64_t lds, T *dst, int64_t ldd, hipStream_t st)
 {
+    const double tri = (double)n * (n + 1) / 2, es = (double)sizeof(T);
+    const double bytes = MODE == TRI_COPY_LOWER ? 2 * tri * es
+                       : MODE == TRI_ZERO_UPPER ? ((double)n * n - tri) * es : 3 * tri * es;
+    prof::Scope ps(CHOL_K_ELEMENTWISE, st, bytes);
     const unsigned t = (unsigned)((n + 31) / 32);
     hipLaunchKernelGGL((k_tri<T, MODE>), dim3(t, t), dim3(256), 0, st, n, src, lds, dst, ldd);
     CHOL_LAUNCH_CHECK();
@@ -374,14 +379,21 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
         const int kb = (int)std::min<int64_t>(nb, n - k0);
         const int64_t r0 = k0 + kb, m = n - r0;
         T *Wkk = L + k0 * ldl + k0;
-        if ((s = diag_potrf<T>(kb, Wkk, ldl, info, k == 0 ? 1 : 2, k0, st)) != CHOL_OK)
-            return s;
+        const double kb3 = (double)kb * kb * kb;
+        {
+            prof::Scope ps(CHOL_K_DIAG_FACTOR, st, kb3 / 3);
+            if ((s = diag_potrf<T>(kb, Wkk, ldl, info, k == 0 ? 1 : 2, k0, st)) != CHOL_OK)
+                return s;
+        }
         if (m == 0)
             break;
         // inverse of L_kk, transposed into the tile's strict upper triangle
-        hipLaunchKernelGGL((k_trinv<T>), dim3(1), dim3(256), 0, st, n, nb, k0, (int64_t)nb, L, ldl, 0,
-                           (T *)nullptr, (int64_t)0, (int64_t)0);
-        CHOL_LAUNCH_CHECK();
+        {
+            prof::Scope ps(CHOL_K_DIAG_INVERSE, st, kb3 / 3);
+            hipLaunchKernelGGL((k_trinv<T>), dim3(1), dim3(256), 0, st, n, nb, k0, (int64_t)nb, L, ldl, 0,
+                               (T *)nullptr, (int64_t)0, (int64_t)0);
+            CHOL_LAUNCH_CHECK();
+        }
         // panel: L_ik = W_ik * Linv^T  (in place; one block spans the full panel width)
         {
             GemmArgs<T> p{};
@@ -389,6 +401,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
             p.a = L + r0 * ldl + k0; p.lda = ldl;
             p.b = Wkk; p.ldb = ldl;
             p.c = L + r0 * ldl + k0; p.ldc = ldl;
+            prof::Scope ps(CHOL_K_PANEL_SOLVE, st, (double)m * kb * kb);
             if ((s = gemm<T, 64, 128, A_N, B_INVT, C_STORE>(p, 1, st)) != CHOL_OK)
                 return s;
         }
@@ -401,6 +414,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
             p.b = L + r0 * ldl + k0; p.ldb = ldl;
             p.c = L + r0 * ldl + r0; p.ldc = ldl;
             p.tri_tiles = tiles;
+            prof::Scope ps(CHOL_K_TRAILING_UPDATE, st, (double)m * (m + 1) * kb);
             if ((s = gemm<T, 64, 64, A_N, B_T, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
                 return s;
         }
@@ -497,9 +511,12 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
             return s;
     }
     // inverses of every diagonal tile, all at once
-    hipLaunchKernelGGL((k_trinv<T>), dim3((unsigned)K), dim3(256), 0, st, n, nb, (int64_t)0, (int64_t)nb,
-                       const_cast<T *>(L), ldl, 1, inv, (int64_t)nb * nb, (int64_t)nb);
-    CHOL_LAUNCH_CHECK();
+    {
+        prof::Scope ps(CHOL_K_DIAG_INVERSE, st, (double)K * nb * nb * nb / 3);
+        hipLaunchKernelGGL((k_trinv<T>), dim3((unsigned)K), dim3(256), 0, st, n, nb, (int64_t)0, (int64_t)nb,
+                           const_cast<T *>(L), ldl, 1, inv, (int64_t)nb * nb, (int64_t)nb);
+        CHOL_LAUNCH_CHECK();
+    }
 
     for (int64_t k = K - 1; k >= 0; --k) {
         const int64_t k0 = k * nb;
@@ -515,21 +532,28 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
             p.a = Wb + r0 * ldw + r0; p.lda = ldw;
             p.b = L + r0 * ldl + k0; p.ldb = ldl;
             p.c = Wb + r0 * ldw + k0; p.ldc = ldw;
-            if ((s = gemm<T, 64, 64, A_SYM, B_N, C_SUB>(p, 1, st)) != CHOL_OK)
-                return s;
+            {
+                prof::Scope ps(CHOL_K_ADJ_TRAILING, st, 2.0 * m * m * kb);
+                if ((s = gemm<T, 64, 64, A_SYM, B_N, C_SUB>(p, 1, st)) != CHOL_OK)
+                    return s;
+            }
             // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block)
             p = GemmArgs<T>{};
             p.M = (int)m; p.N = kb; p.K = kb;
             p.a = Wb + r0 * ldw + k0; p.lda = ldw;
             p.b = invk; p.ldb = nb;
             p.c = Wb + r0 * ldw + k0; p.ldc = ldw;
-            if ((s = gemm<T, 64, 128, A_N, B_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
-                return s;
+            {
+                prof::Scope ps(CHOL_K_ADJ_PANEL, st, (double)m * kb * kb);
+                if ((s = gemm<T, 64, 128, A_N, B_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
+                    return s;
+            }
             // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows
             p = GemmArgs<T>{};
             p.M = kb; p.N = kb; p.K = (int)m;
             p.a = Wb + r0 * ldw + k0; p.lda = ldw;
             p.b = L + r0 * ldl + k0; p.ldb = ldl;
+            prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, st, (double)m * kb * (kb + 1));
             int splits = (int)std::min<int64_t>(ADJ_SPLIT_MAX, (m + 511) / 512);
             if (splits <= 1) {
                 p.c = Wkk; p.ldc = ldw;
@@ -550,8 +574,11 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
             }
         }
         // R3: the tile adjoint on the diagonal
-        if ((s = diag_adjoint<T>(kb, Lkk, ldl, Wkk, ldw, invk, nb, st)) != CHOL_OK)
-            return s;
+        {
+            prof::Scope ps(CHOL_K_ADJ_DIAG, st, 2.0 * kb * kb * kb / 3);
+            if ((s = diag_adjoint<T>(kb, Lkk, ldl, Wkk, ldw, invk, nb, st)) != CHOL_OK)
+                return s;
+        }
     }
     if (need_wb)
         return tri_op<T, TRI_ADD_LOWER>(n, Wb, ldw, adjA, ldaa, st);

@@ -167,6 +167,37 @@ chol_status chol_wave_dot_fwd_adj(chol_dtype dtype, int64_t n,
                                   const void *ybar, void *abar, void *bbar,
                                   int staging, void *stream);
 
+/*
+ * Timing hook (diagnostics; used by the benchmark for per-kernel rooflines).
+ * chol_profile_start() clears previous records and turns timing on for all
+ * later calls in this process: each launch of a kernel family below is then
+ * bracketed by a pair of HIP events recorded on the stream it runs on.
+ * chol_profile_stop() turns timing off, waits for the recorded events, and
+ * writes, for family i < max_ids, the number of launches count[i], their summed
+ * duration ms[i] and their summed algorithmic work work[i] (flops for the
+ * matrix-core and tile kernels, bytes for the bandwidth-bound ones; the unit of
+ * each family is given below).  Arrays are host memory owned by the caller.
+ * Returns CHOL_ERR_HIP if an event could not be read.  While timing is on,
+ * launches from several host threads are recorded together.
+ */
+typedef enum {
+    CHOL_K_SMALL_FACTOR = 0,     /* batched small-tile factor; bytes: 2 * n(n+1)/2 * elem per matrix */
+    CHOL_K_SMALL_ADJOINT = 1,    /* batched small-tile adjoint; bytes: (3 or 4) * n(n+1)/2 * elem */
+    CHOL_K_DIAG_FACTOR = 2,      /* blocked: factor of a diagonal tile; flops: kb^3 / 3 */
+    CHOL_K_DIAG_INVERSE = 3,     /* blocked: inverse of diagonal tiles; flops: kb^3 / 3 per tile */
+    CHOL_K_PANEL_SOLVE = 4,      /* blocked: L_ik = W_ik L_kk^-T; flops: m * kb^2 */
+    CHOL_K_TRAILING_UPDATE = 5,  /* blocked: lower trailing update; flops: m (m + 1) kb */
+    CHOL_K_ADJ_TRAILING = 6,     /* adjoint: Wb_panel -= Sym(Wb22) L_panel; flops: 2 m^2 kb */
+    CHOL_K_ADJ_PANEL = 7,        /* adjoint: X = Wb_panel L_kk^-1; flops: m * kb^2 */
+    CHOL_K_ADJ_DIAG_UPDATE = 8,  /* adjoint: Wb_kk -= tril(X^T L_panel); flops: m * kb (kb + 1) */
+    CHOL_K_ADJ_DIAG = 9,         /* adjoint of the factor on a diagonal tile; flops: 2 kb^3 / 3 */
+    CHOL_K_ELEMENTWISE = 10,     /* triangle copies, zeroing, accumulation; bytes moved */
+    CHOL_K_COUNT = 11
+} chol_kernel_family;
+
+chol_status chol_profile_start(void);
+chol_status chol_profile_stop(int32_t max_ids, int64_t *count, double *ms, double *work);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *chol_status_string(chol_status status);
 

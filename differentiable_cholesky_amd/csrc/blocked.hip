@@ -25,6 +25,7 @@
 #include <cmath>
 
 #include "common.hpp"
+#include "gemm.hpp"
 #include "profile.hpp"
 
 namespace chol {
@@ -163,189 +164,6 @@ k_trinv(int64_t n_total, int nb, int64_t tile0, int64_t step, T *W, int64_t ld, 
         }
 }
 
-// ------------------------------------------------------------ MFMA GEMM ----
-// C (M x N) op= A (M x K) * B (K x N) on 16x16x4 matrix-core steps.
-// Block = 4 wavefronts in a 2 x 2 arrangement; tile BM x BN, K step 16 staged
-// in LDS.  Operand access modes:
-enum { A_N = 0,      // A(r, t) = a[r*lda + t]
-       A_T = 1,      // A(r, t) = a[t*lda + r]
-       A_SYM = 2 };  // A(r, t) = Sym(lower a): a[r][t] (r>t), a[t][r] (r<t), 2 a[r][r]
-enum { B_N = 0,      // B(t, c) = b[t*ldb + c]
-       B_T = 1,      // B(t, c) = b[c*ldb + t]
-       B_INVT = 2,   // B(t, c) = Linv(c, t): b[t][c] (t<c, strict upper holds Linv^T),
-                     //           1 / b[c][c] (t==c, the factor's diagonal), 0 (t>c)
-       B_LOWER = 3 };// B(t, c) = b[t][c] for t >= c, else 0
-enum { C_SUB = 0,        // C -= AB
-       C_SUB_LOWER = 1,  // C -= AB on entries with (row + diag_off) >= col only
-       C_STORE = 2,      // C  = AB
-       C_PARTIAL = 3 };  // part[split] = AB (row-major M x N)
-
-template <typename T> struct GemmArgs {
-    int M, N, K;
-    const T *a; int64_t lda;
-    const T *b; int64_t ldb;
-    T *c; int64_t ldc;
-    int kchunk;          // split-K chunk length (multiple of 16)
-    T *part;             // C_PARTIAL destination
-    int tri_tiles;       // lower-triangular tile grid: number of tile rows (0 = rectangular)
-};
-
-template <typename T, int AM>
-__device__ __forceinline__ T load_a(const GemmArgs<T> &p, int r, int t)
-{
-    if (r >= p.M || t >= p.K)
-        return T(0);
-    if (AM == A_N)
-        return p.a[(int64_t)r * p.lda + t];
-    if (AM == A_T)
-        return p.a[(int64_t)t * p.lda + r];
-    if (r > t)
-        return p.a[(int64_t)r * p.lda + t];
-    if (r < t)
-        return p.a[(int64_t)t * p.lda + r];
-    return T(2) * p.a[(int64_t)r * p.lda + r];
-}
-
-template <typename T, int BMODE>
-__device__ __forceinline__ T load_b(const GemmArgs<T> &p, int t, int c)
-{
-    if (t >= p.K || c >= p.N)
-        return T(0);
-    if (BMODE == B_N)
-        return p.b[(int64_t)t * p.ldb + c];
-    if (BMODE == B_T)
-        return p.b[(int64_t)c * p.ldb + t];
-    if (BMODE == B_INVT) {
-        if (t < c)
-            return p.b[(int64_t)t * p.ldb + c];
-        if (t == c)
-            return T(1) / p.b[(int64_t)c * p.ldb + c];
-        return T(0);
-    }
-    return (t >= c) ? p.b[(int64_t)t * p.ldb + c] : T(0);
-}
-
-template <typename T, int BM, int BN, int AM, int BMODE, int CM>
-__global__ void __launch_bounds__(256)
-k_gemm(GemmArgs<T> p)
-{
-    constexpr int BK = 16;
-    constexpr int WM = BM / 2, WN = BN / 2, TI = WM / 16, TJ = WN / 16;
-    constexpr int PA = BM + 4, PB = BN + 4;
-    __shared__ T As[BK * PA];
-    __shared__ T Bs[BK * PB];
-    typedef typename Acc<T>::type acc_t;
-
-    int ti_blk, tj_blk;
-    if (p.tri_tiles > 0) {
-        const int t = blockIdx.x;
-        int I = (int)((std::sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
-        while (I * (I + 1) / 2 > t) --I;
-        while ((I + 1) * (I + 2) / 2 <= t) ++I;
-        ti_blk = I;
-        tj_blk = t - I * (I + 1) / 2;
-    } else {
-        ti_blk = blockIdx.x;
-        tj_blk = blockIdx.y;
-    }
-    const int r0 = ti_blk * BM, c0 = tj_blk * BN;
-    int kbeg = 0, kend = p.K;
-    if (CM == C_PARTIAL) {
-        kbeg = blockIdx.z * p.kchunk;
-        kend = std::min(p.K, kbeg + p.kchunk);
-    }
-
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int wm = wave / 2, wn = wave % 2;
-
-    acc_t acc[TI][TJ];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-            acc[i][j] = acc_t{0, 0, 0, 0};
-
-    // which thread mapping keeps the A loads contiguous
-    bool a_rowmajor = (AM == A_N);
-    for (int k0 = kbeg; k0 < kend; k0 += BK) {
-        if (AM == A_SYM)
-            a_rowmajor = (r0 >= k0 + BK - 1) || !(r0 + BM - 1 < k0);
-        __syncthreads();
-        // A tile -> As[t][r]
-        for (int idx = tid; idx < BM * BK; idx += 256) {
-            int r, t;
-            if (a_rowmajor) { r = idx / BK; t = idx % BK; }
-            else            { t = idx / BM; r = idx % BM; }
-            const int gt = k0 + t;
-            As[t * PA + r] = (gt < kend) ? load_a<T, AM>(p, r0 + r, gt) : T(0);
-        }
-        // B tile -> Bs[t][c]
-        for (int idx = tid; idx < BN * BK; idx += 256) {
-            int t, c;
-            if (BMODE == B_T) { c = idx / BK; t = idx % BK; }
-            else              { t = idx / BN; c = idx % BN; }
-            const int gt = k0 + t;
-            Bs[t * PB + c] = (gt < kend) ? load_b<T, BMODE>(p, gt, c0 + c) : T(0);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 4) {
-            const int kr = kk + lane / 16;
-            T af[TI], bf[TJ];
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-                af[i] = As[kr * PA + wm * WM + i * 16 + lane % 16];
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-                bf[j] = Bs[kr * PB + wn * WN + j * 16 + lane % 16];
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    acc[i][j] = mfma16x16x4(af[i], bf[j], acc[i][j]);
-        }
-    }
-
-    // epilogue: acc[i][j][v] -> C[row][col] (row within the 16x16 tile per the MFMA output layout)
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = r0 + wm * WM + i * 16 + Acc<T>::row(lane, v);
-                const int col = c0 + wn * WN + j * 16 + lane % 16;
-                if (row >= p.M || col >= p.N)
-                    continue;
-                const T val = acc[i][j][v];
-                if (CM == C_SUB) {
-                    p.c[(int64_t)row * p.ldc + col] -= val;
-                } else if (CM == C_SUB_LOWER) {
-                    if (row >= col)
-                        p.c[(int64_t)row * p.ldc + col] -= val;
-                } else if (CM == C_STORE) {
-                    p.c[(int64_t)row * p.ldc + col] = val;
-                } else {
-                    p.part[(int64_t)blockIdx.z * p.M * p.N + (int64_t)row * p.N + col] = val;
-                }
-            }
-}
-
-template <typename T, int BM, int BN, int AM, int BMODE, int CM>
-static chol_status gemm(const GemmArgs<T> &p, int splits, hipStream_t st)
-{
-    if (p.M <= 0 || p.N <= 0)
-        return CHOL_OK;
-    dim3 grid;
-    if (p.tri_tiles > 0)
-        grid = dim3((unsigned)(p.tri_tiles * (p.tri_tiles + 1) / 2), 1, 1);
-    else
-        grid = dim3((unsigned)((p.M + BM - 1) / BM), (unsigned)((p.N + BN - 1) / BN), (unsigned)splits);
-    hipLaunchKernelGGL((k_gemm<T, BM, BN, AM, BMODE, CM>), grid, dim3(256), 0, st, p);
-    CHOL_LAUNCH_CHECK();
-    return CHOL_OK;
-}
-
 // C_lower(n x n) -= sum_s part[s] (lower entries only)
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -361,6 +179,35 @@ k_splitk_reduce_lower(int n, int splits, const T *part, T *c, int64_t ldc)
     for (int q = 0; q < splits; ++q)
         s += part[(int64_t)q * n * n + idx];
     c[(int64_t)r * ldc + col] -= s;
+}
+
+// C(M x N) -= sum_s part[s] (all entries), part row-major M x N per split
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_splitk_reduce(int M, int N, int splits, const T *part, T *c, int64_t ldc)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t tot = (int64_t)M * N;
+    if (idx >= tot)
+        return;
+    const int r = (int)(idx / N), col = (int)(idx % N);
+    T s = T(0);
+    for (int q = 0; q < splits; ++q)
+        s += part[(int64_t)q * tot + idx];
+    c[(int64_t)r * ldc + col] -= s;
+}
+
+// Split of a long contraction so that about two blocks per CU are busy.
+static inline int split_count(int64_t tiles, int64_t K, int max_splits)
+{
+    int s = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
+    s = (int)std::min<int64_t>(s, std::max<int64_t>(1, K / 256));
+    return s;
+}
+static inline int split_chunk(int64_t K, int splits)
+{
+    int c = (int)((K + splits - 1) / splits);
+    return (c + 15) / 16 * 16;
 }
 
 // ------------------------------------------------------------- forward ----
@@ -402,20 +249,19 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
             p.b = Wkk; p.ldb = ldl;
             p.c = L + r0 * ldl + k0; p.ldc = ldl;
             prof::Scope ps(CHOL_K_PANEL_SOLVE, st, (double)m * kb * kb);
-            if ((s = gemm<T, 64, 128, A_N, B_INVT, C_STORE>(p, 1, st)) != CHOL_OK)
+            if ((s = gemm<T, OP_MK, OP_KM_INVT, C_STORE>(p, 1, st)) != CHOL_OK)
                 return s;
         }
         // trailing: W22 lower -= P P^T
         {
-            const int tiles = (int)((m + 63) / 64);
             GemmArgs<T> p{};
             p.M = (int)m; p.N = (int)m; p.K = kb;
             p.a = L + r0 * ldl + k0; p.lda = ldl;
             p.b = L + r0 * ldl + k0; p.ldb = ldl;
             p.c = L + r0 * ldl + r0; p.ldc = ldl;
-            p.tri_tiles = tiles;
+            p.tri = 1;
             prof::Scope ps(CHOL_K_TRAILING_UPDATE, st, (double)m * (m + 1) * kb);
-            if ((s = gemm<T, 64, 64, A_N, B_T, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
+            if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
                 return s;
         }
     }
@@ -428,7 +274,8 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
 //   [inv: K * nb * nb]   inverses of the diagonal tiles of L
 //   [part: SPLITS * nb * nb]  split-K partial products
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-static const int ADJ_SPLIT_MAX = 64;
+static const int ADJ_SPLIT_MAX = 64;     // splits of the tile-sized product Wb_kk -= tril(X^T L)
+static const int R1_SPLIT_MAX = 8;       // splits of the panel product Wb_panel -= Sym(Wb22) L
 
 size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
 {
@@ -437,7 +284,7 @@ size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
     if (need_wb)
         s += align256((size_t)n * n * esize);
     s += align256((size_t)K * nb * nb * esize);
-    s += align256((size_t)ADJ_SPLIT_MAX * nb * nb * esize);
+    s += align256(std::max((size_t)ADJ_SPLIT_MAX * nb * nb, (size_t)R1_SPLIT_MAX * n * nb) * esize);
     return s;
 }
 
@@ -463,15 +310,15 @@ static chol_status diag_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t 
     p.a = Wb + (int64_t)h * ldw + h; p.lda = ldw;
     p.b = L + (int64_t)h * ldl; p.ldb = ldl;
     p.c = Wb + (int64_t)h * ldw; p.ldc = ldw;
-    if ((s = gemm<T, 64, 64, A_SYM, B_N, C_SUB>(p, 1, st)) != CHOL_OK)
+    if ((s = gemm<T, OP_SYM, OP_KM, C_SUB>(p, 1, st)) != CHOL_OK)
         return s;
-    // X = Wb10 L00^{-1}  (in place, full width)
+    // X = Wb10 L00^{-1}  (in place: one block spans the full width)
     p = GemmArgs<T>{};
     p.M = m; p.N = h; p.K = h;
     p.a = Wb + (int64_t)h * ldw; p.lda = ldw;
     p.b = inv; p.ldb = ldi;
     p.c = Wb + (int64_t)h * ldw; p.ldc = ldw;
-    if ((s = gemm<T, 64, 128, A_N, B_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
+    if ((s = gemm<T, OP_MK, OP_KM_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
         return s;
     // Wb00 -= tril(X^T L10)
     p = GemmArgs<T>{};
@@ -479,7 +326,7 @@ static chol_status diag_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t 
     p.a = Wb + (int64_t)h * ldw; p.lda = ldw;
     p.b = L + (int64_t)h * ldl; p.ldb = ldl;
     p.c = Wb; p.ldc = ldw;
-    if ((s = gemm<T, 64, 64, A_T, B_N, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
+    if ((s = gemm<T, OP_KM, OP_KM, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
         return s;
     return diag_adjoint<T>(h, L, ldl, Wb, ldw, inv, ldi, st);
 }
@@ -527,15 +374,25 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
         const T *invk = inv + k * nb * nb;
         if (m > 0) {
             GemmArgs<T> p{};
-            // R1: Wb_panel -= Sym(Wb22) L_panel
+            // R1: Wb_panel -= Sym(Wb22) L_panel, the contraction over m split
+            // into partial products reduced in a fixed order
             p.M = (int)m; p.N = kb; p.K = (int)m;
             p.a = Wb + r0 * ldw + r0; p.lda = ldw;
             p.b = L + r0 * ldl + k0; p.ldb = ldl;
             p.c = Wb + r0 * ldw + k0; p.ldc = ldw;
             {
                 prof::Scope ps(CHOL_K_ADJ_TRAILING, st, 2.0 * m * m * kb);
-                if ((s = gemm<T, 64, 64, A_SYM, B_N, C_SUB>(p, 1, st)) != CHOL_OK)
+                const int64_t tiles = ((m + 127) / 128) * ((kb + 127) / 128);
+                const int splits = split_count(tiles, m, R1_SPLIT_MAX);
+                p.kchunk = split_chunk(m, splits);
+                const int used = (int)((m + p.kchunk - 1) / p.kchunk);
+                p.part = part;
+                if ((s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st)) != CHOL_OK)
                     return s;
+                const int64_t tot = m * kb;
+                hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
+                                   (int)m, kb, used, (const T *)part, p.c, ldw);
+                CHOL_LAUNCH_CHECK();
             }
             // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block)
             p = GemmArgs<T>{};
@@ -545,7 +402,7 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
             p.c = Wb + r0 * ldw + k0; p.ldc = ldw;
             {
                 prof::Scope ps(CHOL_K_ADJ_PANEL, st, (double)m * kb * kb);
-                if ((s = gemm<T, 64, 128, A_N, B_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
+                if ((s = gemm<T, OP_MK, OP_KM_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
                     return s;
             }
             // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows
@@ -557,7 +414,7 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
             int splits = (int)std::min<int64_t>(ADJ_SPLIT_MAX, (m + 511) / 512);
             if (splits <= 1) {
                 p.c = Wkk; p.ldc = ldw;
-                if ((s = gemm<T, 64, 64, A_T, B_N, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
+                if ((s = gemm<T, OP_KM, OP_KM, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
                     return s;
             } else {
                 int chunk = (int)((m + splits - 1) / splits);
@@ -565,7 +422,7 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
                 splits = (int)((m + chunk - 1) / chunk);
                 p.kchunk = chunk;
                 p.part = part;
-                if ((s = gemm<T, 64, 64, A_T, B_N, C_PARTIAL>(p, splits, st)) != CHOL_OK)
+                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, st)) != CHOL_OK)
                     return s;
                 const int64_t tot = (int64_t)kb * kb;
                 hipLaunchKernelGGL((k_splitk_reduce_lower<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256),

@@ -1,0 +1,356 @@
+// Matrix-core product used by the blocked factor and adjoint:
+//     C (M x N) op= A (M x K) * B (K x N)
+// with each operand described by how its tile sits in memory.  Both operands
+// are indexed (m, k): m runs along the output (rows of C for A, columns of C
+// for B), k along the contraction.
+//
+//   OP_MK    element (m, k) at p[m * ld + k]   (rows of a row-major panel)
+//   OP_KM    element (m, k) at p[k * ld + m]
+//   OP_SYM   symmetric matrix stored as its lower triangle: (m, k) is
+//            p[m][k] below the diagonal, p[k][m] above, 2 p[m][m] on it
+//            (the adjoint of a lower-triangle-only trailing update reads the
+//            gradient this way)
+//   OP_KM_LOWER  OP_KM with entries k < m replaced by 0
+//   OP_KM_INVT   element (m, k) = X(m, k) of X = Linv where the tile p holds
+//            L's diagonal and Linv^T in its strict upper triangle:
+//            p[k][m] for k < m, 1 / p[m][m] for k == m, 0 for k > m
+//
+// Design for gfx950: a 256-thread block computes a 128 x 128 tile as 2 x 2
+// wavefronts of 64 x 64, each a 4 x 4 grid of 16x16x4 MFMA steps.  K advances
+// in chunks of 16 staged in LDS k-major (S[k][m]) and double-buffered; the next
+// chunk is fetched into registers with 16-byte global loads while the current
+// one feeds the matrix cores (the thread-to-element maps are given at Map
+// below).  Blocks are mapped to tiles so that each of the 8 XCDs receives a
+// contiguous row-major range of tiles (rows of A and columns of B stay in one
+// XCD's L2).
+#pragma once
+
+#include "common.hpp"
+
+namespace chol {
+
+enum { OP_MK = 0, OP_KM = 1, OP_SYM = 2, OP_KM_LOWER = 3, OP_KM_INVT = 4 };
+enum { C_SUB = 0,        // C -= AB
+       C_SUB_LOWER = 1,  // C -= AB where row >= col
+       C_STORE = 2,      // C  = AB
+       C_PARTIAL = 3 };  // part[split] = AB (row-major M x N)
+
+template <typename T> struct GemmArgs {
+    int M, N, K;
+    const T *a; int64_t lda;
+    const T *b; int64_t ldb;
+    T *c; int64_t ldc;
+    int kchunk;          // split-K: contraction length per split (multiple of 16)
+    T *part;             // C_PARTIAL destination, splits * M * N
+    int tri;             // 1: lower-triangular tile grid (M == N)
+    int vec;             // 1: 16-byte global loads are legal for both operands
+};
+
+namespace gemm_detail {
+
+constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int NT = 256;
+// LDS pitch of a k row (elements): even, so 16-byte writes stay aligned, and
+// chosen so the row-panel scatter is at most 2-way bank conflicted.
+template <typename T> struct Pitch;
+template <> struct Pitch<double> { static constexpr int v = 130; };
+template <> struct Pitch<float> { static constexpr int v = 132; };
+
+// element (m, k) of an operand, with bounds (m < mlim, k < klim) -> 0 outside
+template <typename T, int OP>
+__device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim, int klim)
+{
+    if (m >= mlim || k >= klim)
+        return T(0);
+    if (OP == OP_MK)
+        return p[(int64_t)m * ld + k];
+    if (OP == OP_KM)
+        return p[(int64_t)k * ld + m];
+    if (OP == OP_KM_LOWER)
+        return k >= m ? p[(int64_t)k * ld + m] : T(0);
+    if (OP == OP_KM_INVT) {
+        if (k < m)
+            return p[(int64_t)k * ld + m];
+        if (k == m)
+            return T(1) / p[(int64_t)m * ld + m];
+        return T(0);
+    }
+    // OP_SYM
+    if (m > k)
+        return p[(int64_t)m * ld + k];
+    if (m < k)
+        return p[(int64_t)k * ld + m];
+    return T(2) * p[(int64_t)m * ld + m];
+}
+
+// Eight elements per thread per chunk, fetched as 16-byte loads of PER
+// consecutive elements.  Element j of thread t (wave w = t / 64, lane l):
+//   q = j / PER (load number), e = j % PER
+//   row-panel layout (LAY_MK): LPR = 16 / PER lanes cover the 16 k of one row
+//       m = w * 32 + q * (64 / LPR) + l / LPR,   k = (l % LPR) * PER + e
+//   k-major layout (LAY_KM): LPK = 128 / PER lanes cover the 128 m of one k row
+//       k = w * 4 + q * (64 / LPK) + l / LPK,    m = (l % LPK) * PER + e
+// so every load instruction reads whole 64- or 128-byte segments.
+template <typename T> struct Vec8 { T v[8]; };
+enum { LAY_MK = 0, LAY_KM = 1 };
+
+template <typename T> struct Map {
+    static constexpr int PER = 16 / sizeof(T);
+    static constexpr int LPR = BK / PER;        // lanes per row (row-panel)
+    static constexpr int LPK = BM / PER;        // lanes per k row (k-major)
+    static __device__ __forceinline__ void mk(int t, int j, int &m, int &k)
+    {
+        const int w = t / 64, l = t % 64, q = j / PER, e = j % PER;
+        m = w * 32 + q * (64 / LPR) + l / LPR;
+        k = (l % LPR) * PER + e;
+    }
+    static __device__ __forceinline__ void km(int t, int j, int &m, int &k)
+    {
+        const int w = t / 64, l = t % 64, q = j / PER, e = j % PER;
+        k = w * 4 + q * (64 / LPK) + l / LPK;
+        m = (l % LPK) * PER + e;
+    }
+};
+
+template <typename T, int OP>
+struct Operand {
+    const T *p;
+    int64_t ld;
+    int m0;      // tile origin along m
+    int mlim;    // M (or N) bound
+    int vec;
+
+    // layout used for a chunk starting at k0 (uniform over the block)
+    __device__ __forceinline__ int layout(int k0) const
+    {
+        if (OP == OP_MK)
+            return LAY_MK;
+        if (OP == OP_SYM)
+            return (m0 >= k0 + BK) ? LAY_MK : LAY_KM;
+        return LAY_KM;
+    }
+    // does the chunk need the per-element path (edges, diagonal crossing, masks)?
+    __device__ __forceinline__ bool generic(int k0, int klim) const
+    {
+        if (!vec || m0 + BM > mlim || k0 + BK > klim)
+            return true;
+        if (OP == OP_SYM)
+            return !(m0 >= k0 + BK || m0 + BM <= k0);
+        if (OP == OP_KM_LOWER)
+            return !(k0 >= m0 + BM - 1);         // plain only if every k >= every m
+        if (OP == OP_KM_INVT)
+            return !(k0 + BK - 1 < m0);          // plain only if every k < every m
+        return false;
+    }
+
+    __device__ __forceinline__ void fetch(Vec8<T> &r, int tid, int k0, int klim) const
+    {
+        typedef Map<T> MP;
+        const int lay = layout(k0);
+        if (!generic(k0, klim)) {
+            typedef T vt __attribute__((ext_vector_type(MP::PER)));
+#pragma unroll
+            for (int q = 0; q < 8 / MP::PER; ++q) {
+                int m, k;
+                if (lay == LAY_MK)
+                    MP::mk(tid, q * MP::PER, m, k);
+                else
+                    MP::km(tid, q * MP::PER, m, k);
+                const T *src = (lay == LAY_MK) ? p + (int64_t)(m0 + m) * ld + k0 + k
+                                               : p + (int64_t)(k0 + k) * ld + m0 + m;
+                const vt x = *reinterpret_cast<const vt *>(src);
+#pragma unroll
+                for (int e = 0; e < MP::PER; ++e)
+                    r.v[q * MP::PER + e] = x[e];
+            }
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int m, k;
+            if (lay == LAY_MK)
+                MP::mk(tid, j, m, k);
+            else
+                MP::km(tid, j, m, k);
+            r.v[j] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim);
+        }
+    }
+
+    __device__ __forceinline__ void stash(const Vec8<T> &r, T *S, int tid, int k0) const
+    {
+        typedef Map<T> MP;
+        const int lay = layout(k0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int m, k;
+            if (lay == LAY_MK)
+                MP::mk(tid, j, m, k);
+            else
+                MP::km(tid, j, m, k);
+            S[k * Pitch<T>::v + m] = r.v[j];
+        }
+    }
+};
+
+// blockIdx.x -> tile index so that each XCD (blocks b with equal b % 8) takes a
+// contiguous range of the row-major tile order.
+__device__ __forceinline__ int xcd_tile(int b, int nt)
+{
+    const int per = nt / 8, rem = nt % 8;
+    const int x = b % 8, i = b / 8;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+} // namespace gemm_detail
+
+template <typename T, int AOP, int BOP, int CM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_gemm(GemmArgs<T> p)
+{
+    using namespace gemm_detail;
+    typedef typename Acc<T>::type acc_t;
+    constexpr int PITCH = Pitch<T>::v;
+    __shared__ T lds[2][2][BK * PITCH];    // [buffer][operand A/B]
+
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int wm = wave / 2, wn = wave % 2;
+
+    // tile coordinates
+    int I, J;
+    {
+        const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
+        const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
+        const int t = xcd_tile(blockIdx.x, nt);
+        if (p.tri) {
+            int r = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+            while (r * (r + 1) / 2 > t) --r;
+            while ((r + 1) * (r + 2) / 2 <= t) ++r;
+            I = r;
+            J = t - r * (r + 1) / 2;
+        } else {
+            I = t / TJ;
+            J = t % TJ;
+        }
+    }
+    const int r0 = I * BM, c0 = J * BN;
+    int kbeg = 0, kend = p.K;
+    if (CM == C_PARTIAL) {
+        kbeg = blockIdx.y * p.kchunk;
+        kend = min(p.K, kbeg + p.kchunk);
+    }
+
+    Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec};
+    Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec};
+
+    // C -= AB runs as acc = C, acc += (-A) B: the accumulators start from C,
+    // so the epilogue is a plain store and no accumulator has to leave the
+    // matrix-core registers for a read-modify-write.
+    constexpr bool FROM_C = (CM == C_SUB || CM == C_SUB_LOWER);
+    acc_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                T x = T(0);
+                if (FROM_C) {
+                    const int row = r0 + wm * 64 + i * 16 + Acc<T>::row(lane, v);
+                    const int col = c0 + wn * 64 + j * 16 + lane % 16;
+                    if (row < p.M && col < p.N)
+                        x = p.c[(int64_t)row * p.ldc + col];
+                }
+                acc[i][j][v] = x;
+            }
+
+    Vec8<T> ra, rb;
+    int buf = 0;
+    if (kbeg < kend) {
+        A.fetch(ra, tid, kbeg, kend);
+        B.fetch(rb, tid, kbeg, kend);
+        A.stash(ra, lds[0][0], tid, kbeg);
+        B.stash(rb, lds[0][1], tid, kbeg);
+    }
+    __syncthreads();
+    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+        const bool more = k0 + BK < kend;
+        if (more) {
+            A.fetch(ra, tid, k0 + BK, kend);
+            B.fetch(rb, tid, k0 + BK, kend);
+        }
+        const T *SA = lds[buf][0];
+        const T *SB = lds[buf][1];
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 4) {
+            const int kr = kk + lane / 16;
+            T af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = SA[kr * PITCH + wm * 64 + i * 16 + lane % 16];
+                if (FROM_C)
+                    af[i] = -af[i];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = SB[kr * PITCH + wn * 64 + j * 16 + lane % 16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = mfma16x16x4(af[i], bf[j], acc[i][j]);
+        }
+        if (more) {
+            A.stash(ra, lds[buf ^ 1][0], tid, k0 + BK);
+            B.stash(rb, lds[buf ^ 1][1], tid, k0 + BK);
+        }
+        __syncthreads();
+        buf ^= 1;
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = r0 + wm * 64 + i * 16 + Acc<T>::row(lane, v);
+                const int col = c0 + wn * 64 + j * 16 + lane % 16;
+                if (row >= p.M || col >= p.N)
+                    continue;
+                const T val = acc[i][j][v];
+                if (CM == C_SUB || CM == C_STORE) {
+                    p.c[(int64_t)row * p.ldc + col] = val;
+                } else if (CM == C_SUB_LOWER) {
+                    if (row >= col)
+                        p.c[(int64_t)row * p.ldc + col] = val;
+                } else {
+                    p.part[(int64_t)blockIdx.y * p.M * p.N + (int64_t)row * p.N + col] = val;
+                }
+            }
+}
+
+// host side -------------------------------------------------------------------
+
+template <typename T>
+static inline bool aligned16(const T *p, int64_t ld)
+{
+    constexpr int PER = 16 / sizeof(T);
+    return ((uintptr_t)p % 16 == 0) && (ld % PER == 0);
+}
+
+template <typename T, int AOP, int BOP, int CM>
+static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
+{
+    using namespace gemm_detail;
+    if (p.M <= 0 || p.N <= 0)
+        return CHOL_OK;
+    p.vec = aligned16(p.a, p.lda) && aligned16(p.b, p.ldb);
+    const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
+    const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
+    hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1)),
+                       dim3(NT), 0, st, p);
+    CHOL_LAUNCH_CHECK();
+    return CHOL_OK;
+}
+
+} // namespace chol

@@ -50,14 +50,14 @@ Scope::Scope(int id_, hipStream_t st_, double work_) : id(id_), st(st_), work(wo
         a = b = nullptr;
         return;
     }
-    hipEventRecord(a, st);
+    (void)hipEventRecord(a, st);
 }
 
 Scope::~Scope()
 {
     if (!a || !b)
         return;
-    hipEventRecord(b, st);
+    (void)hipEventRecord(b, st);
     std::lock_guard<std::mutex> lk(g_mu);
     g_recs.push_back(Rec{id, a, b, work});
 }

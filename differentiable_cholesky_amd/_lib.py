@@ -51,7 +51,7 @@ def _load() -> ctypes.CDLL:
     lib.chol_abi_version.restype = ctypes.c_int
     lib.chol_abi_version.argtypes = []
     lib.chol_profile_start.restype = st
-    lib.chol_profile_start.argtypes = []
+    lib.chol_profile_start.argtypes = [ctypes.c_uint32]
     lib.chol_profile_stop.restype = st
     lib.chol_profile_stop.argtypes = [ctypes.c_int32, vp, vp, vp]
     return lib

@@ -27,16 +27,13 @@
 #include "common.hpp"
 #include "gemm.hpp"
 #include "profile.hpp"
+#include "side.hpp"
 
 namespace chol {
 
 template <typename T>
 chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base,
                        hipStream_t st);
-template <typename T>
-chol_status small_potrf_adjoint(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
-                                const T *adjL, int64_t ldal, int64_t sAL, T *adjA, int64_t ldaa,
-                                int64_t sAA, int accumulate, hipStream_t st);
 
 // ------------------------------------------------------------ elementwise ----
 enum { TRI_COPY_LOWER = 0, TRI_ZERO_UPPER = 1, TRI_ADD_LOWER = 2 };
@@ -197,13 +194,6 @@ k_splitk_reduce(int M, int N, int splits, const T *part, T *c, int64_t ldc)
     c[(int64_t)r * ldc + col] -= s;
 }
 
-// Split of a long contraction so that about two blocks per CU are busy.
-static inline int split_count(int64_t tiles, int64_t K, int max_splits)
-{
-    int s = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
-    s = (int)std::min<int64_t>(s, std::max<int64_t>(1, K / 256));
-    return s;
-}
 static inline int split_chunk(int64_t K, int splits)
 {
     int c = (int)((K + splits - 1) / splits);
@@ -211,36 +201,53 @@ static inline int split_chunk(int64_t K, int splits)
 }
 
 // ------------------------------------------------------------- forward ----
+// Two library streams: `sx` (all but a few CUs) runs every kernel that spans
+// the matrix -- panel solve, update of the next tile column, update of the
+// rest -- in order; `sc` runs only the one-block kernels of the next tile
+// column (diagonal factor and its inverse), which find free CUs among the
+// reserved ones while sx updates the rest of the trailing matrix:
+//   sx: [wait diag(k)] solve(k) -> next(k) -> {record} -> rest(k) -> ...
+//   sc: [wait next(k)] diag(k+1) + inverse(k+1) -> {record diag(k+1)}
 template <typename T>
-chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info, int nb,
-                          hipStream_t st)
+static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info,
+                                    int nb, hipStream_t sc, hipStream_t sx, hipEvent_t e_diag, hipEvent_t e_next)
 {
     chol_status s;
     if (A != L) {
-        if ((s = tri_op<T, TRI_COPY_LOWER>(n, A, lda, L, ldl, st)) != CHOL_OK)
+        if ((s = tri_op<T, TRI_COPY_LOWER>(n, A, lda, L, ldl, sc)) != CHOL_OK)
             return s;
     }
     const int64_t K = (n + nb - 1) / nb;
+    // diagonal factor (and inverse, if a panel follows) of tile column k, on sc
+    auto diag_step = [&](int64_t k) -> chol_status {
+        const int64_t k0 = k * nb;
+        const int kb = (int)std::min<int64_t>(nb, n - k0);
+        const double kb3 = (double)kb * kb * kb;
+        chol_status r;
+        {
+            prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, kb3 / 3);
+            if ((r = diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, k == 0 ? 1 : 2, k0, sc)) != CHOL_OK)
+                return r;
+        }
+        if (k0 + kb < n) {
+            prof::Scope ps(CHOL_K_DIAG_INVERSE, sc, kb3 / 3);
+            hipLaunchKernelGGL((k_trinv<T>), dim3(1), dim3(256), 0, sc, n, nb, k0, (int64_t)nb, L, ldl, 0,
+                               (T *)nullptr, (int64_t)0, (int64_t)0);
+            CHOL_LAUNCH_CHECK();
+        }
+        return CHOL_OK;
+    };
+    if ((s = diag_step(0)) != CHOL_OK)
+        return s;
     for (int64_t k = 0; k < K; ++k) {
         const int64_t k0 = k * nb;
         const int kb = (int)std::min<int64_t>(nb, n - k0);
         const int64_t r0 = k0 + kb, m = n - r0;
-        T *Wkk = L + k0 * ldl + k0;
-        const double kb3 = (double)kb * kb * kb;
-        {
-            prof::Scope ps(CHOL_K_DIAG_FACTOR, st, kb3 / 3);
-            if ((s = diag_potrf<T>(kb, Wkk, ldl, info, k == 0 ? 1 : 2, k0, st)) != CHOL_OK)
-                return s;
-        }
         if (m == 0)
             break;
-        // inverse of L_kk, transposed into the tile's strict upper triangle
-        {
-            prof::Scope ps(CHOL_K_DIAG_INVERSE, st, kb3 / 3);
-            hipLaunchKernelGGL((k_trinv<T>), dim3(1), dim3(256), 0, st, n, nb, k0, (int64_t)nb, L, ldl, 0,
-                               (T *)nullptr, (int64_t)0, (int64_t)0);
-            CHOL_LAUNCH_CHECK();
-        }
+        T *Wkk = L + k0 * ldl + k0;
+        if (stream_join(sx, sc, e_diag) != hipSuccess)
+            return CHOL_ERR_HIP;
         // panel: L_ik = W_ik * Linv^T  (in place; one block spans the full panel width)
         {
             GemmArgs<T> p{};
@@ -248,34 +255,79 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
             p.a = L + r0 * ldl + k0; p.lda = ldl;
             p.b = Wkk; p.ldb = ldl;
             p.c = L + r0 * ldl + k0; p.ldc = ldl;
-            prof::Scope ps(CHOL_K_PANEL_SOLVE, st, (double)m * kb * kb);
-            if ((s = gemm<T, OP_MK, OP_KM_INVT, C_STORE>(p, 1, st)) != CHOL_OK)
+            prof::Scope ps(CHOL_K_PANEL_SOLVE, sx, (double)m * kb * kb);
+            if ((s = gemm<T, OP_MK, OP_KM_INVT, C_STORE>(p, 1, sx)) != CHOL_OK)
                 return s;
         }
-        // trailing: W22 lower -= P P^T
+        const T *P = L + r0 * ldl + k0;          // solved panel, m x kb
+        const int kn = (int)std::min<int64_t>(nb, m);
+        const int64_t m2 = m - kn;
+        // next tile column: W[r0:, r0:r0+kn] (lower part) -= P P[0:kn]^T
         {
             GemmArgs<T> p{};
-            p.M = (int)m; p.N = (int)m; p.K = kb;
-            p.a = L + r0 * ldl + k0; p.lda = ldl;
-            p.b = L + r0 * ldl + k0; p.ldb = ldl;
+            p.M = (int)m; p.N = kn; p.K = kb;
+            p.a = P; p.lda = ldl;
+            p.b = P; p.ldb = ldl;
             p.c = L + r0 * ldl + r0; p.ldc = ldl;
+            prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, (double)kn * (kn + 1) * kb + 2.0 * m2 * kn * kb);
+            if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx)) != CHOL_OK)
+                return s;
+        }
+        // the next tile column's one-block kernels start on sc ...
+        if (stream_join(sc, sx, e_next) != hipSuccess)
+            return CHOL_ERR_HIP;
+        if ((s = diag_step(k + 1)) != CHOL_OK)
+            return s;
+        // ... while sx updates the rest: lower part of W[r0+kn:, r0+kn:] -= P2 P2^T
+        if (m2 > 0) {
+            const T *P2 = P + (int64_t)kn * ldl;
+            GemmArgs<T> p{};
+            p.M = (int)m2; p.N = (int)m2; p.K = kb;
+            p.a = P2; p.lda = ldl;
+            p.b = P2; p.ldb = ldl;
+            p.c = L + (r0 + kn) * ldl + r0 + kn; p.ldc = ldl;
             p.tri = 1;
-            prof::Scope ps(CHOL_K_TRAILING_UPDATE, st, (double)m * (m + 1) * kb);
-            if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
+            prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, (double)m2 * (m2 + 1) * kb);
+            if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx)) != CHOL_OK)
                 return s;
         }
     }
-    return tri_op<T, TRI_ZERO_UPPER>(n, nullptr, 0, L, ldl, st);
+    if (stream_join(sc, sx, e_next) != hipSuccess)
+        return CHOL_ERR_HIP;
+    return tri_op<T, TRI_ZERO_UPPER>(n, nullptr, 0, L, ldl, sc);
+}
+
+template <typename T>
+chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info, int nb,
+                          hipStream_t st)
+{
+    Side *sd = side_resources();
+    if (!sd)
+        return CHOL_ERR_HIP;
+    std::lock_guard<std::mutex> lk(sd->mu);
+    // both library streams start after the caller's earlier work; the caller's
+    // stream resumes after both are done
+    if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
+        return CHOL_ERR_HIP;
+    const chol_status s = blocked_potrf_on<T>(n, A, lda, L, ldl, info, nb, sd->chain, sd->x, sd->ev[0], sd->ev[1]);
+    const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
+                        stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
+    if (s != CHOL_OK)
+        return s;
+    return joined ? CHOL_OK : CHOL_ERR_HIP;
 }
 
 // ------------------------------------------------------------- adjoint ----
-// Workspace layout (bytes, each part 256-aligned):
-//   [Wb : n*n]  (absent when the gradient is formed directly in adj_A)
-//   [inv: K * nb * nb]   inverses of the diagonal tiles of L
-//   [part: SPLITS * nb * nb]  split-K partial products
+// Workspace layout (each part 256-byte aligned):
+//   [Wb    : n * n]                         running gradient (absent when formed in adj_A)
+//   [inv   : K * nb * nb]                   inverses of the diagonal tiles of L
+//   [part_x: SIDE_SPLIT_MAX * n * nb]       split partials of the large symmetric product
+//   [part_b: (TILE_SPLIT_MAX + 1) * nb * nb] split partials of tile-sized products, plus
+//                                           the slot the tile adjoint adds
+//   [part_c: 2 * nb * nb]                   the tile adjoint's scratch tiles
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-static const int ADJ_SPLIT_MAX = 64;     // splits of the tile-sized product Wb_kk -= tril(X^T L)
-static const int R1_SPLIT_MAX = 8;       // splits of the panel product Wb_panel -= Sym(Wb22) L
+static const int TILE_SPLIT_MAX = 256;   // splits of tile-sized products with a long contraction
+static const int SIDE_SPLIT_MAX = 8;     // splits of the large symmetric product
 
 size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
 {
@@ -284,56 +336,182 @@ size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
     if (need_wb)
         s += align256((size_t)n * n * esize);
     s += align256((size_t)K * nb * nb * esize);
-    s += align256(std::max((size_t)ADJ_SPLIT_MAX * nb * nb, (size_t)R1_SPLIT_MAX * n * nb) * esize);
+    s += align256((size_t)SIDE_SPLIT_MAX * n * nb * esize);
+    s += align256((size_t)(TILE_SPLIT_MAX + 1) * nb * nb * esize);
+    s += align256((size_t)2 * nb * nb * esize);
     return s;
 }
 
-// Adjoint of chol on one kb x kb diagonal tile, in place on Wb (lower):
-// the blocked reverse steps again with 64-wide sub-tiles, the 64-edge tile
-// kernel at the leaves.  inv holds L^{-1} of this tile (its diagonal
-// sub-blocks are the sub-tiles' inverses).
-template <typename T>
-static chol_status diag_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv,
-                                int64_t ldi, hipStream_t st)
+// Split count and chunk for a tile-sized product with contraction length K.
+static inline int tile_splits(int64_t K, int64_t &chunk)
 {
-    if (kb <= 64)
-        return small_potrf_adjoint<T>(kb, 1, L, ldl, 0, Wb, ldw, 0, Wb, ldw, 0, 0, st);
-    chol_status s;
-    const int h = 64, m = kb - h;
-    // lower sub-tile first (reverse order)
-    if ((s = diag_adjoint<T>(m, L + (int64_t)h * ldl + h, ldl, Wb + (int64_t)h * ldw + h, ldw,
-                             inv + (int64_t)h * ldi + h, ldi, st)) != CHOL_OK)
-        return s;
-    GemmArgs<T> p{};
-    // Wb10 -= Sym(Wb11) L10
-    p.M = m; p.N = h; p.K = m;
-    p.a = Wb + (int64_t)h * ldw + h; p.lda = ldw;
-    p.b = L + (int64_t)h * ldl; p.ldb = ldl;
-    p.c = Wb + (int64_t)h * ldw; p.ldc = ldw;
-    if ((s = gemm<T, OP_SYM, OP_KM, C_SUB>(p, 1, st)) != CHOL_OK)
-        return s;
-    // X = Wb10 L00^{-1}  (in place: one block spans the full width)
-    p = GemmArgs<T>{};
-    p.M = m; p.N = h; p.K = h;
-    p.a = Wb + (int64_t)h * ldw; p.lda = ldw;
-    p.b = inv; p.ldb = ldi;
-    p.c = Wb + (int64_t)h * ldw; p.ldc = ldw;
-    if ((s = gemm<T, OP_MK, OP_KM_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
-        return s;
-    // Wb00 -= tril(X^T L10)
-    p = GemmArgs<T>{};
-    p.M = h; p.N = h; p.K = m;
-    p.a = Wb + (int64_t)h * ldw; p.lda = ldw;
-    p.b = L + (int64_t)h * ldl; p.ldb = ldl;
-    p.c = Wb; p.ldc = ldw;
-    if ((s = gemm<T, OP_KM, OP_KM, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
-        return s;
-    return diag_adjoint<T>(h, L, ldl, Wb, ldw, inv, ldi, st);
+    int splits = (int)std::max<int64_t>(1, std::min<int64_t>(TILE_SPLIT_MAX, (K + 127) / 128));
+    chunk = split_chunk(K, splits);
+    return (int)((K + chunk - 1) / chunk);
 }
 
+// C (M x N) -= Sym(S)[0:M, 0:K] B with S symmetric stored as its lower triangle
+// (diagonal doubled by the operand) and B k-major; the contraction is split so
+// that about two blocks per CU work, and the partials are summed in a fixed
+// order, so the result does not depend on scheduling.
 template <typename T>
-chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
-                            int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t st)
+static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, const T *B, int64_t ldb, T *C,
+                               int64_t ldc, T *part, int max_splits, int min_chunk, hipStream_t st)
+{
+    if (M <= 0 || N <= 0 || K <= 0)
+        return CHOL_OK;
+    GemmArgs<T> p{};
+    p.M = M; p.N = N; p.K = K;
+    p.a = S; p.lda = lds;
+    p.b = B; p.ldb = ldb;
+    p.c = C; p.ldc = ldc;
+    // at most one wave of blocks (two per CU), minus a few slots for the
+    // one-block kernels running beside it: a partial second wave would double
+    // the time of the launch
+    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t slots = 2 * 256 - 32;
+    int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, slots / tiles));
+    splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, K / min_chunk));
+    p.kchunk = split_chunk(K, splits);
+    const int used = (K + p.kchunk - 1) / p.kchunk;
+    p.part = part;
+    chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st);
+    if (s != CHOL_OK)
+        return s;
+    const int64_t tot = (int64_t)M * N;
+    hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N, used,
+                       (const T *)part, C, ldc);
+    CHOL_LAUNCH_CHECK();
+    return CHOL_OK;
+}
+
+// Adjoint of chol on one kb x kb diagonal tile (kb <= 128), in place on the
+// lower triangle of Wb, from the tile's factor L and its inverse Linv:
+//   P = Phi(L^T tril(Wb))     lower triangle, into scratch s1
+//   V = Sym(P) Linv           Sym(P) = P + P^T = Psi (diagonal M_ii); into s2
+//   G = Phi(Linv^T V)         lower triangle, into Wb
+// and, when `slot` is given, the one term of the previous tile column's
+// trailing-update adjoint that needs G:  slot = Sym(G) Lnext  (kb x nj, row
+// major), with Lnext = L[this tile's rows, previous tile column].
+// Each stage is one 128 x 128 x 128 matrix-core product of the whole block;
+// between stages the block's global writes are made visible by the barrier.
+template <typename T>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv, int64_t ldi, T *s1, T *s2,
+               int64_t lds_scr, const T *Lnext, int nj, T *slot)
+{
+    using namespace gemm_detail;
+    typedef typename Acc<T>::type acc_t;
+    __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
+    acc_t acc[4][4];
+    auto zero = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = acc_t{0, 0, 0, 0};
+    };
+    // stage 1: M = L^T tril(Wb); A(r, t) = L[t][r] (t >= r), B(t, c) = Wb[t][c] (t >= c)
+    zero();
+    {
+        Operand<T, OP_KM_LOWER> A{L, ldl, 0, kb, 0};
+        Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, 0};
+        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false>(acc, A, B, 0, kb, lds);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int r, c;
+                acc_pos<T>(i, j, v, r, c);
+                if (r < kb && c <= r)
+                    s1[(int64_t)r * lds_scr + c] = (r == c) ? T(0.5) * acc[i][j][v] : acc[i][j][v];
+            }
+    __threadfence_block();
+    __syncthreads();
+    // stage 2: V = Sym(P) Linv; B(t, c) = Linv[t][c] (t >= c)
+    zero();
+    {
+        Operand<T, OP_SYM> A{s1, lds_scr, 0, kb, 0};
+        Operand<T, OP_KM_LOWER> B{inv, ldi, 0, kb, 0};
+        tile_mma<T, OP_SYM, OP_KM_LOWER, false>(acc, A, B, 0, kb, lds);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int r, c;
+                acc_pos<T>(i, j, v, r, c);
+                if (r < kb && c < kb)
+                    s2[(int64_t)r * lds_scr + c] = acc[i][j][v];
+            }
+    __threadfence_block();
+    __syncthreads();
+    // stage 3: Z = Linv^T V; A(r, t) = Linv[t][r] (t >= r), B(t, c) = V[t][c]
+    zero();
+    {
+        Operand<T, OP_KM_LOWER> A{inv, ldi, 0, kb, 0};
+        Operand<T, OP_KM> B{s2, lds_scr, 0, kb, 0};
+        tile_mma<T, OP_KM_LOWER, OP_KM, false>(acc, A, B, 0, kb, lds);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int r, c;
+                acc_pos<T>(i, j, v, r, c);
+                if (r < kb && c <= r)
+                    Wb[(int64_t)r * ldw + c] = (r == c) ? T(0.5) * acc[i][j][v] : acc[i][j][v];
+            }
+    if (!slot)
+        return;
+    __threadfence_block();
+    __syncthreads();
+    // stage 4: slot = Sym(G) Lnext; A = Sym of the lower triangle just written,
+    // B(t, c) = Lnext[t][c]
+    zero();
+    {
+        Operand<T, OP_SYM> A{Wb, ldw, 0, kb, 0};
+        Operand<T, OP_KM> B{Lnext, ldl, 0, nj, 0};
+        tile_mma<T, OP_SYM, OP_KM, false>(acc, A, B, 0, kb, lds);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int r, c;
+                acc_pos<T>(i, j, v, r, c);
+                if (r < kb && c < nj)
+                    slot[(int64_t)r * nj + c] = acc[i][j][v];
+            }
+}
+
+// Reverse sweep over the tile columns with depth-1 look-ahead.  With
+// Bk = rows of tile column k+1 and Rk = rows past it, tile column k's adjoint
+// of the trailing update, Wb_panel(k) -= Sym(Wb22(k)) L_panel(k), is the sum of
+//   early:  Wb[Rk]  -= Sym(Wb[Rk, Rk]) L[Rk]     needs Wb22(k+1): final after
+//                                                tile column k+2 is done
+//   late_a: Wb[Rk]  -= X(k+1) L[Bk]              needs X(k+1) = Wb_panel(k+1)
+//   late_b: Wb[Bk]  -= X(k+1)^T L[Rk]                after its panel-solve adjoint
+//   late_c: Wb[Bk]  -= Sym(G(k+1)) L[Bk]         needs the tile adjoint G(k+1)
+// (all L terms restricted to tile column k).  The wide stream sx runs, per
+// tile column k: the reduction that lands late_b and late_c, the panel-solve
+// adjoint X(k) = Wb_panel(k) Linv_k, the tile-sized product Wb_kk -= tril(X^T L),
+// then -- while the one-block stream sc computes the tile adjoint G(k), with
+// late_c of tile column k-1 as its last stage -- late_a, late_b and early of
+// tile column k-1.
+template <typename T>
+static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
+                                      int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t sc,
+                                      hipStream_t sx, hipEvent_t e_tile, hipEvent_t e_wide)
 {
     chol_status s;
     const int64_t K = (n + nb - 1) / nb;
@@ -351,95 +529,151 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
     }
     T *inv = (T *)w;
     w += align256((size_t)K * nb * nb * sizeof(T));
-    T *part = (T *)w;
+    T *part_x = (T *)w;
+    w += align256((size_t)SIDE_SPLIT_MAX * n * nb * sizeof(T));
+    T *part_b = (T *)w;
+    w += align256((size_t)(TILE_SPLIT_MAX + 1) * nb * nb * sizeof(T));
+    T *part_c = (T *)w;
 
     if ((const T *)Wb != adjL) {
-        if ((s = tri_op<T, TRI_COPY_LOWER>(n, adjL, ldal, Wb, ldw, st)) != CHOL_OK)
+        if ((s = tri_op<T, TRI_COPY_LOWER>(n, adjL, ldal, Wb, ldw, sx)) != CHOL_OK)
             return s;
     }
-    // inverses of every diagonal tile, all at once
     {
-        prof::Scope ps(CHOL_K_DIAG_INVERSE, st, (double)K * nb * nb * nb / 3);
-        hipLaunchKernelGGL((k_trinv<T>), dim3((unsigned)K), dim3(256), 0, st, n, nb, (int64_t)0, (int64_t)nb,
+        prof::Scope ps(CHOL_K_DIAG_INVERSE, sx, (double)K * nb * nb * nb / 3);
+        hipLaunchKernelGGL((k_trinv<T>), dim3((unsigned)K), dim3(256), 0, sx, n, nb, (int64_t)0, (int64_t)nb,
                            const_cast<T *>(L), ldl, 1, inv, (int64_t)nb * nb, (int64_t)nb);
         CHOL_LAUNCH_CHECK();
     }
 
+    int pending = -1;   // splits in part_b waiting for the tile adjoint's slot (-1: none)
     for (int64_t k = K - 1; k >= 0; --k) {
         const int64_t k0 = k * nb;
         const int kb = (int)std::min<int64_t>(nb, n - k0);
         const int64_t r0 = k0 + kb, m = n - r0;
+        const int kn = (int)std::min<int64_t>(nb, m);
         const T *Lkk = L + k0 * ldl + k0;
         T *Wkk = Wb + k0 * ldw + k0;
         const T *invk = inv + k * nb * nb;
+        const T *Lp = L + r0 * ldl + k0;       // L_panel, m x kb
+        T *Wp = Wb + r0 * ldw + k0;            // Wb_panel, m x kb
         if (m > 0) {
-            GemmArgs<T> p{};
-            // R1: Wb_panel -= Sym(Wb22) L_panel, the contraction over m split
-            // into partial products reduced in a fixed order
-            p.M = (int)m; p.N = kb; p.K = (int)m;
-            p.a = Wb + r0 * ldw + r0; p.lda = ldw;
-            p.b = L + r0 * ldl + k0; p.ldb = ldl;
-            p.c = Wb + r0 * ldw + k0; p.ldc = ldw;
+            // late_b and late_c of this tile column (the latter from tile column
+            // k+1's tile adjoint on sc) land in the first kn rows of Wb_panel
+            if (stream_join(sx, sc, e_tile) != hipSuccess)
+                return CHOL_ERR_HIP;
             {
-                prof::Scope ps(CHOL_K_ADJ_TRAILING, st, 2.0 * m * m * kb);
-                const int64_t tiles = ((m + 127) / 128) * ((kb + 127) / 128);
-                const int splits = split_count(tiles, m, R1_SPLIT_MAX);
-                p.kchunk = split_chunk(m, splits);
-                const int used = (int)((m + p.kchunk - 1) / p.kchunk);
-                p.part = part;
-                if ((s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st)) != CHOL_OK)
-                    return s;
-                const int64_t tot = m * kb;
-                hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
-                                   (int)m, kb, used, (const T *)part, p.c, ldw);
+                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 0.0);
+                const int64_t tot = (int64_t)kn * kb;
+                hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, sx,
+                                   kn, kb, pending + 1, (const T *)part_b, Wp, ldw);
                 CHOL_LAUNCH_CHECK();
             }
             // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block)
-            p = GemmArgs<T>{};
-            p.M = (int)m; p.N = kb; p.K = kb;
-            p.a = Wb + r0 * ldw + k0; p.lda = ldw;
-            p.b = invk; p.ldb = nb;
-            p.c = Wb + r0 * ldw + k0; p.ldc = ldw;
             {
-                prof::Scope ps(CHOL_K_ADJ_PANEL, st, (double)m * kb * kb);
-                if ((s = gemm<T, OP_MK, OP_KM_LOWER, C_STORE>(p, 1, st)) != CHOL_OK)
+                GemmArgs<T> p{};
+                p.M = (int)m; p.N = kb; p.K = kb;
+                p.a = Wp; p.lda = ldw;
+                p.b = invk; p.ldb = nb;
+                p.c = Wp; p.ldc = ldw;
+                prof::Scope ps(CHOL_K_ADJ_PANEL, sx, (double)m * kb * kb);
+                if ((s = gemm<T, OP_MK, OP_KM_LOWER, C_STORE>(p, 1, sx)) != CHOL_OK)
                     return s;
             }
             // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows
-            p = GemmArgs<T>{};
-            p.M = kb; p.N = kb; p.K = (int)m;
-            p.a = Wb + r0 * ldw + k0; p.lda = ldw;
-            p.b = L + r0 * ldl + k0; p.ldb = ldl;
-            prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, st, (double)m * kb * (kb + 1));
-            int splits = (int)std::min<int64_t>(ADJ_SPLIT_MAX, (m + 511) / 512);
-            if (splits <= 1) {
-                p.c = Wkk; p.ldc = ldw;
-                if ((s = gemm<T, OP_KM, OP_KM, C_SUB_LOWER>(p, 1, st)) != CHOL_OK)
-                    return s;
-            } else {
-                int chunk = (int)((m + splits - 1) / splits);
-                chunk = (chunk + 15) / 16 * 16;
-                splits = (int)((m + chunk - 1) / chunk);
-                p.kchunk = chunk;
-                p.part = part;
-                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, st)) != CHOL_OK)
+            {
+                GemmArgs<T> p{};
+                p.M = kb; p.N = kb; p.K = (int)m;
+                p.a = Wp; p.lda = ldw;
+                p.b = Lp; p.ldb = ldl;
+                prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, sx, (double)m * kb * (kb + 1));
+                int64_t chunk;
+                const int splits = tile_splits(m, chunk);
+                p.kchunk = (int)chunk;
+                p.part = part_b;
+                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sx)) != CHOL_OK)
                     return s;
                 const int64_t tot = (int64_t)kb * kb;
                 hipLaunchKernelGGL((k_splitk_reduce_lower<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256),
-                                   0, st, kb, splits, (const T *)part, Wkk, ldw);
+                                   0, sx, kb, splits, (const T *)part_b, Wkk, ldw);
                 CHOL_LAUNCH_CHECK();
             }
         }
-        // R3: the tile adjoint on the diagonal
+        // tile adjoint of tile column k on sc; its last stage is late_c of
+        // tile column k-1, written after the late_b partials of k-1
+        const int64_t j0 = k0 - nb;                 // previous tile column (if k >= 1)
+        int64_t late_b_chunk = 0;
+        const int late_b_splits = (k >= 1 && m > 0) ? tile_splits(m, late_b_chunk) : 0;
+        if (stream_join(sc, sx, e_wide) != hipSuccess)
+            return CHOL_ERR_HIP;
         {
-            prof::Scope ps(CHOL_K_ADJ_DIAG, st, 2.0 * kb * kb * kb / 3);
-            if ((s = diag_adjoint<T>(kb, Lkk, ldl, Wkk, ldw, invk, nb, st)) != CHOL_OK)
-                return s;
+            prof::Scope ps(CHOL_K_ADJ_DIAG, sc, 2.0 * kb * kb * kb / 3 + (k >= 1 ? 2.0 * kb * kb * nb : 0.0));
+            const T *Lnext = (k >= 1) ? L + k0 * ldl + j0 : nullptr;
+            T *slot = (k >= 1) ? part_b + (int64_t)late_b_splits * kb * nb : nullptr;
+            hipLaunchKernelGGL((k_tile_adjoint<T>), dim3(1), dim3(256), 0, sc, kb, Lkk, ldl, Wkk, ldw, invk,
+                               (int64_t)nb, part_c, part_c + (int64_t)nb * nb, (int64_t)nb, Lnext, nb, slot);
+            CHOL_LAUNCH_CHECK();
+        }
+        pending = (k >= 1) ? late_b_splits : -1;
+        if (k >= 1 && m > 0) {
+            const T *Lj = L + r0 * ldl + j0;        // L[rows past tile column k, tile column k-1]
+            // late_a(k-1): Wb[r0:, j] -= X(k) L[tile k, tile j]
+            {
+                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * m * kb * nb);
+                GemmArgs<T> p{};
+                p.M = (int)m; p.N = nb; p.K = kb;
+                p.a = Wp; p.lda = ldw;
+                p.b = L + k0 * ldl + j0; p.ldb = ldl;
+                p.c = Wb + r0 * ldw + j0; p.ldc = ldw;
+                if ((s = gemm<T, OP_MK, OP_KM, C_SUB>(p, 1, sx)) != CHOL_OK)
+                    return s;
+            }
+            // late_b(k-1) partials: X(k)^T L[r0:, tile j]  (kb x nb, contraction over m)
+            {
+                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * m * kb * nb);
+                GemmArgs<T> p{};
+                p.M = kb; p.N = nb; p.K = (int)m;
+                p.a = Wp; p.lda = ldw;
+                p.b = Lj; p.ldb = ldl;
+                p.kchunk = (int)late_b_chunk;
+                p.part = part_b;
+                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, late_b_splits, sx)) != CHOL_OK)
+                    return s;
+            }
+            // early(k-1): Wb[r0+kn':, j] -= Sym(Wb22(k)) L[r0:, j] restricted to rows and
+            // columns past tile column k, i.e. Wb22(k) itself
+            {
+                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * nb * (double)m * m);
+                if ((s = sym_product<T>((int)m, nb, (int)m, Wb + r0 * ldw + r0, ldw, Lj, ldl, Wb + r0 * ldw + j0,
+                                        ldw, part_x, SIDE_SPLIT_MAX, 256, sx)) != CHOL_OK)
+                    return s;
+            }
         }
     }
+    if (stream_join(sx, sc, e_tile) != hipSuccess)
+        return CHOL_ERR_HIP;
     if (need_wb)
-        return tri_op<T, TRI_ADD_LOWER>(n, Wb, ldw, adjA, ldaa, st);
+        return tri_op<T, TRI_ADD_LOWER>(n, Wb, ldw, adjA, ldaa, sx);
     return CHOL_OK;
+}
+
+template <typename T>
+chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
+                            int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t st)
+{
+    Side *sd = side_resources();
+    if (!sd)
+        return CHOL_ERR_HIP;
+    std::lock_guard<std::mutex> lk(sd->mu);
+    if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
+        return CHOL_ERR_HIP;
+    const chol_status s = blocked_adjoint_on<T>(n, L, ldl, adjL, ldal, adjA, ldaa, accumulate, nb, ws, sd->chain,
+                                                sd->x, sd->ev[0], sd->ev[1]);
+    const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
+                        stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
+    if (s != CHOL_OK)
+        return s;
+    return joined ? CHOL_OK : CHOL_ERR_HIP;
 }
 
 #define CHOL_INST(T)                                                                                     \

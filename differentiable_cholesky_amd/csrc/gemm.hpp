@@ -203,17 +203,94 @@ __device__ __forceinline__ int xcd_tile(int b, int nt)
 
 } // namespace gemm_detail
 
+// The K loop of one 128 x 128 tile: acc += (NEG ? -A : A) B over k in
+// [kbeg, kend), operands staged through `lds` (2 buffers x 2 operands x
+// BK * Pitch<T>::v elements).  Called by all 256 threads of the block.
+// A's global loads run two chunks ahead of the matrix cores (chunk c+1 waits
+// in one register set to be written to LDS while chunk c+2 is in flight in
+// the other); B, a panel that stays in L2, is fetched one chunk ahead.
+template <typename T, int AOP, int BOP, bool NEG>
+__device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
+                                         const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
+{
+    using namespace gemm_detail;
+    constexpr int PITCH = Pitch<T>::v, SZ = BK * PITCH;
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int wm = wave / 2, wn = wave % 2;
+    Vec8<T> ra0, ra1, rb;
+    if (kbeg < kend) {
+        A.fetch(ra0, tid, kbeg, kend);
+        B.fetch(rb, tid, kbeg, kend);
+        A.stash(ra0, lds, tid, kbeg);
+        B.stash(rb, lds + SZ, tid, kbeg);
+        if (kbeg + BK < kend) {
+            A.fetch(ra1, tid, kbeg + BK, kend);
+            B.fetch(rb, tid, kbeg + BK, kend);
+        }
+        if (kbeg + 2 * BK < kend)
+            A.fetch(ra0, tid, kbeg + 2 * BK, kend);
+    }
+    __syncthreads();
+    int c = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += BK, ++c) {
+        const int buf = c & 1;
+        const T *SA = lds + buf * 2 * SZ;
+        const T *SB = SA + SZ;
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 4) {
+            const int kr = kk + lane / 16;
+            T af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = SA[kr * PITCH + wm * 64 + i * 16 + lane % 16];
+                if (NEG)
+                    af[i] = -af[i];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = SB[kr * PITCH + wn * 64 + j * 16 + lane % 16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = mfma16x16x4(af[i], bf[j], acc[i][j]);
+        }
+        if (k0 + BK < kend) {
+            T *D = lds + (buf ^ 1) * 2 * SZ;
+            B.stash(rb, D + SZ, tid, k0 + BK);
+            if (k0 + 2 * BK < kend)
+                B.fetch(rb, tid, k0 + 2 * BK, kend);
+            // chunk c+1 of A sits in set (c+1)&1; refill that set with chunk c+3
+            if ((c & 1) == 0) {
+                A.stash(ra1, D, tid, k0 + BK);
+                if (k0 + 3 * BK < kend)
+                    A.fetch(ra1, tid, k0 + 3 * BK, kend);
+            } else {
+                A.stash(ra0, D, tid, k0 + BK);
+                if (k0 + 3 * BK < kend)
+                    A.fetch(ra0, tid, k0 + 3 * BK, kend);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Position of accumulator element (i, j, v) of this thread inside the 128 x 128 tile.
+template <typename T>
+__device__ __forceinline__ void acc_pos(int i, int j, int v, int &row, int &col)
+{
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    row = (wave / 2) * 64 + i * 16 + Acc<T>::row(lane, v);
+    col = (wave % 2) * 64 + j * 16 + lane % 16;
+}
+
 template <typename T, int AOP, int BOP, int CM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm(GemmArgs<T> p)
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
-    constexpr int PITCH = Pitch<T>::v;
-    __shared__ T lds[2][2][BK * PITCH];    // [buffer][operand A/B]
-
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int wm = wave / 2, wn = wave % 2;
+    __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
 
     // tile coordinates
     int I, J;
@@ -239,9 +316,6 @@ k_gemm(GemmArgs<T> p)
         kend = min(p.K, kbeg + p.kchunk);
     }
 
-    Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec};
-    Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec};
-
     // C -= AB runs as acc = C, acc += (-A) B: the accumulators start from C,
     // so the epilogue is a plain store and no accumulator has to leave the
     // matrix-core registers for a read-modify-write.
@@ -255,57 +329,19 @@ k_gemm(GemmArgs<T> p)
             for (int v = 0; v < 4; ++v) {
                 T x = T(0);
                 if (FROM_C) {
-                    const int row = r0 + wm * 64 + i * 16 + Acc<T>::row(lane, v);
-                    const int col = c0 + wn * 64 + j * 16 + lane % 16;
+                    int row, col;
+                    acc_pos<T>(i, j, v, row, col);
+                    row += r0;
+                    col += c0;
                     if (row < p.M && col < p.N)
                         x = p.c[(int64_t)row * p.ldc + col];
                 }
                 acc[i][j][v] = x;
             }
 
-    Vec8<T> ra, rb;
-    int buf = 0;
-    if (kbeg < kend) {
-        A.fetch(ra, tid, kbeg, kend);
-        B.fetch(rb, tid, kbeg, kend);
-        A.stash(ra, lds[0][0], tid, kbeg);
-        B.stash(rb, lds[0][1], tid, kbeg);
-    }
-    __syncthreads();
-    for (int k0 = kbeg; k0 < kend; k0 += BK) {
-        const bool more = k0 + BK < kend;
-        if (more) {
-            A.fetch(ra, tid, k0 + BK, kend);
-            B.fetch(rb, tid, k0 + BK, kend);
-        }
-        const T *SA = lds[buf][0];
-        const T *SB = lds[buf][1];
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 4) {
-            const int kr = kk + lane / 16;
-            T af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = SA[kr * PITCH + wm * 64 + i * 16 + lane % 16];
-                if (FROM_C)
-                    af[i] = -af[i];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = SB[kr * PITCH + wn * 64 + j * 16 + lane % 16];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = mfma16x16x4(af[i], bf[j], acc[i][j]);
-        }
-        if (more) {
-            A.stash(ra, lds[buf ^ 1][0], tid, k0 + BK);
-            B.stash(rb, lds[buf ^ 1][1], tid, k0 + BK);
-        }
-        __syncthreads();
-        buf ^= 1;
-    }
+    Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec};
+    Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec};
+    tile_mma<T, AOP, BOP, FROM_C>(acc, A, B, kbeg, kend, lds);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -313,8 +349,10 @@ k_gemm(GemmArgs<T> p)
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = r0 + wm * 64 + i * 16 + Acc<T>::row(lane, v);
-                const int col = c0 + wn * 64 + j * 16 + lane % 16;
+                int row, col;
+                acc_pos<T>(i, j, v, row, col);
+                row += r0;
+                col += c0;
                 if (row >= p.M || col >= p.N)
                     continue;
                 const T val = acc[i][j][v];

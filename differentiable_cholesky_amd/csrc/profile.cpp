@@ -9,7 +9,7 @@
 namespace chol {
 namespace prof {
 
-std::atomic<bool> g_on{false};
+std::atomic<uint32_t> g_mask{0};
 
 namespace {
 struct Rec {
@@ -37,7 +37,7 @@ hipEvent_t take()
 
 Scope::Scope(int id_, hipStream_t st_, double work_) : id(id_), st(st_), work(work_)
 {
-    if (id < 0 || !g_on.load(std::memory_order_relaxed))
+    if (id < 0 || id >= 32 || !((g_mask.load(std::memory_order_relaxed) >> id) & 1u))
         return;
     std::lock_guard<std::mutex> lk(g_mu);
     a = take();
@@ -69,7 +69,7 @@ using namespace chol::prof;
 
 extern "C" {
 
-chol_status chol_profile_start(void)
+chol_status chol_profile_start(uint32_t mask)
 {
     std::lock_guard<std::mutex> lk(g_mu);
     for (auto &r : g_recs) {
@@ -77,13 +77,13 @@ chol_status chol_profile_start(void)
         g_pool.push_back(r.b);
     }
     g_recs.clear();
-    g_on.store(true);
+    g_mask.store(mask);
     return CHOL_OK;
 }
 
 chol_status chol_profile_stop(int32_t max_ids, int64_t *count, double *ms, double *work)
 {
-    g_on.store(false);
+    g_mask.store(0);
     std::lock_guard<std::mutex> lk(g_mu);
     if (max_ids < 0 || (max_ids > 0 && (!count || !ms || !work)))
         return CHOL_ERR_INVALID_VALUE;

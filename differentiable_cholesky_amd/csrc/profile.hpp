@@ -11,7 +11,7 @@
 namespace chol {
 namespace prof {
 
-extern std::atomic<bool> g_on;
+extern std::atomic<uint32_t> g_mask;   // families being timed, 0: timing off
 
 struct Scope {
     int id;

@@ -1,0 +1,39 @@
+#include "side.hpp"
+
+
+namespace chol {
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+Side g_side[MAX_DEVICES];
+std::once_flag g_once[MAX_DEVICES];
+} // namespace
+
+Side *side_resources()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+        return nullptr;
+    Side &s = g_side[dev];
+    std::call_once(g_once[dev], [&s]() {
+        if (hipStreamCreateWithFlags(&s.chain, hipStreamNonBlocking) != hipSuccess)
+            return;
+        if (hipStreamCreateWithFlags(&s.x, hipStreamNonBlocking) != hipSuccess)
+            return;
+        for (auto &e : s.ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+                return;
+        s.ok = true;
+    });
+    return s.ok ? &s : nullptr;
+}
+
+hipError_t stream_join(hipStream_t waiter, hipStream_t src, hipEvent_t ev)
+{
+    hipError_t e = hipEventRecord(ev, src);
+    if (e != hipSuccess)
+        return e;
+    return hipStreamWaitEvent(waiter, ev, 0);
+}
+
+} // namespace chol

@@ -1,0 +1,31 @@
+// Streams on which the blocked factor and adjoint run, so that the large
+// trailing products (wide stream `x`) overlap the one-block kernels of the
+// next tile column (stream `chain`).  Both are created on first use per
+// device and kept for the life of the process, at default priority and
+// non-blocking with respect to the null stream; work is ordered against the
+// caller's stream and between the two streams by events only.  The large
+// products are launched with at most one wave of blocks, short of a few
+// block slots that stay free for the one-block kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+namespace chol {
+
+struct Side {
+    hipStream_t chain = nullptr;   // one-block kernels
+    hipStream_t x = nullptr;       // kernels that span the matrix
+    hipEvent_t ev[6] = {};
+    std::mutex mu;                 // one blocked call enqueues on these resources at a time
+    bool ok = false;
+};
+
+// Resources of the current device, or nullptr if they could not be created.
+Side *side_resources();
+
+// Enqueue-side helpers: make `waiter` wait for everything enqueued so far on `src`.
+hipError_t stream_join(hipStream_t waiter, hipStream_t src, hipEvent_t ev);
+
+} // namespace chol

@@ -169,9 +169,11 @@ chol_status chol_wave_dot_fwd_adj(chol_dtype dtype, int64_t n,
 
 /*
  * Timing hook (diagnostics; used by the benchmark for per-kernel rooflines).
- * chol_profile_start() clears previous records and turns timing on for all
- * later calls in this process: each launch of a kernel family below is then
- * bracketed by a pair of HIP events recorded on the stream it runs on.
+ * chol_profile_start(mask) clears previous records and turns timing on for
+ * later calls in this process: each launch of a kernel family i below with
+ * bit i set in `mask` is then bracketed by a pair of HIP events recorded on
+ * the stream it runs on (CHOL_PROFILE_ALL selects every family).  Timing only
+ * the families of interest keeps the event records out of the others' path.
  * chol_profile_stop() turns timing off, waits for the recorded events, and
  * writes, for family i < max_ids, the number of launches count[i], their summed
  * duration ms[i] and their summed algorithmic work work[i] (flops for the
@@ -195,7 +197,8 @@ typedef enum {
     CHOL_K_COUNT = 11
 } chol_kernel_family;
 
-chol_status chol_profile_start(void);
+#define CHOL_PROFILE_ALL 0xffffffffu
+chol_status chol_profile_start(uint32_t mask);
 chol_status chol_profile_stop(int32_t max_ids, int64_t *count, double *ms, double *work);
 
 /* Human-readable name of a status code (static string, never NULL). */

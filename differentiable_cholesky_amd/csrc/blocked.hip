@@ -201,11 +201,11 @@ static inline int split_chunk(int64_t K, int splits)
 }
 
 // ------------------------------------------------------------- forward ----
-// Two library streams: `sx` (all but a few CUs) runs every kernel that spans
-// the matrix -- panel solve, update of the next tile column, update of the
-// rest -- in order; `sc` runs only the one-block kernels of the next tile
-// column (diagonal factor and its inverse), which find free CUs among the
-// reserved ones while sx updates the rest of the trailing matrix:
+// Two library streams: `sx` runs every kernel that spans the matrix -- panel
+// solve, update of the next tile column, update of the rest -- in order; `sc`
+// runs only the one-block kernels of the next tile column (diagonal factor and
+// its inverse), which the hardware schedules beside the blocks of the update
+// of the rest on sx:
 //   sx: [wait diag(k)] solve(k) -> next(k) -> {record} -> rest(k) -> ...
 //   sc: [wait next(k)] diag(k+1) + inverse(k+1) -> {record diag(k+1)}
 template <typename T>
@@ -352,8 +352,8 @@ static inline int tile_splits(int64_t K, int64_t &chunk)
 
 // C (M x N) -= Sym(S)[0:M, 0:K] B with S symmetric stored as its lower triangle
 // (diagonal doubled by the operand) and B k-major; the contraction is split so
-// that about two blocks per CU work, and the partials are summed in a fixed
-// order, so the result does not depend on scheduling.
+// that the launch fills at most one wave of blocks, and the partials are summed
+// in a fixed order, so the result does not depend on scheduling.
 template <typename T>
 static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, const T *B, int64_t ldb, T *C,
                                int64_t ldc, T *part, int max_splits, int min_chunk, hipStream_t st)

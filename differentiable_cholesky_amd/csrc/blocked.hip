@@ -32,7 +32,7 @@
 namespace chol {
 
 template <typename T>
-chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base,
+chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, bool inverse,
                        hipStream_t st);
 
 // ------------------------------------------------------------ elementwise ----
@@ -99,12 +99,20 @@ k_trinv(int64_t n_total, int nb, int64_t tile0, int64_t step, T *W, int64_t ld, 
     const int64_t k0 = tile0 + (int64_t)blockIdx.x * step;
     const int kb = (int)std::min<int64_t>(nb, n_total - k0);
     const T *Lkk = W + k0 * ld + k0;
-    for (int idx = tid; idx < NP * NP; idx += 256) {
-        const int i = idx / NP, k = idx % NP;
-        T v = (i == k) ? T(1) : T(0);
+    // all of the thread's loads are issued before the first LDS write
+    constexpr int PER = NP * NP / 256;
+    T stage[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int idx = tid + 256 * q, i = idx / NP, k = idx % NP;
+        stage[q] = (i == k) ? T(1) : T(0);
         if (i < kb && k <= i)
-            v = Lkk[(int64_t)i * ld + k];
-        ls[i * LP + k] = v;
+            stage[q] = Lkk[(int64_t)i * ld + k];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int idx = tid + 256 * q, i = idx / NP, k = idx % NP;
+        ls[i * LP + k] = stage[q];
     }
     T x[E][E];
 #pragma unroll
@@ -204,13 +212,14 @@ static inline int split_chunk(int64_t K, int splits)
 // Two library streams: `sx` runs every kernel that spans the matrix -- panel
 // solve, update of the next tile column, update of the rest -- in order; `sc`
 // runs only the one-block kernels of the next tile column (diagonal factor and
-// its inverse), which the hardware schedules beside the blocks of the update
-// of the rest on sx:
+// its inverse); the update of the rest runs as persistent blocks that leave a
+// few block slots free, so those kernels start at once beside it:
 //   sx: [wait diag(k)] solve(k) -> next(k) -> {record} -> rest(k) -> ...
 //   sc: [wait next(k)] diag(k+1) + inverse(k+1) -> {record diag(k+1)}
 template <typename T>
 static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info,
-                                    int nb, hipStream_t sc, hipStream_t sx, hipEvent_t e_diag, hipEvent_t e_next)
+                                    int nb, hipStream_t sc, hipStream_t sx, hipEvent_t e_diag, hipEvent_t e_next,
+                                    int *sched_x)
 {
     chol_status s;
     if (A != L) {
@@ -224,18 +233,11 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         const int kb = (int)std::min<int64_t>(nb, n - k0);
         const double kb3 = (double)kb * kb * kb;
         chol_status r;
-        {
-            prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, kb3 / 3);
-            if ((r = diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, k == 0 ? 1 : 2, k0, sc)) != CHOL_OK)
-                return r;
-        }
-        if (k0 + kb < n) {
-            prof::Scope ps(CHOL_K_DIAG_INVERSE, sc, kb3 / 3);
-            hipLaunchKernelGGL((k_trinv<T>), dim3(1), dim3(256), 0, sc, n, nb, k0, (int64_t)nb, L, ldl, 0,
-                               (T *)nullptr, (int64_t)0, (int64_t)0);
-            CHOL_LAUNCH_CHECK();
-        }
-        return CHOL_OK;
+        // the factor of the tile and, if a panel follows, its inverse (written
+        // transposed into the tile's strict upper triangle for the panel solve)
+        const bool inv = k0 + kb < n;
+        prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, inv ? 2 * kb3 / 3 : kb3 / 3);
+        return diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, k == 0 ? 1 : 2, k0, inv, sc);
     };
     if ((s = diag_step(0)) != CHOL_OK)
         return s;
@@ -287,6 +289,7 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             p.b = P2; p.ldb = ldl;
             p.c = L + (r0 + kn) * ldl + r0 + kn; p.ldc = ldl;
             p.tri = 1;
+            p.sched = sched_x;
             prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, (double)m2 * (m2 + 1) * kb);
             if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx)) != CHOL_OK)
                 return s;
@@ -309,7 +312,8 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
     // stream resumes after both are done
     if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
         return CHOL_ERR_HIP;
-    const chol_status s = blocked_potrf_on<T>(n, A, lda, L, ldl, info, nb, sd->chain, sd->x, sd->ev[0], sd->ev[1]);
+    const chol_status s = blocked_potrf_on<T>(n, A, lda, L, ldl, info, nb, sd->chain, sd->x, sd->ev[0], sd->ev[1],
+                                              sd->sched);
     const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
                         stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
     if (s != CHOL_OK)
@@ -327,7 +331,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
 //   [part_c: 2 * nb * nb]                   the tile adjoint's scratch tiles
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static const int TILE_SPLIT_MAX = 256;   // splits of tile-sized products with a long contraction
-static const int SIDE_SPLIT_MAX = 8;     // splits of the large symmetric product
+static const int SIDE_SPLIT_MAX = 16;    // splits of the large symmetric product
 
 size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
 {
@@ -356,7 +360,7 @@ static inline int tile_splits(int64_t K, int64_t &chunk)
 // in a fixed order, so the result does not depend on scheduling.
 template <typename T>
 static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, const T *B, int64_t ldb, T *C,
-                               int64_t ldc, T *part, int max_splits, int min_chunk, hipStream_t st)
+                               int64_t ldc, T *part, int max_splits, int min_chunk, int *sched, hipStream_t st)
 {
     if (M <= 0 || N <= 0 || K <= 0)
         return CHOL_OK;
@@ -365,16 +369,16 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
     p.a = S; p.lda = lds;
     p.b = B; p.ldb = ldb;
     p.c = C; p.ldc = ldc;
-    // at most one wave of blocks (two per CU), minus a few slots for the
-    // one-block kernels running beside it: a partial second wave would double
-    // the time of the launch
+    // about four (split, tile) items per block slot, taken dynamically by
+    // persistent blocks, so that blocks slowed by a neighbour take fewer
     const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t slots = 2 * 256 - 32;
-    int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, slots / tiles));
+    const int64_t want = 4 * 2 * (256 - 16);
+    int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (want + tiles - 1) / tiles));
     splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, K / min_chunk));
     p.kchunk = split_chunk(K, splits);
     const int used = (K + p.kchunk - 1) / p.kchunk;
     p.part = part;
+    p.sched = sched;
     chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st);
     if (s != CHOL_OK)
         return s;
@@ -511,7 +515,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
 template <typename T>
 static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
                                       int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t sc,
-                                      hipStream_t sx, hipEvent_t e_tile, hipEvent_t e_wide)
+                                      hipStream_t sx, hipEvent_t e_tile, hipEvent_t e_wide, int *sched_x)
 {
     chol_status s;
     const int64_t K = (n + nb - 1) / nb;
@@ -645,7 +649,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
             {
                 prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * nb * (double)m * m);
                 if ((s = sym_product<T>((int)m, nb, (int)m, Wb + r0 * ldw + r0, ldw, Lj, ldl, Wb + r0 * ldw + j0,
-                                        ldw, part_x, SIDE_SPLIT_MAX, 256, sx)) != CHOL_OK)
+                                        ldw, part_x, SIDE_SPLIT_MAX, 256, sched_x, sx)) != CHOL_OK)
                     return s;
             }
         }
@@ -668,7 +672,7 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
     if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
         return CHOL_ERR_HIP;
     const chol_status s = blocked_adjoint_on<T>(n, L, ldl, adjL, ldal, adjA, ldaa, accumulate, nb, ws, sd->chain,
-                                                sd->x, sd->ev[0], sd->ev[1]);
+                                                sd->x, sd->ev[0], sd->ev[1], sd->sched);
     const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
                         stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
     if (s != CHOL_OK)

@@ -25,6 +25,8 @@
 // XCD's L2).
 #pragma once
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace chol {
@@ -44,6 +46,10 @@ template <typename T> struct GemmArgs {
     T *part;             // C_PARTIAL destination, splits * M * N
     int tri;             // 1: lower-triangular tile grid (M == N)
     int vec;             // 1: 16-byte global loads are legal for both operands
+    int splits;          // split count (C_PARTIAL)
+    int *sched;          // non-null: blocks take (split, tile) items from this
+                         // device counter pair (item, finished blocks), which
+                         // must be zero at launch and is zero again afterwards
 };
 
 namespace gemm_detail {
@@ -284,37 +290,13 @@ __device__ __forceinline__ void acc_pos(int i, int j, int v, int &row, int &col)
     col = (wave % 2) * 64 + j * 16 + lane % 16;
 }
 
+// One 128 x 128 output tile (I, J) over the contraction range [kbeg, kend).
 template <typename T, int AOP, int BOP, int CM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-k_gemm(GemmArgs<T> p)
+__device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, int split, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
-    __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
-
-    // tile coordinates
-    int I, J;
-    {
-        const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
-        const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
-        const int t = xcd_tile(blockIdx.x, nt);
-        if (p.tri) {
-            int r = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-            while (r * (r + 1) / 2 > t) --r;
-            while ((r + 1) * (r + 2) / 2 <= t) ++r;
-            I = r;
-            J = t - r * (r + 1) / 2;
-        } else {
-            I = t / TJ;
-            J = t % TJ;
-        }
-    }
     const int r0 = I * BM, c0 = J * BN;
-    int kbeg = 0, kend = p.K;
-    if (CM == C_PARTIAL) {
-        kbeg = blockIdx.y * p.kchunk;
-        kend = min(p.K, kbeg + p.kchunk);
-    }
 
     // C -= AB runs as acc = C, acc += (-A) B: the accumulators start from C,
     // so the epilogue is a plain store and no accumulator has to leave the
@@ -362,9 +344,77 @@ k_gemm(GemmArgs<T> p)
                     if (row >= col)
                         p.c[(int64_t)row * p.ldc + col] = val;
                 } else {
-                    p.part[(int64_t)blockIdx.y * p.M * p.N + (int64_t)row * p.N + col] = val;
+                    p.part[(int64_t)split * p.M * p.N + (int64_t)row * p.N + col] = val;
                 }
             }
+}
+
+__device__ __forceinline__ void tile_of(int t, int tri, int TJ, int &I, int &J)
+{
+    if (tri) {
+        int r = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+        while (r * (r + 1) / 2 > t) --r;
+        while ((r + 1) * (r + 2) / 2 <= t) ++r;
+        I = r;
+        J = t - r * (r + 1) / 2;
+    } else {
+        I = t / TJ;
+        J = t % TJ;
+    }
+}
+
+template <typename T, int AOP, int BOP, int CM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_gemm(GemmArgs<T> p)
+{
+    using namespace gemm_detail;
+    __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
+    const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
+    const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
+
+    if (!p.sched) {
+        // static: one tile per block, tiles spread over the XCDs in contiguous ranges
+        int I, J;
+        tile_of(gemm_detail::xcd_tile(blockIdx.x, nt), p.tri, TJ, I, J);
+        int kbeg = 0, kend = p.K;
+        if (CM == C_PARTIAL) {
+            kbeg = blockIdx.y * p.kchunk;
+            kend = min(p.K, kbeg + p.kchunk);
+        }
+        gemm_tile<T, AOP, BOP, CM>(p, I, J, blockIdx.y, kbeg, kend, lds);
+        return;
+    }
+
+    // dynamic: every block takes (split, tile) items until none are left, so a
+    // block that shares its CU with other work simply takes fewer items
+    __shared__ int s_item;
+    const int splits = (CM == C_PARTIAL) ? p.splits : 1;
+    const int items = nt * splits;
+    for (;;) {
+        if (threadIdx.x == 0)
+            s_item = atomicAdd(p.sched, 1);
+        __syncthreads();
+        const int it = s_item;
+        if (it >= items)
+            break;
+        const int split = it / nt;
+        int I, J;
+        tile_of(it % nt, p.tri, TJ, I, J);
+        int kbeg = 0, kend = p.K;
+        if (CM == C_PARTIAL) {
+            kbeg = split * p.kchunk;
+            kend = min(p.K, kbeg + p.kchunk);
+        }
+        gemm_tile<T, AOP, BOP, CM>(p, I, J, split, kbeg, kend, lds);
+    }
+    // the last block to finish returns the counters to zero for the next launch
+    if (threadIdx.x == 0) {
+        const int done = atomicAdd(p.sched + 1, 1);
+        if (done == (int)gridDim.x - 1) {
+            atomicExch(p.sched, 0);
+            atomicExch(p.sched + 1, 0);
+        }
+    }
 }
 
 // host side -------------------------------------------------------------------
@@ -383,10 +433,20 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     if (p.M <= 0 || p.N <= 0)
         return CHOL_OK;
     p.vec = aligned16(p.a, p.lda) && aligned16(p.b, p.ldb);
+    p.splits = splits;
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
     const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
-    hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1)),
-                       dim3(NT), 0, st, p);
+    if (p.sched) {
+        // persistent blocks, all resident at once: two per CU on all but 16
+        // CUs, whose slots stay free for the one-block kernels of the other
+        // library stream
+        const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1);
+        const unsigned grid = (unsigned)std::min<int64_t>(items, 2 * (256 - 16));
+        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3(grid), dim3(NT), 0, st, p);
+    } else {
+        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1)),
+                           dim3(NT), 0, st, p);
+    }
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;
 }

@@ -23,6 +23,11 @@ Side *side_resources()
         for (auto &e : s.ev)
             if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
                 return;
+        const size_t bytes = sizeof(int) * SCHED_SLOTS * SCHED_STRIDE;
+        if (hipMalloc((void **)&s.sched, bytes) != hipSuccess)
+            return;
+        if (hipMemset(s.sched, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+            return;
         s.ok = true;
     });
     return s.ok ? &s : nullptr;

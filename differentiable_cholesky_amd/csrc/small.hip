@@ -27,10 +27,14 @@
 // cyclically over a G x G lane grid: lane (lr, lc) owns entries
 // (lr + G*a, lc + G*b), a, b in [0, E).  Every step of the column loops then
 // retires the same number of entries on every lane, and whole blocks of
-// (a, b) fall out of the trailing work at compile time.  Global memory is read
-// and written row-contiguously through an LDS staging tile; per-step
-// broadcasts (a column of the trailing matrix, a solved row or column) go
-// through a small double-buffered LDS vector.
+// (a, b) fall out of the trailing work at compile time.  Each lane loads the
+// entries it owns straight from global memory into registers (all loads in
+// flight at once) and stores them back the same way, so a lane only ever
+// writes entries it read itself (in-place calls need no ordering between
+// lanes).  Per-step broadcasts -- a column of the trailing matrix, a row of L,
+// a solved row or column -- go through small double-buffered LDS vectors in
+// which column c of a row sits at (c % G) * E + c / G, so that every lane reads
+// the E entries it needs as one contiguous run.
 #include "common.hpp"
 
 namespace chol {
@@ -42,13 +46,18 @@ template <int G_, int E_> struct TileShape {
     static constexpr int LPM = G * G;                     // lanes per matrix
     static constexpr int THREADS = LPM < 64 ? 64 : LPM;   // one wavefront at least
     static constexpr int MPB = THREADS / LPM;             // matrices per block
-    static constexpr int LDP = NP + G;                    // natural-layout LDS pitch
-    static constexpr int MSTRIDE = NP * LDP + 16;         // per-matrix LDS region
+    static constexpr bool UNROLL = false;                 // unroll the lane loop of each step
 };
 
-// Position of column c inside a "permuted" LDS row: the E entries that lane
-// column lc needs (columns lc, lc+G, ...) sit contiguously at lc*E.
-template <int G, int E> __device__ __forceinline__ int perm_col(int c) { return (c % G) * E + c / G; }
+// Waves per SIMD the register allocation aims for (the scheduler otherwise
+// trades occupancy for overlap of the fully unrolled steps): a tile's values
+// take E*E/2 (factor) or about 2*E*E (adjoint) registers per lane.
+template <typename T, int G, int E> struct TileWaves {
+    static constexpr int words = (int)(sizeof(T) / 4);
+    static constexpr int tile = E * E * words;
+    static constexpr int factor = tile <= 32 ? 8 : (tile <= 64 ? 5 : 2);
+    static constexpr int adjoint = tile <= 16 ? 8 : (tile <= 32 ? 4 : (tile <= 64 ? 3 : 1));
+};
 
 // info_mode: 0 -> info[mat] = first failing column + 1 (or 0);
 //            1 -> info[0] = (fail ? info_base + fail : 0)            (first tile of a blocked call)
@@ -65,80 +74,203 @@ __device__ __forceinline__ void write_info(int32_t *info, int64_t mat, int fail,
         info[0] = (int32_t)(base + fail);
 }
 
+// Pivot arithmetic.  fp64 keeps IEEE square root and reciprocal; fp32 uses the
+// hardware reciprocal square root and reciprocal (about 1 ulp), far inside the
+// fp32 tolerance and much shorter than the correctly rounded sequences.
+template <typename T> struct Piv;
+template <> struct Piv<double> {
+    static __device__ __forceinline__ void sqrt_rsqrt(double d, double &sq, double &rs)
+    {
+        sq = __dsqrt_rn(d);
+        rs = __drcp_rn(sq);
+    }
+    static __device__ __forceinline__ double rcp(double x) { return __drcp_rn(x); }
+};
+template <> struct Piv<float> {
+    static __device__ __forceinline__ void sqrt_rsqrt(float d, float &sq, float &rs)
+    {
+        rs = __builtin_amdgcn_rsqf(d);
+        sq = d * rs;
+    }
+    static __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+};
+
+// 16-byte global access for fp32 tiles whose edge is a multiple of 4 and whose
+// rows and matrices start on 16-byte boundaries.  A quad of lanes (lc = 0..3,
+// same lr) then moves one 64-byte run of a row per instruction: lane lc moves
+// the 4 columns 4q .. 4q+3 with q = lc + 4q', and a 4 x 4 transpose across the
+// quad turns that into the cyclic ownership above (lane lc holds columns
+// lc + 4b, b = c + 4q', c = 0..3).
+__device__ __forceinline__ float dpp_xor1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+// On entry lane l of the quad holds w[e] = M[l][e]; on exit w[e] = M[e][l].
+// Two butterfly stages (partners l^1, then l^2); every lane of the quad must
+// execute it.
+__device__ __forceinline__ void quad_transpose(float (&w)[4], int l)
+{
+    const bool odd = (l & 1) != 0, hi = (l & 2) != 0;
+    const float p1 = dpp_xor1(w[1]), p0 = dpp_xor1(w[0]), p3 = dpp_xor1(w[3]), p2 = dpp_xor1(w[2]);
+    const float t0 = odd ? p1 : w[0];
+    const float t1 = odd ? w[1] : p0;
+    const float t2 = odd ? p3 : w[2];
+    const float t3 = odd ? w[3] : p2;
+    const float q2 = dpp_xor2(t2), q3 = dpp_xor2(t3), q0 = dpp_xor2(t0), q1 = dpp_xor2(t1);
+    w[0] = hi ? q2 : t0;
+    w[1] = hi ? q3 : t1;
+    w[2] = hi ? t2 : q0;
+    w[3] = hi ? t3 : q1;
+}
+
+// Load the lower blocks of one fp32 tile (edge 4E) into the cyclic layout:
+// dst[a][b] for b <= a; entries right of the diagonal come back as zero.  All
+// loads are issued before the first transpose needs one.
+template <int E>
+__device__ __forceinline__ void vec_load_lower(float (&dst)[E][E], const float *M, int64_t ld, bool mv, int lr,
+                                               int lc)
+{
+    float4 raw[E][E / 4];
+#pragma unroll
+    for (int a = 0; a < E; ++a) {
+        const int r = lr + 4 * a;
+#pragma unroll
+        for (int qq = 0; qq < E / 4; ++qq) {
+            raw[a][qq] = make_float4(0.f, 0.f, 0.f, 0.f);
+            const int q = lc + 4 * qq;
+            if (16 * qq <= 4 * a + 3 && mv && 4 * q <= r)
+                raw[a][qq] = *reinterpret_cast<const float4 *>(M + (int64_t)r * ld + 4 * q);
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < E; ++a) {
+#pragma unroll
+        for (int qq = 0; qq < E / 4; ++qq) {
+            if (16 * qq > 4 * a + 3)
+                continue;                       // the whole group is right of the diagonal
+            float w[4] = {raw[a][qq].x, raw[a][qq].y, raw[a][qq].z, raw[a][qq].w};
+            quad_transpose(w, lc);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int b = c + 4 * qq;
+                if (b > a)
+                    continue;
+                // diagonal block: keep column lc + 4a <= row lr + 4a only
+                dst[a][b] = (b < a || lc <= lr) ? w[c] : 0.f;
+            }
+        }
+    }
+}
+
+// Store rows of one fp32 tile from the cyclic layout.  src(a, b) gives the
+// value of entry (lr + 4a, lc + 4b).  mode 0 writes the whole row (entries
+// right of the diagonal must already be zero in src); mode 1 writes only
+// entries on or left of the diagonal.
+template <int E, int MODE, typename F>
+__device__ __forceinline__ void vec_store(float *M, int64_t ld, bool mv, int lr, int lc, F &&src)
+{
+#pragma unroll
+    for (int a = 0; a < E; ++a) {
+        const int r = lr + 4 * a;
+#pragma unroll
+        for (int qq = 0; qq < E / 4; ++qq) {
+            const int q = lc + 4 * qq;
+            if (16 * qq > 4 * a + 3) {
+                if (MODE == 0 && mv)
+                    *reinterpret_cast<float4 *>(M + (int64_t)r * ld + 4 * q) = make_float4(0.f, 0.f, 0.f, 0.f);
+                continue;
+            }
+            float w[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                w[c] = src(a, c + 4 * qq);
+            quad_transpose(w, lc);
+            if (!mv)
+                continue;
+            float *dst = M + (int64_t)r * ld + 4 * q;
+            if (MODE == 0 || 4 * q + 3 <= r) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
+            } else if (4 * q <= r) {
+                dst[0] = w[0];
+                if (4 * q + 1 <= r)
+                    dst[1] = w[1];
+                if (4 * q + 2 <= r)
+                    dst[2] = w[2];
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------------
 // Factor: right-looking column loop on register-resident tiles.
-// A and L may be the same buffer (in place); each block reads all of its
-// matrices before it writes any.
 // ------------------------------------------------------------------------
-template <typename T, int G, int E>
+template <typename T, int G, int E, bool VEC>
 __global__ void __launch_bounds__((TileShape<G, E>::THREADS))
+__attribute__((amdgpu_waves_per_eu(TileWaves<T, G, E>::factor)))
 k_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
              T *L, int64_t ldl, int64_t sL, int32_t *info, int info_mode, int64_t info_base)
 {
     typedef TileShape<G, E> S;
-    constexpr int NP = S::NP, LDP = S::LDP, MSTRIDE = S::MSTRIDE, MPB = S::MPB, THREADS = S::THREADS;
-    __shared__ T stage[MPB * MSTRIDE];
+    constexpr int NP = S::NP, MPB = S::MPB;
     __shared__ T colbuf[2 * MPB * NP];
 
     const int tid = threadIdx.x;
     const int g = tid / S::LPM;
     const int lr = (tid % S::LPM) / G;
     const int lc = tid % G;
-    const int64_t mat0 = (int64_t)blockIdx.x * MPB;
+    const int64_t mat = (int64_t)blockIdx.x * MPB + g;
+    const bool mv = mat < batch;
 
-    // global -> LDS, row-contiguous; padding is the identity
-    for (int m = 0; m < MPB; ++m) {
-        const int64_t mat = mat0 + m;
-        const bool mv = mat < batch;
-        const T *Am = A + (mv ? mat * sA : 0);
-        T *St = stage + m * MSTRIDE;
-        for (int idx = tid; idx < NP * NP; idx += THREADS) {
-            const int i = idx / NP, k = idx % NP;
-            T v = (i == k) ? T(1) : T(0);
-            if (mv && i < n && k <= i)
-                v = Am[(int64_t)i * lda + k];
-            St[i * LDP + k] = v;
-        }
-    }
-    __syncthreads();
-
+    static_assert(!VEC || (G == 4 && E % 4 == 0 && sizeof(T) == 4), "16-byte path: fp32, G = 4");
+    // global -> registers (lower blocks only; padding is the identity)
     T x[E][E];
-    {
-        const T *St = stage + g * MSTRIDE;
+    if constexpr (VEC) {
+        vec_load_lower<E>(x, A + (mv ? mat * sA : 0), lda, mv, lr, lc);
+    } else {
+        const T *Am = A + (mv ? mat * sA : 0);
 #pragma unroll
         for (int a = 0; a < E; ++a)
 #pragma unroll
-            for (int b = 0; b <= a; ++b)
-                x[a][b] = St[(lr + G * a) * LDP + lc + G * b];
+            for (int b = 0; b <= a; ++b) {
+                const int i = lr + G * a, k = lc + G * b;
+                x[a][b] = (i == k) ? T(1) : T(0);
+                if (mv && i < n && k <= i)
+                    x[a][b] = Am[(int64_t)i * lda + k];
+            }
     }
 
     int fail = 0;
-    // column j = jb*G + jr; jb selects registers (compile time), jr only lanes
 #pragma unroll
-    for (int jb = 0; jb < E; ++jb) {
-#pragma unroll 1
-        for (int jr = 0; jr < G; ++jr) {
+    for (int t_ = 0; t_ < E; ++t_) {
+        const int jb = t_;
+#pragma unroll(S::UNROLL ? G : 1)
+        for (int u_ = 0; u_ < G; ++u_) {
+            const int jr = u_;
             const int j = jb * G + jr;
             T *cb = colbuf + ((j & 1) * MPB + g) * NP;
             // owners of column j publish it (unscaled); rows lr + G*a
             if (lc == jr) {
-#pragma unroll
+    #pragma unroll
                 for (int a = jb; a < E; ++a)
                     cb[lr * E + a] = x[a][jb];
             }
             __syncthreads();
             const T d = cb[jr * E + jb];
             T u[E], v[E];
-#pragma unroll
+    #pragma unroll
             for (int a = jb; a < E; ++a)
                 u[a] = cb[lr * E + a];
-#pragma unroll
+    #pragma unroll
             for (int b = jb; b < E; ++b)
                 v[b] = cb[lc * E + b];
             if (!(d > T(0)) && fail == 0)
                 fail = j + 1;
-            const T sq = dsqrt(d);
-            const T rs = drcp(sq);
+            T sq, rs;
+            Piv<T>::sqrt_rsqrt(d, sq, rs);
             const T rd = rs * rs;
             // only rows / columns strictly below / right of j take part in the update
             if (lr <= jr)
@@ -146,235 +278,281 @@ k_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
             if (lc <= jr)
                 v[jb] = T(0);
             if (lc == jr) {
-#pragma unroll
+    #pragma unroll
                 for (int a = jb; a < E; ++a)
                     x[a][jb] = (a == jb && lr == jr) ? sq : x[a][jb] * rs;
             }
-#pragma unroll
+    #pragma unroll
             for (int a = jb; a < E; ++a) {
                 const T ua = u[a] * rd;
-#pragma unroll
+    #pragma unroll
                 for (int b = jb; b <= a; ++b)
                     x[a][b] -= ua * v[b];
             }
         }
     }
 
-    // registers -> LDS -> global (lower triangle and zeroed upper)
-    __syncthreads();
-    {
-        T *St = stage + g * MSTRIDE;
+    // registers -> global: lower triangle and zeroed upper triangle
+    if constexpr (VEC) {
+        vec_store<E, 0>(L + (mv ? mat * sL : 0), ldl, mv, lr, lc, [&](int a, int b) {
+            return (b < a || (b == a && lc <= lr)) ? x[a][b] : 0.f;
+        });
+        if (mv && lr == 0 && lc == 0)
+            write_info(info, mat, fail, info_mode, info_base);
+    } else if (mv) {
+        T *Lm = L + mat * sL;
 #pragma unroll
         for (int a = 0; a < E; ++a)
 #pragma unroll
-            for (int b = 0; b <= a; ++b)
-                St[(lr + G * a) * LDP + lc + G * b] = x[a][b];
+            for (int b = 0; b < E; ++b) {
+                const int i = lr + G * a, k = lc + G * b;
+                if (i < n && k < n)
+                    Lm[(int64_t)i * ldl + k] = (b <= a && k <= i) ? x[a][b] : T(0);
+            }
+        if (lr == 0 && lc == 0)
+            write_info(info, mat, fail, info_mode, info_base);
     }
-    __syncthreads();
-    for (int m = 0; m < MPB; ++m) {
-        const int64_t mat = mat0 + m;
-        if (mat >= batch)
-            break;
-        T *Lm = L + mat * sL;
-        const T *St = stage + m * MSTRIDE;
-        for (int idx = tid; idx < NP * NP; idx += THREADS) {
-            const int i = idx / NP, k = idx % NP;
-            if (i < n && k < n)
-                Lm[(int64_t)i * ldl + k] = (k <= i) ? St[i * LDP + k] : T(0);
-        }
-    }
-    if (lr == 0 && lc == 0 && mat0 + g < batch)
-        write_info(info, mat0 + g, fail, info_mode, info_base);
 }
 
 // ------------------------------------------------------------------------
-// Adjoint: Psi = sym(Phi(L^T adj_L)), V = Psi L^{-1}, Z = L^{-T} V (lower),
-// lower(adj_A) (+)= Phi(Z).  adj_A may be adj_L itself when accumulate == 0.
+// Adjoint: M = L^T tril(adj_L) (lower part), Psi = P + P^T with P = Phi(M)
+// (M's lower part mirrored, diagonal M_ii), V = Psi L^{-1}, Z = L^{-T} V
+// (lower part), lower(adj_A) (+)= Phi(Z).  L and adj_L stay in registers; each
+// step publishes the one row of L it needs and the vector it produces.
+// adj_A may be adj_L itself when accumulate == 0.
 // ------------------------------------------------------------------------
-template <typename T, int G, int E>
+template <typename T, int G, int E, bool VEC>
 __global__ void __launch_bounds__((TileShape<G, E>::THREADS))
+__attribute__((amdgpu_waves_per_eu(TileWaves<T, G, E>::adjoint)))
 k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
                  const T *adjL, int64_t ldal, int64_t sAL,
                  T *adjA, int64_t ldaa, int64_t sAA, int accumulate)
 {
     typedef TileShape<G, E> S;
-    constexpr int NP = S::NP, LDP = S::LDP, MSTRIDE = S::MSTRIDE, MPB = S::MPB, THREADS = S::THREADS;
-    constexpr int LPSTRIDE = NP * NP + 16;
-    __shared__ T lp[MPB * LPSTRIDE];      // L, rows natural, columns permuted; upper = 0
-    __shared__ T scr[MPB * MSTRIDE];      // adj_L (permuted), then transposes, then G
-    __shared__ T bc[2 * MPB * NP];
+    constexpr int NP = S::NP, MPB = S::MPB;
+    static_assert(S::LPM <= 64, "one matrix per wavefront at most (lane shuffles)");
+    __shared__ T rowb[2 * MPB * NP];    // a row of L
+    __shared__ T vecb[2 * MPB * NP];    // a row of adj_L, a column of V or a row of Z
+    __shared__ T dinv[MPB * NP];        // 1 / L_jj
 
     const int tid = threadIdx.x;
     const int g = tid / S::LPM;
     const int lr = (tid % S::LPM) / G;
     const int lc = tid % G;
-    const int64_t mat0 = (int64_t)blockIdx.x * MPB;
+    const int64_t mat = (int64_t)blockIdx.x * MPB + g;
+    const bool mv = mat < batch;
 
-    for (int m = 0; m < MPB; ++m) {
-        const int64_t mat = mat0 + m;
-        const bool mv = mat < batch;
+    static_assert(!VEC || (G == 4 && E % 4 == 0 && sizeof(T) == 4), "16-byte path: fp32, G = 4");
+    // global -> registers: L (identity padding) and tril(adj_L) (zero padding)
+    T lw[E][E], bw[E][E];
+    if constexpr (VEC) {
+        vec_load_lower<E>(lw, L + (mv ? mat * sL : 0), ldl, mv, lr, lc);
+        __builtin_amdgcn_sched_barrier(0);     // keep the two tiles' raw loads from all being live at once
+        vec_load_lower<E>(bw, adjL + (mv ? mat * sAL : 0), ldal, mv, lr, lc);
+        if (!mv && lr == lc) {
+#pragma unroll
+            for (int a = 0; a < E; ++a)
+                lw[a][a] = T(1);
+        }
+    } else {
         const T *Lm = L + (mv ? mat * sL : 0);
         const T *Bm = adjL + (mv ? mat * sAL : 0);
-        T *Lp = lp + m * LPSTRIDE;
-        T *Sc = scr + m * MSTRIDE;
-        for (int idx = tid; idx < NP * NP; idx += THREADS) {
-            const int i = idx / NP, k = idx % NP;
-            T lv = (i == k) ? T(1) : T(0);
-            T bv = T(0);
-            if (mv && i < n && k <= i) {
-                lv = Lm[(int64_t)i * ldl + k];
-                bv = Bm[(int64_t)i * ldal + k];
+#pragma unroll
+        for (int a = 0; a < E; ++a)
+#pragma unroll
+            for (int b = 0; b <= a; ++b) {
+                const int i = lr + G * a, k = lc + G * b;
+                const bool in = mv && i < n && k <= i;
+                lw[a][b] = (i == k) ? T(1) : T(0);
+                bw[a][b] = T(0);
+                if (in) {
+                    lw[a][b] = Lm[(int64_t)i * ldl + k];
+                    bw[a][b] = Bm[(int64_t)i * ldal + k];
+                }
             }
-            Lp[i * NP + perm_col<G, E>(k)] = lv;
-            Sc[i * LDP + perm_col<G, E>(k)] = bv;
-        }
     }
-    __syncthreads();
+    if (lr == lc) {
+#pragma unroll
+        for (int a = 0; a < E; ++a)
+            dinv[g * NP + lr + G * a] = Piv<T>::rcp(lw[a][a]);
+    }
 
-    const T *Lp = lp + g * LPSTRIDE;
-    T *Sc = scr + g * MSTRIDE;
-
-    // M = L^T tril(adj_L), lower part: M_ij = sum_k L_ki adjL_kj (k >= i >= j).
     T p[E][E];
 #pragma unroll
     for (int a = 0; a < E; ++a)
 #pragma unroll
         for (int b = 0; b < E; ++b)
             p[a][b] = T(0);
+
+    // M_ij = sum_{k >= i} L_ki adjL_kj (i >= j): row k of L and of adj_L per step
 #pragma unroll
-    for (int kb = 0; kb < E; ++kb) {
-#pragma unroll 1
-        for (int kr = 0; kr < G; ++kr) {
+    for (int t_ = 0; t_ < E; ++t_) {
+        const int kb = t_;
+#pragma unroll(S::UNROLL ? G : 1)
+        for (int u_ = 0; u_ < G; ++u_) {
+            const int kr = u_;
             const int k = kb * G + kr;
+            T *rb = rowb + ((k & 1) * MPB + g) * NP;
+            T *vb = vecb + ((k & 1) * MPB + g) * NP;
+            if (lr == kr) {
+    #pragma unroll
+                for (int b = 0; b < E; ++b) {
+                    rb[lc * E + b] = (b <= kb) ? lw[kb][b] : T(0);
+                    vb[lc * E + b] = (b <= kb) ? bw[kb][b] : T(0);
+                }
+            }
+            __syncthreads();
             T lk[E], ak[E];
-#pragma unroll
+    #pragma unroll
             for (int a = 0; a <= kb; ++a)
-                lk[a] = Lp[k * NP + lr * E + a];    // L[k][lr + G a]
-#pragma unroll
+                lk[a] = rb[lr * E + a];          // L[k][lr + G a]
+    #pragma unroll
             for (int b = 0; b <= kb; ++b)
-                ak[b] = Sc[k * LDP + lc * E + b];   // adjL[k][lc + G b]
-#pragma unroll
+                ak[b] = vb[lc * E + b];          // adjL[k][lc + G b]
+    #pragma unroll
             for (int a = 0; a <= kb; ++a)
-#pragma unroll
+    #pragma unroll
                 for (int b = 0; b <= a; ++b)
                     p[a][b] += lk[a] * ak[b];
         }
     }
 
-    // Psi = P + P^T: lower entries of M stay; the upper ones are M's transposed
-    // lower entries; the diagonal keeps M_ii (Phi halves it, the mirror adds it back).
-    __syncthreads();
+    // Psi: the upper entries are M's transposed lower entries, held by lane
+    // (lc, lr) of the same matrix at block (b, a)
+    {
+        const int src = (tid / S::LPM) * S::LPM % 64 + lc * G + lr;
 #pragma unroll
-    for (int a = 0; a < E; ++a)
+        for (int a = 0; a < E; ++a) {
 #pragma unroll
-        for (int b = 0; b <= a; ++b) {
-            const int i = lr + G * a, j = lc + G * b;
-            if (i >= j)
-                Sc[j * LDP + i] = p[a][b];      // transposed
+            for (int b = a + 1; b < E; ++b)
+                p[a][b] = __shfl(p[b][a], src, 64);
+            const T t = __shfl(p[a][a], src, 64);
+            if (lr < lc)
+                p[a][a] = t;
         }
+    }
     __syncthreads();
-#pragma unroll
-    for (int a = 0; a < E; ++a)
-#pragma unroll
-        for (int b = a; b < E; ++b) {
-            const int i = lr + G * a, j = lc + G * b;
-            if (i < j)
-                p[a][b] = Sc[i * LDP + j];      // = M_ji
-        }
 
     // V = Psi L^{-1}  (V L = Psi), columns j = NP-1 .. 0:
     //   V[:, j] = R[:, j] / L_jj ;  R[:, k] -= V[:, j] L_jk  (k < j)
 #pragma unroll
-    for (int jb = E - 1; jb >= 0; --jb) {
-#pragma unroll 1
-        for (int jr = G - 1; jr >= 0; --jr) {
+    for (int t_ = 0; t_ < E; ++t_) {
+        const int jb = E - 1 - t_;
+#pragma unroll(S::UNROLL ? G : 1)
+        for (int u_ = 0; u_ < G; ++u_) {
+            const int jr = G - 1 - u_;
             const int j = jb * G + jr;
-            T *cb = bc + ((j & 1) * MPB + g) * NP;
+            T *rb = rowb + ((j & 1) * MPB + g) * NP;
+            T *vb = vecb + ((j & 1) * MPB + g) * NP;
             if (lc == jr) {
-                const T rinv = drcp(Lp[j * NP + jr * E + jb]);
-#pragma unroll
+                const T r = dinv[g * NP + j];
+    #pragma unroll
                 for (int a = 0; a < E; ++a) {
-                    p[a][jb] *= rinv;
-                    cb[lr * E + a] = p[a][jb];
+                    p[a][jb] *= r;
+                    vb[lr * E + a] = p[a][jb];
                 }
+            }
+            if (lr == jr) {
+    #pragma unroll
+                for (int b = 0; b <= jb; ++b)
+                    rb[lc * E + b] = lw[jb][b];
             }
             __syncthreads();
             T u[E], lj[E];
-#pragma unroll
+    #pragma unroll
             for (int a = 0; a < E; ++a)
-                u[a] = cb[lr * E + a];
-#pragma unroll
+                u[a] = vb[lr * E + a];           // V[lr + G a][j]
+    #pragma unroll
             for (int b = 0; b <= jb; ++b)
-                lj[b] = Lp[j * NP + lc * E + b];    // L[j][lc + G b]; zero right of j
+                lj[b] = rb[lc * E + b];          // L[j][lc + G b]; zero right of j
             if (lc == jr)
-                lj[jb] = T(0);                      // the solved column itself
-#pragma unroll
+                lj[jb] = T(0);                   // the solved column itself
+    #pragma unroll
             for (int a = 0; a < E; ++a)
-#pragma unroll
+    #pragma unroll
                 for (int b = 0; b <= jb; ++b)
                     p[a][b] -= u[a] * lj[b];
         }
+    }
+    __syncthreads();
+
+    // the accumulated output is read while Z is solved
+    T acc[E][E];
+    if constexpr (!VEC) {
+      if (accumulate && mv) {
+        const T *Gm = adjA + mat * sAA;
+#pragma unroll
+        for (int a = 0; a < E; ++a)
+#pragma unroll
+            for (int b = 0; b <= a; ++b) {
+                const int i = lr + G * a, k = lc + G * b;
+                acc[a][b] = (i < n && k <= i) ? Gm[(int64_t)i * ldaa + k] : T(0);
+            }
+      }
     }
 
     // Z = L^{-T} V (L^T Z = V), lower part, rows i = NP-1 .. 0:
     //   Z[i, :] = R[i, :] / L_ii ;  R[t, :] -= L_it Z[i, :]  (t < i)
 #pragma unroll
-    for (int ib = E - 1; ib >= 0; --ib) {
-#pragma unroll 1
-        for (int ir = G - 1; ir >= 0; --ir) {
+    for (int t_ = 0; t_ < E; ++t_) {
+        const int ib = E - 1 - t_;
+#pragma unroll(S::UNROLL ? G : 1)
+        for (int u_ = 0; u_ < G; ++u_) {
+            const int ir = G - 1 - u_;
             const int i = ib * G + ir;
-            T *cb = bc + ((i & 1) * MPB + g) * NP;
+            T *rb = rowb + ((i & 1) * MPB + g) * NP;
+            T *vb = vecb + ((i & 1) * MPB + g) * NP;
             if (lr == ir) {
-                const T rinv = drcp(Lp[i * NP + ir * E + ib]);
-#pragma unroll
+                const T r = dinv[g * NP + i];
+    #pragma unroll
                 for (int b = 0; b <= ib; ++b) {
-                    p[ib][b] *= rinv;
-                    cb[lc * E + b] = p[ib][b];
+                    p[ib][b] *= r;
+                    vb[lc * E + b] = p[ib][b];
+                    rb[lc * E + b] = lw[ib][b];
                 }
             }
             __syncthreads();
             T w[E], li[E];
-#pragma unroll
+    #pragma unroll
             for (int b = 0; b <= ib; ++b)
-                w[b] = cb[lc * E + b];
-#pragma unroll
+                w[b] = vb[lc * E + b];           // Z[i][lc + G b]
+    #pragma unroll
             for (int a = 0; a <= ib; ++a)
-                li[a] = Lp[i * NP + lr * E + a];    // L[i][lr + G a]; zero right of i
+                li[a] = rb[lr * E + a];          // L[i][lr + G a]; zero right of i
             if (lr == ir)
-                li[ib] = T(0);                      // the solved row itself
-#pragma unroll
+                li[ib] = T(0);                   // the solved row itself
+    #pragma unroll
             for (int a = 0; a <= ib; ++a)
-#pragma unroll
+    #pragma unroll
                 for (int b = 0; b <= a; ++b)
                     p[a][b] -= li[a] * w[b];
         }
     }
 
-    // G = Phi(Z): halve the diagonal; stage the lower triangle and store it.
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < E; ++a)
-#pragma unroll
-        for (int b = 0; b <= a; ++b) {
-            const int i = lr + G * a, j = lc + G * b;
-            if (i >= j)
-                Sc[i * LDP + j] = (i == j) ? p[a][b] * T(0.5) : p[a][b];
-        }
-    __syncthreads();
-    for (int m = 0; m < MPB; ++m) {
-        const int64_t mat = mat0 + m;
-        if (mat >= batch)
-            break;
+    // G = Phi(Z): halve the diagonal; lower triangle only
+    if constexpr (VEC) {
+        // (16-byte path: the accumulated output is read only now, which keeps
+        // its registers out of the solve)
+        if (accumulate)
+            vec_load_lower<E>(acc, adjA + (mv ? mat * sAA : 0), ldaa, mv, lr, lc);
+        vec_store<E, 1>(adjA + (mv ? mat * sAA : 0), ldaa, mv, lr, lc, [&](int a, int b) {
+            if (b > a)
+                return 0.f;
+            const float gv = (b == a && lc == lr) ? p[a][b] * 0.5f : p[a][b];
+            return accumulate ? acc[a][b] + gv : gv;
+        });
+    } else if (mv) {
         T *Gm = adjA + mat * sAA;
-        const T *Sm = scr + m * MSTRIDE;
-        for (int idx = tid; idx < NP * NP; idx += THREADS) {
-            const int i = idx / NP, k = idx % NP;
-            if (i < n && k <= i) {
-                T *dst = Gm + (int64_t)i * ldaa + k;
-                const T gv = Sm[i * LDP + k];
-                *dst = accumulate ? *dst + gv : gv;
+#pragma unroll
+        for (int a = 0; a < E; ++a)
+#pragma unroll
+            for (int b = 0; b <= a; ++b) {
+                const int i = lr + G * a, k = lc + G * b;
+                if (i < n && k <= i) {
+                    const T gv = (i == k) ? p[a][b] * T(0.5) : p[a][b];
+                    Gm[(int64_t)i * ldaa + k] = accumulate ? acc[a][b] + gv : gv;
+                }
             }
-        }
     }
 }
 
@@ -422,7 +600,128 @@ k_wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar, T *bbar,
     }
 }
 
+// ------------------------------------------------------------------------
+// Diagonal tile of the blocked factor with its inverse (one 128-edge tile per
+// 256-thread block, lane grid 16 x 16).  The inverse X = L^{-1} is built row
+// by row alongside the factor: after factor step j has published column j of
+// the trailing matrix, the lanes of row j of X scale it by 1 / L_jj and publish
+// it, and every row t > j takes R_t -= L_tj X_j, with L_tj already in
+// registers from the factor step.  No tile-sized LDS buffer is needed, so the
+// kernel fits beside the blocks of a running matrix-core product.  X's strict
+// lower triangle is written transposed into the tile's strict upper triangle,
+// where the panel solve of the blocked factorisation reads it (that triangle
+// is cleared at the end of the factorisation).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base)
+{
+    constexpr int G = 16, E = 8, NP = G * E;
+    __shared__ T colbuf[2 * NP];
+    __shared__ T rowbuf[2 * NP];
+    const int tid = threadIdx.x, lr = tid / G, lc = tid % G;
+
+    T x[E][E], y[E][E];
+#pragma unroll
+    for (int a = 0; a < E; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b) {
+            const int i = lr + G * a, k = lc + G * b;
+            x[a][b] = (i == k) ? T(1) : T(0);
+            if (i < n && k <= i)
+                x[a][b] = W[(int64_t)i * ld + k];
+            y[a][b] = (i == k) ? T(1) : T(0);
+        }
+
+    int fail = 0;
+#pragma unroll
+    for (int jb = 0; jb < E; ++jb) {
+#pragma unroll 1
+        for (int jr = 0; jr < G; ++jr) {
+            const int j = jb * G + jr;
+            T *cb = colbuf + (j & 1) * NP;
+            T *rb = rowbuf + (j & 1) * NP;
+            if (lc == jr) {
+#pragma unroll
+                for (int a = jb; a < E; ++a)
+                    cb[lr * E + a] = x[a][jb];
+            }
+            __syncthreads();
+            const T d = cb[jr * E + jb];
+            T u[E], v[E];
+#pragma unroll
+            for (int a = jb; a < E; ++a)
+                u[a] = cb[lr * E + a];
+#pragma unroll
+            for (int b = jb; b < E; ++b)
+                v[b] = cb[lc * E + b];
+            if (!(d > T(0)) && fail == 0)
+                fail = j + 1;
+            T sq, rs;
+            Piv<T>::sqrt_rsqrt(d, sq, rs);
+            const T rd = rs * rs;
+            if (lr <= jr)
+                u[jb] = T(0);
+            if (lc <= jr)
+                v[jb] = T(0);
+            if (lc == jr) {
+#pragma unroll
+                for (int a = jb; a < E; ++a)
+                    x[a][jb] = (a == jb && lr == jr) ? sq : x[a][jb] * rs;
+            }
+#pragma unroll
+            for (int a = jb; a < E; ++a) {
+                const T ua = u[a] * rd;
+#pragma unroll
+                for (int b = jb; b <= a; ++b)
+                    x[a][b] -= ua * v[b];
+            }
+            // row j of X: X_j = R_j / L_jj, published at the lane columns
+            if (lr == jr) {
+#pragma unroll
+                for (int b = 0; b <= jb; ++b) {
+                    y[jb][b] *= rs;
+                    rb[lc * E + b] = y[jb][b];
+                }
+            }
+            __syncthreads();
+            T w[E];
+#pragma unroll
+            for (int b = 0; b <= jb; ++b)
+                w[b] = rb[lc * E + b];
+            // R_t -= L_tj X_j for rows t = lr + G a > j (u is zero elsewhere)
+#pragma unroll
+            for (int a = jb; a < E; ++a) {
+                const T ltj = u[a] * rs;
+#pragma unroll
+                for (int b = 0; b <= jb; ++b)
+                    y[a][b] -= ltj * w[b];
+            }
+        }
+    }
+
+    // L (lower) and X^T (strict upper)
+#pragma unroll
+    for (int a = 0; a < E; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b) {
+            const int i = lr + G * a, k = lc + G * b;
+            if (i < n && k <= i) {
+                W[(int64_t)i * ld + k] = x[a][b];
+                if (k < i)
+                    W[(int64_t)k * ld + i] = y[a][b];
+            }
+        }
+    if (tid == 0)
+        write_info(info, 0, fail, info_mode, info_base);
+}
+
 // ------------------------------------------------------------------ hosts ----
+// The 16-byte path needs every row start of every matrix on a 16-byte boundary.
+static inline bool rows_aligned16(const void *p, int64_t ld, int64_t stride)
+{
+    return ((uintptr_t)p % 16) == 0 && ld % 4 == 0 && stride % 4 == 0;
+}
+
 template <typename T, int G, int E>
 static chol_status launch_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
                                      T *L, int64_t ldl, int64_t sL, int32_t *info, int info_mode,
@@ -430,7 +729,15 @@ static chol_status launch_potrf_tile(int n, int64_t batch, const T *A, int64_t l
 {
     typedef TileShape<G, E> S;
     const int64_t blocks = (batch + S::MPB - 1) / S::MPB;
-    hipLaunchKernelGGL((k_potrf_tile<T, G, E>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
+    if constexpr (sizeof(T) == 4 && G == 4 && E % 4 == 0) {
+        if (n == S::NP && rows_aligned16(A, lda, sA) && rows_aligned16(L, ldl, sL)) {
+            hipLaunchKernelGGL((k_potrf_tile<T, G, E, true>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
+                               n, batch, A, lda, sA, L, ldl, sL, info, info_mode, info_base);
+            CHOL_LAUNCH_CHECK();
+            return CHOL_OK;
+        }
+    }
+    hipLaunchKernelGGL((k_potrf_tile<T, G, E, false>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
                        n, batch, A, lda, sA, L, ldl, sL, info, info_mode, info_base);
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;
@@ -443,7 +750,16 @@ static chol_status launch_adj_tile(int n, int64_t batch, const T *L, int64_t ldl
 {
     typedef TileShape<G, E> S;
     const int64_t blocks = (batch + S::MPB - 1) / S::MPB;
-    hipLaunchKernelGGL((k_potrf_adj_tile<T, G, E>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
+    if constexpr (sizeof(T) == 4 && G == 4 && E % 4 == 0) {
+        if (n == S::NP && rows_aligned16(L, ldl, sL) && rows_aligned16(adjL, ldal, sAL) &&
+            rows_aligned16(adjA, ldaa, sAA)) {
+            hipLaunchKernelGGL((k_potrf_adj_tile<T, G, E, true>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
+                               n, batch, L, ldl, sL, adjL, ldal, sAL, adjA, ldaa, sAA, accumulate);
+            CHOL_LAUNCH_CHECK();
+            return CHOL_OK;
+        }
+    }
+    hipLaunchKernelGGL((k_potrf_adj_tile<T, G, E, false>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
                        n, batch, L, ldl, sL, adjL, ldal, sAL, adjA, ldaa, sAA, accumulate);
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;
@@ -465,11 +781,17 @@ chol_status small_potrf(int n, int64_t batch, const T *A, int64_t lda, int64_t s
     return launch_potrf_tile<T, 8, 8>(n, batch, A, lda, sA, L, ldl, sL, info, info_mode, info_base, st);
 }
 
-// Diagonal tile of the blocked factor: n <= 128, one 256-thread block.
+// Diagonal tile of the blocked factor: n <= 128, one 256-thread block; with
+// `inverse`, the tile's inverse is also formed (transposed, strict upper).
 template <typename T>
-chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base,
+chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, bool inverse,
                        hipStream_t st)
 {
+    if (inverse) {
+        hipLaunchKernelGGL((k_potrf_inv_tile<T>), dim3(1), dim3(256), 0, st, n, W, ld, info, info_mode, info_base);
+        CHOL_LAUNCH_CHECK();
+        return CHOL_OK;
+    }
     if (n <= 64)
         return small_potrf<T>(n, 1, W, ld, 0, W, ld, 0, info, info_mode, info_base, st);
     return launch_potrf_tile<T, 16, 8>(n, 1, W, ld, 0, W, ld, 0, info, info_mode, info_base, st);
@@ -503,7 +825,7 @@ chol_status wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar
 #define CHOL_INST(T)                                                                                      \
     template chol_status small_potrf<T>(int, int64_t, const T *, int64_t, int64_t, T *, int64_t, int64_t, \
                                         int32_t *, int, int64_t, hipStream_t);                            \
-    template chol_status diag_potrf<T>(int, T *, int64_t, int32_t *, int, int64_t, hipStream_t);          \
+    template chol_status diag_potrf<T>(int, T *, int64_t, int32_t *, int, int64_t, bool, hipStream_t);    \
     template chol_status small_potrf_adjoint<T>(int, int64_t, const T *, int64_t, int64_t, const T *,     \
                                                 int64_t, int64_t, T *, int64_t, int64_t, int, hipStream_t); \
     template chol_status wave_dot<T>(int, const T *, const T *, T *, const T *, T *, T *, int, hipStream_t);

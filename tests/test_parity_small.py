@@ -144,13 +144,58 @@ def test_strided_views_and_in_place():
     assert np.array_equal(np.tril(host(buf)), np.tril(ref))
 
 
+@pytest.mark.parametrize("n", [16, 32])
+def test_fp32_row_alignment_paths_agree(n):
+    """fp32 tiles of edge 16 or 32 whose rows start on 16-byte boundaries move
+    through 16-byte accesses; other leading dimensions take 4-byte accesses.
+    Both must give the same bits, write nothing outside the lower triangle
+    (adjoint) or the n x n tile (factor), and work in place."""
+    batch = 13
+    A = workloads.batched_spd(batch, n, seed=21 + n, dtype=np.float32)
+    adjL = workloads.lower_normal(n, seed=22 + n, batch=batch, dtype=np.float32)
+    base = np.random.default_rng(23).standard_normal((batch, n, n)).astype(np.float32)
+    results = {}
+    for ld in (n, n + 4, n + 1):                      # aligned, aligned view, unaligned view
+        big = np.full((batch, n + 2, ld), 5.0, dtype=np.float32)
+        big[:, :n, :n] = A
+        Ab = dev(big)
+        view = Ab[:, :n, :n]
+        _, info = dc().chol_potrf_batched(view, L=view)        # in place
+        bigh = host(Ab)
+        assert np.all(host(info) == 0)
+        assert np.all(bigh[:, :n, n:] == 5.0) and np.all(bigh[:, n:, :] == 5.0)
+        Lh = bigh[:, :n, :n].copy()
+        gbig = np.full((batch, n + 2, ld), 5.0, dtype=np.float32)
+        gbig[:, :n, :n] = base
+        Gb = dev(gbig)
+        gview = Gb[:, :n, :n]
+        dc().chol_potrf_adjoint_batched(dev(Lh), dev(adjL), gview, accumulate=True)
+        gh = host(Gb)
+        assert np.array_equal(np.triu(gh[:, :n, :n], 1), np.triu(base, 1))    # strict upper untouched
+        assert np.all(gh[:, :n, n:] == 5.0) and np.all(gh[:, n:, :] == 5.0)
+        results[ld] = (Lh, gh[:, :n, :n].copy())
+    Lo, _ = oracle.potrf(A)
+    assert_close(results[n][0], Lo, 2e-4, "L")
+    Go = oracle.potrf_adjoint(results[n][0], adjL, base, accumulate=True)
+    assert_close(np.tril(results[n][1]), np.tril(Go), 2e-4, "adj_A")
+    for ld in (n + 4, n + 1):
+        assert np.array_equal(results[ld][0], results[n][0])
+        assert np.array_equal(results[ld][1], results[n][1])
+    # adjoint in place over adj_L (accumulate = 0) on the 16-byte path
+    buf = dev(adjL)
+    dc().chol_potrf_adjoint_batched(dev(results[n][0]), buf, buf, accumulate=False)
+    ref = host(dc().chol_potrf_adjoint_batched(dev(results[n][0]), dev(adjL), accumulate=False))
+    assert np.array_equal(np.tril(host(buf)), np.tril(ref))
+
+
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
-def test_info_per_batch_element(dtype):
-    n, batch = 12, 10
+@pytest.mark.parametrize("n", [12, 32])
+def test_info_per_batch_element(n, dtype):
+    batch = 10
     A = workloads.batched_spd(batch, n, seed=13, dtype=np.float64)
     A[2, 0, 0] = -1.0
     A[5, 7, 7] = -50.0
-    A[8, 11, 11] = np.nan
+    A[8, n - 1, n - 1] = np.nan
     A = A.astype(dtype)
     _, info = dc().chol_potrf_batched(dev(A))
     _, io = oracle.potrf(A)

@@ -355,12 +355,14 @@ static inline int tile_splits(int64_t K, int64_t &chunk)
 }
 
 // C (M x N) -= Sym(S)[0:M, 0:K] B with S symmetric stored as its lower triangle
-// (diagonal doubled by the operand) and B k-major; the contraction is split so
+// (diagonal doubled by the operand), its leading excl x excl block left out,
+// and B k-major; the contraction is split so
 // that the launch fills at most one wave of blocks, and the partials are summed
 // in a fixed order, so the result does not depend on scheduling.
 template <typename T>
 static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, const T *B, int64_t ldb, T *C,
-                               int64_t ldc, T *part, int max_splits, int min_chunk, int *sched, hipStream_t st)
+                               int64_t ldc, int excl, T *part, int max_splits, int min_chunk, int *sched,
+                               hipStream_t st)
 {
     if (M <= 0 || N <= 0 || K <= 0)
         return CHOL_OK;
@@ -379,6 +381,7 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
     const int used = (K + p.kchunk - 1) / p.kchunk;
     p.part = part;
     p.sched = sched;
+    p.excl = excl;
     chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st);
     if (s != CHOL_OK)
         return s;
@@ -498,20 +501,19 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
             }
 }
 
-// Reverse sweep over the tile columns with depth-1 look-ahead.  With
-// Bk = rows of tile column k+1 and Rk = rows past it, tile column k's adjoint
-// of the trailing update, Wb_panel(k) -= Sym(Wb22(k)) L_panel(k), is the sum of
-//   early:  Wb[Rk]  -= Sym(Wb[Rk, Rk]) L[Rk]     needs Wb22(k+1): final after
-//                                                tile column k+2 is done
-//   late_a: Wb[Rk]  -= X(k+1) L[Bk]              needs X(k+1) = Wb_panel(k+1)
-//   late_b: Wb[Bk]  -= X(k+1)^T L[Rk]                after its panel-solve adjoint
-//   late_c: Wb[Bk]  -= Sym(G(k+1)) L[Bk]         needs the tile adjoint G(k+1)
-// (all L terms restricted to tile column k).  The wide stream sx runs, per
-// tile column k: the reduction that lands late_b and late_c, the panel-solve
-// adjoint X(k) = Wb_panel(k) Linv_k, the tile-sized product Wb_kk -= tril(X^T L),
-// then -- while the one-block stream sc computes the tile adjoint G(k), with
-// late_c of tile column k-1 as its last stage -- late_a, late_b and early of
-// tile column k-1.
+// Reverse sweep over the tile columns with depth-1 look-ahead.  Tile column
+// j's adjoint of the trailing update, Wb_panel(j) -= Sym(Wb22(j)) L_panel(j),
+// with Wb22(j) starting at tile column k = j+1, is split as
+//   Sym(Wb22(j)) without its leading block Wb_kk:  available once the
+//                 panel-solve adjoint of tile column k has produced
+//                 X(k) = Wb_panel(k) (the rest of Wb22(k) is final by then);
+//   Sym(G(k)) L[tile k, tile j]:  needs the tile adjoint G(k) = the final Wb_kk.
+// The wide stream sx runs, per tile column k: the reduction that adds the
+// second term of tile column k (from tile column k+1's tile adjoint), the
+// panel-solve adjoint X(k) = Wb_panel(k) Linv_k, the tile-sized product
+// Wb_kk -= tril(X^T L_panel), and then -- while the one-block stream sc runs
+// the tile adjoint G(k), ending with the second term of tile column k-1 --
+// the first term of tile column k-1 as one symmetric product.
 template <typename T>
 static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
                                       int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t sc,
@@ -538,6 +540,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
     T *part_b = (T *)w;
     w += align256((size_t)(TILE_SPLIT_MAX + 1) * nb * nb * sizeof(T));
     T *part_c = (T *)w;
+    T *slot = part_b + (int64_t)TILE_SPLIT_MAX * nb * nb;   // Sym(G(k)) L[tile k, tile k-1]
 
     if ((const T *)Wb != adjL) {
         if ((s = tri_op<T, TRI_COPY_LOWER>(n, adjL, ldal, Wb, ldw, sx)) != CHOL_OK)
@@ -550,7 +553,6 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         CHOL_LAUNCH_CHECK();
     }
 
-    int pending = -1;   // splits in part_b waiting for the tile adjoint's slot (-1: none)
     for (int64_t k = K - 1; k >= 0; --k) {
         const int64_t k0 = k * nb;
         const int kb = (int)std::min<int64_t>(nb, n - k0);
@@ -562,15 +564,15 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         const T *Lp = L + r0 * ldl + k0;       // L_panel, m x kb
         T *Wp = Wb + r0 * ldw + k0;            // Wb_panel, m x kb
         if (m > 0) {
-            // late_b and late_c of this tile column (the latter from tile column
-            // k+1's tile adjoint on sc) land in the first kn rows of Wb_panel
+            // the second term of this tile column (from tile column k+1's tile
+            // adjoint on sc) lands in the first kn rows of Wb_panel
             if (stream_join(sx, sc, e_tile) != hipSuccess)
                 return CHOL_ERR_HIP;
             {
                 prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 0.0);
                 const int64_t tot = (int64_t)kn * kb;
                 hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, sx,
-                                   kn, kb, pending + 1, (const T *)part_b, Wp, ldw);
+                                   kn, kb, 1, (const T *)slot, Wp, ldw);
                 CHOL_LAUNCH_CHECK();
             }
             // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block)
@@ -603,55 +605,27 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 CHOL_LAUNCH_CHECK();
             }
         }
-        // tile adjoint of tile column k on sc; its last stage is late_c of
-        // tile column k-1, written after the late_b partials of k-1
+        // tile adjoint of tile column k on sc; its last stage is the second
+        // term of tile column k-1
         const int64_t j0 = k0 - nb;                 // previous tile column (if k >= 1)
-        int64_t late_b_chunk = 0;
-        const int late_b_splits = (k >= 1 && m > 0) ? tile_splits(m, late_b_chunk) : 0;
         if (stream_join(sc, sx, e_wide) != hipSuccess)
             return CHOL_ERR_HIP;
         {
             prof::Scope ps(CHOL_K_ADJ_DIAG, sc, 2.0 * kb * kb * kb / 3 + (k >= 1 ? 2.0 * kb * kb * nb : 0.0));
             const T *Lnext = (k >= 1) ? L + k0 * ldl + j0 : nullptr;
-            T *slot = (k >= 1) ? part_b + (int64_t)late_b_splits * kb * nb : nullptr;
             hipLaunchKernelGGL((k_tile_adjoint<T>), dim3(1), dim3(256), 0, sc, kb, Lkk, ldl, Wkk, ldw, invk,
-                               (int64_t)nb, part_c, part_c + (int64_t)nb * nb, (int64_t)nb, Lnext, nb, slot);
+                               (int64_t)nb, part_c, part_c + (int64_t)nb * nb, (int64_t)nb, Lnext, nb,
+                               k >= 1 ? slot : (T *)nullptr);
             CHOL_LAUNCH_CHECK();
         }
-        pending = (k >= 1) ? late_b_splits : -1;
+        // first term of tile column k-1: rows and columns from tile column k on,
+        // the block Wb_kk left out
         if (k >= 1 && m > 0) {
-            const T *Lj = L + r0 * ldl + j0;        // L[rows past tile column k, tile column k-1]
-            // late_a(k-1): Wb[r0:, j] -= X(k) L[tile k, tile j]
-            {
-                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * m * kb * nb);
-                GemmArgs<T> p{};
-                p.M = (int)m; p.N = nb; p.K = kb;
-                p.a = Wp; p.lda = ldw;
-                p.b = L + k0 * ldl + j0; p.ldb = ldl;
-                p.c = Wb + r0 * ldw + j0; p.ldc = ldw;
-                if ((s = gemm<T, OP_MK, OP_KM, C_SUB>(p, 1, sx)) != CHOL_OK)
-                    return s;
-            }
-            // late_b(k-1) partials: X(k)^T L[r0:, tile j]  (kb x nb, contraction over m)
-            {
-                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * m * kb * nb);
-                GemmArgs<T> p{};
-                p.M = kb; p.N = nb; p.K = (int)m;
-                p.a = Wp; p.lda = ldw;
-                p.b = Lj; p.ldb = ldl;
-                p.kchunk = (int)late_b_chunk;
-                p.part = part_b;
-                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, late_b_splits, sx)) != CHOL_OK)
-                    return s;
-            }
-            // early(k-1): Wb[r0+kn':, j] -= Sym(Wb22(k)) L[r0:, j] restricted to rows and
-            // columns past tile column k, i.e. Wb22(k) itself
-            {
-                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * nb * (double)m * m);
-                if ((s = sym_product<T>((int)m, nb, (int)m, Wb + r0 * ldw + r0, ldw, Lj, ldl, Wb + r0 * ldw + j0,
-                                        ldw, part_x, SIDE_SPLIT_MAX, 256, sched_x, sx)) != CHOL_OK)
-                    return s;
-            }
+            prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * nb * ((double)(m + kb) * (m + kb) - (double)kb * kb));
+            if ((s = sym_product<T>((int)(m + kb), nb, (int)(m + kb), Wkk, ldw, L + k0 * ldl + j0, ldl,
+                                    Wb + k0 * ldw + j0, ldw, kb, part_x, SIDE_SPLIT_MAX, 256, sched_x, sx)) !=
+                CHOL_OK)
+                return s;
         }
     }
     if (stream_join(sx, sc, e_tile) != hipSuccess)

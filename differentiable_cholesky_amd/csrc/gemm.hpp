@@ -47,6 +47,8 @@ template <typename T> struct GemmArgs {
     int tri;             // 1: lower-triangular tile grid (M == N)
     int vec;             // 1: 16-byte global loads are legal for both operands
     int splits;          // split count (C_PARTIAL)
+    int excl;            // OP_SYM A operand: entries (m, k) with m < excl and
+                         // k < excl read as zero (a block left out of the product)
     int *sched;          // non-null: blocks take (split, tile) items from this
                          // device counter pair (item, finished blocks), which
                          // must be zero at launch and is zero again afterwards
@@ -64,9 +66,11 @@ template <> struct Pitch<float> { static constexpr int v = 132; };
 
 // element (m, k) of an operand, with bounds (m < mlim, k < klim) -> 0 outside
 template <typename T, int OP>
-__device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim, int klim)
+__device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim, int klim, int excl)
 {
     if (m >= mlim || k >= klim)
+        return T(0);
+    if (OP == OP_SYM && m < excl && k < excl)
         return T(0);
     if (OP == OP_MK)
         return p[(int64_t)m * ld + k];
@@ -125,6 +129,7 @@ struct Operand {
     int m0;      // tile origin along m
     int mlim;    // M (or N) bound
     int vec;
+    int excl;    // OP_SYM: leading excl x excl block left out
 
     // layout used for a chunk starting at k0 (uniform over the block)
     __device__ __forceinline__ int layout(int k0) const
@@ -141,7 +146,7 @@ struct Operand {
         if (!vec || m0 + BM > mlim || k0 + BK > klim)
             return true;
         if (OP == OP_SYM)
-            return !(m0 >= k0 + BK || m0 + BM <= k0);
+            return !(m0 >= k0 + BK || m0 + BM <= k0) || (m0 < excl && k0 < excl);
         if (OP == OP_KM_LOWER)
             return !(k0 >= m0 + BM - 1);         // plain only if every k >= every m
         if (OP == OP_KM_INVT)
@@ -178,7 +183,7 @@ struct Operand {
                 MP::mk(tid, j, m, k);
             else
                 MP::km(tid, j, m, k);
-            r.v[j] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim);
+            r.v[j] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim, excl);
         }
     }
 
@@ -321,8 +326,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
                 acc[i][j][v] = x;
             }
 
-    Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec};
-    Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec};
+    Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
+    Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec, 0};
     tile_mma<T, AOP, BOP, FROM_C>(acc, A, B, kbeg, kend, lds);
 
 #pragma unroll

@@ -104,6 +104,12 @@ __device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim
 template <typename T> struct Vec8 { T v[8]; };
 enum { LAY_MK = 0, LAY_KM = 1 };
 
+// staging layouts an operand kind can use on the 16-byte path
+constexpr bool can_lay(int op, int lay)
+{
+    return op == OP_SYM || (op == OP_MK ? lay == LAY_MK : lay == LAY_KM);
+}
+
 template <typename T> struct Map {
     static constexpr int PER = 16 / sizeof(T);
     static constexpr int LPR = BK / PER;        // lanes per row (row-panel)
@@ -154,6 +160,49 @@ struct Operand {
         return false;
     }
 
+    // layout of the chunk at k0 if it can take the 16-byte path, else -1
+    __device__ __forceinline__ int fast_lay(int k0, int klim) const
+    {
+        return generic(k0, klim) ? -1 : layout(k0);
+    }
+
+    // 16-byte loads of a chunk known to be on the fast path with layout LAY
+    template <int LAY>
+    __device__ __forceinline__ void fetch_fast(Vec8<T> &r, int tid, int k0) const
+    {
+        typedef Map<T> MP;
+        typedef T vt __attribute__((ext_vector_type(MP::PER)));
+#pragma unroll
+        for (int q = 0; q < 8 / MP::PER; ++q) {
+            int m, k;
+            if (LAY == LAY_MK)
+                MP::mk(tid, q * MP::PER, m, k);
+            else
+                MP::km(tid, q * MP::PER, m, k);
+            const T *src = (LAY == LAY_MK) ? p + (int64_t)(m0 + m) * ld + k0 + k
+                                           : p + (int64_t)(k0 + k) * ld + m0 + m;
+            const vt x = *reinterpret_cast<const vt *>(src);
+#pragma unroll
+            for (int e = 0; e < MP::PER; ++e)
+                r.v[q * MP::PER + e] = x[e];
+        }
+    }
+
+    template <int LAY>
+    static __device__ __forceinline__ void stash_lay(const Vec8<T> &r, T *S, int tid)
+    {
+        typedef Map<T> MP;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int m, k;
+            if (LAY == LAY_MK)
+                MP::mk(tid, j, m, k);
+            else
+                MP::km(tid, j, m, k);
+            S[k * Pitch<T>::v + m] = r.v[j];
+        }
+    }
+
     __device__ __forceinline__ void fetch(Vec8<T> &r, int tid, int k0, int klim) const
     {
         typedef Map<T> MP;
@@ -187,6 +236,22 @@ struct Operand {
         }
     }
 
+    // per-element path straight into the LDS chunk
+    __device__ __forceinline__ void put(T *S, int tid, int k0, int klim) const
+    {
+        typedef Map<T> MP;
+        const int lay = layout(k0);
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+            int m, k;
+            if (lay == LAY_MK)
+                MP::mk(tid, j, m, k);
+            else
+                MP::km(tid, j, m, k);
+            S[k * Pitch<T>::v + m] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim, excl);
+        }
+    }
+
     __device__ __forceinline__ void stash(const Vec8<T> &r, T *S, int tid, int k0) const
     {
         typedef Map<T> MP;
@@ -214,58 +279,98 @@ __device__ __forceinline__ int xcd_tile(int b, int nt)
 
 } // namespace gemm_detail
 
-// The K loop of one 128 x 128 tile: acc += (NEG ? -A : A) B over k in
-// [kbeg, kend), operands staged through `lds` (2 buffers x 2 operands x
-// BK * Pitch<T>::v elements).  Called by all 256 threads of the block.
-// A's global loads run two chunks ahead of the matrix cores (chunk c+1 waits
-// in one register set to be written to LDS while chunk c+2 is in flight in
-// the other); B, a panel that stays in L2, is fetched one chunk ahead.
-template <typename T, int AOP, int BOP, bool NEG>
-__device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
-                                         const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
+namespace gemm_detail {
+
+// acc += (NEG ? -A : B) over one chunk staged at SA (A) and SB (B) in LDS
+template <typename T, bool NEG>
+__device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], const T *SA, const T *SB, int lane,
+                                          int wm, int wn)
 {
-    using namespace gemm_detail;
-    constexpr int PITCH = Pitch<T>::v, SZ = BK * PITCH;
+    constexpr int PITCH = Pitch<T>::v;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 4) {
+        const int kr = kk + lane / 16;
+        T af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            af[i] = SA[kr * PITCH + wm * 64 + i * 16 + lane % 16];
+            if (NEG)
+                af[i] = -af[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = SB[kr * PITCH + wn * 64 + j * 16 + lane % 16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = mfma16x16x4(af[i], bf[j], acc[i][j]);
+    }
+}
+
+// A run of nc >= 1 chunks starting at k0, all on the 16-byte path with fixed
+// layouts.  Software pipeline: while the matrix cores work on one LDS buffer,
+// the other is filled from registers loaded one chunk earlier, and the next
+// chunk's loads are issued.  Every load is unconditional (indices past the run
+// repeat its last chunk), so no loaded register ever merges with an older
+// value and the loads stay in flight across the matrix-core work.
+template <typename T, int AOP, int BOP, int LA, int LB, bool NEG>
+__device__ __forceinline__ void mma_run(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
+                                        const Operand<T, BOP> &B, int k0, int nc, T *lds)
+{
+    constexpr int SZ = BK * Pitch<T>::v;
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int wm = wave / 2, wn = wave % 2;
+    auto kc = [&](int c) { return k0 + (c < nc ? c : nc - 1) * BK; };
+    Vec8<T> a, b;
+    A.template fetch_fast<LA>(a, tid, k0);
+    B.template fetch_fast<LB>(b, tid, k0);
+    __syncthreads();                      // earlier users of the LDS buffers are done
+    Operand<T, AOP>::template stash_lay<LA>(a, lds, tid);
+    Operand<T, BOP>::template stash_lay<LB>(b, lds + SZ, tid);
+    A.template fetch_fast<LA>(a, tid, kc(1));
+    B.template fetch_fast<LB>(b, tid, kc(1));
+    __syncthreads();
+    for (int c = 0; c < nc; ++c) {
+        const T *S = lds + (c & 1) * 2 * SZ;
+        T *D = lds + ((c + 1) & 1) * 2 * SZ;
+        chunk_mma<T, NEG>(acc, S, S + SZ, lane, wm, wn);                   // chunk c
+        Operand<T, AOP>::template stash_lay<LA>(a, D, tid);                // chunk c+1
+        Operand<T, BOP>::template stash_lay<LB>(b, D + SZ, tid);
+        A.template fetch_fast<LA>(a, tid, kc(c + 2));
+        B.template fetch_fast<LB>(b, tid, kc(c + 2));
+        __syncthreads();
+    }
+}
+
+// The K loop through the general path, chunk by chunk, for tiles with edges,
+// diagonal crossings or masks: every chunk is fetched by the path it needs
+// (16-byte or per element).  A's loads run two chunks ahead, B's one.
+template <typename T, int AOP, int BOP, bool NEG>
+__device__ __forceinline__ void mma_general(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
+                                            const Operand<T, BOP> &B, int kbeg, int kend, T *lds)
+{
+    constexpr int SZ = BK * Pitch<T>::v;
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int wm = wave / 2, wn = wave % 2;
     Vec8<T> ra0, ra1, rb;
-    if (kbeg < kend) {
-        A.fetch(ra0, tid, kbeg, kend);
-        B.fetch(rb, tid, kbeg, kend);
-        A.stash(ra0, lds, tid, kbeg);
-        B.stash(rb, lds + SZ, tid, kbeg);
-        if (kbeg + BK < kend) {
-            A.fetch(ra1, tid, kbeg + BK, kend);
-            B.fetch(rb, tid, kbeg + BK, kend);
-        }
-        if (kbeg + 2 * BK < kend)
-            A.fetch(ra0, tid, kbeg + 2 * BK, kend);
+    __syncthreads();
+    A.fetch(ra0, tid, kbeg, kend);
+    B.fetch(rb, tid, kbeg, kend);
+    A.stash(ra0, lds, tid, kbeg);
+    B.stash(rb, lds + SZ, tid, kbeg);
+    if (kbeg + BK < kend) {
+        A.fetch(ra1, tid, kbeg + BK, kend);
+        B.fetch(rb, tid, kbeg + BK, kend);
     }
+    if (kbeg + 2 * BK < kend)
+        A.fetch(ra0, tid, kbeg + 2 * BK, kend);
     __syncthreads();
     int c = 0;
     for (int k0 = kbeg; k0 < kend; k0 += BK, ++c) {
         const int buf = c & 1;
         const T *SA = lds + buf * 2 * SZ;
-        const T *SB = SA + SZ;
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 4) {
-            const int kr = kk + lane / 16;
-            T af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = SA[kr * PITCH + wm * 64 + i * 16 + lane % 16];
-                if (NEG)
-                    af[i] = -af[i];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = SB[kr * PITCH + wn * 64 + j * 16 + lane % 16];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = mfma16x16x4(af[i], bf[j], acc[i][j]);
-        }
+        chunk_mma<T, NEG>(acc, SA, SA + SZ, lane, wm, wn);
         if (k0 + BK < kend) {
             T *D = lds + (buf ^ 1) * 2 * SZ;
             B.stash(rb, D + SZ, tid, k0 + BK);
@@ -283,6 +388,61 @@ __device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], con
             }
         }
         __syncthreads();
+    }
+}
+
+} // namespace gemm_detail
+
+// The K loop of one 128 x 128 tile: acc += (NEG ? -A : A) B over k in
+// [kbeg, kend), operands staged through `lds` (2 buffers x 2 operands x
+// BK * Pitch<T>::v elements).  Called by all 256 threads of the block.  When
+// every chunk can take the 16-byte path, the range is cut into runs of chunks
+// on which both operands keep one layout each (pipelined); otherwise the tile
+// takes the general loop.
+template <typename T, int AOP, int BOP, bool NEG, bool RUNS>
+__device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
+                                         const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
+{
+    using namespace gemm_detail;
+    // products whose operands are rarely on the 16-byte path, and those that
+    // start their accumulators from C (the extra registers of the pipelined
+    // runs would not fit beside them), always take the general loop
+    if constexpr (!RUNS) {
+        mma_general<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, lds);
+        return;
+    }
+    // any chunk that needs the per-element path sends the whole tile down the
+    // general loop (kept apart so the fast runs stay lean in registers)
+    for (int k = kbeg; k < kend; k += BK) {
+        if (A.fast_lay(k, kend) < 0 || B.fast_lay(k, kend) < 0) {
+            mma_general<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, lds);
+            return;
+        }
+    }
+    int k = kbeg;
+    while (k < kend) {
+        const int la = A.fast_lay(k, kend), lb = B.fast_lay(k, kend);
+        int nc = 1;
+        while (k + nc * BK < kend && A.fast_lay(k + nc * BK, kend) == la && B.fast_lay(k + nc * BK, kend) == lb)
+            ++nc;
+        // only the layout pairs the operand kinds can produce are instantiated
+        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_MK)) {
+            if (la == LAY_MK && lb == LAY_MK)
+                mma_run<T, AOP, BOP, LAY_MK, LAY_MK, NEG>(acc, A, B, k, nc, lds);
+        }
+        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_KM)) {
+            if (la == LAY_MK && lb == LAY_KM)
+                mma_run<T, AOP, BOP, LAY_MK, LAY_KM, NEG>(acc, A, B, k, nc, lds);
+        }
+        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_MK)) {
+            if (la == LAY_KM && lb == LAY_MK)
+                mma_run<T, AOP, BOP, LAY_KM, LAY_MK, NEG>(acc, A, B, k, nc, lds);
+        }
+        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_KM)) {
+            if (la == LAY_KM && lb == LAY_KM)
+                mma_run<T, AOP, BOP, LAY_KM, LAY_KM, NEG>(acc, A, B, k, nc, lds);
+        }
+        k += nc * BK;
     }
 }
 
@@ -328,7 +488,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
 
     Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
     Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec, 0};
-    tile_mma<T, AOP, BOP, FROM_C>(acc, A, B, kbeg, kend, lds);
+    constexpr bool PLAIN = (AOP == OP_MK || AOP == OP_KM || AOP == OP_SYM) && (BOP == OP_MK || BOP == OP_KM);
+    tile_mma<T, AOP, BOP, FROM_C, PLAIN && !FROM_C>(acc, A, B, kbeg, kend, lds);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)

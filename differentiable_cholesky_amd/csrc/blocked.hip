@@ -219,7 +219,7 @@ static inline int split_chunk(int64_t K, int splits)
 template <typename T>
 static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info,
                                     int nb, hipStream_t sc, hipStream_t sx, hipEvent_t e_diag, hipEvent_t e_next,
-                                    int *sched_x)
+                                    int *sched_x, int cap_x)
 {
     chol_status s;
     if (A != L) {
@@ -290,6 +290,7 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             p.c = L + (r0 + kn) * ldl + r0 + kn; p.ldc = ldl;
             p.tri = 1;
             p.sched = sched_x;
+            p.cap = cap_x;
             prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, (double)m2 * (m2 + 1) * kb);
             if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx)) != CHOL_OK)
                 return s;
@@ -313,7 +314,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
     if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
         return CHOL_ERR_HIP;
     const chol_status s = blocked_potrf_on<T>(n, A, lda, L, ldl, info, nb, sd->chain, sd->x, sd->ev[0], sd->ev[1],
-                                              sd->sched);
+                                              sd->sched, 2 * sd->wide_cus);
     const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
                         stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
     if (s != CHOL_OK)
@@ -362,7 +363,7 @@ static inline int tile_splits(int64_t K, int64_t &chunk)
 template <typename T>
 static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, const T *B, int64_t ldb, T *C,
                                int64_t ldc, int excl, T *part, int max_splits, int min_chunk, int *sched,
-                               hipStream_t st)
+                               int cap, double flops, hipStream_t st)
 {
     if (M <= 0 || N <= 0 || K <= 0)
         return CHOL_OK;
@@ -374,18 +375,23 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
     // about four (split, tile) items per block slot, taken dynamically by
     // persistent blocks, so that blocks slowed by a neighbour take fewer
     const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t want = 4 * 2 * (256 - 16);
+    const int64_t want = 4 * (int64_t)cap;
     int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (want + tiles - 1) / tiles));
     splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, K / min_chunk));
     p.kchunk = split_chunk(K, splits);
     const int used = (K + p.kchunk - 1) / p.kchunk;
     p.part = part;
     p.sched = sched;
+    p.cap = cap;
     p.excl = excl;
-    chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st);
-    if (s != CHOL_OK)
-        return s;
+    {
+        prof::Scope ps(CHOL_K_ADJ_TRAILING, st, flops);
+        chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st);
+        if (s != CHOL_OK)
+            return s;
+    }
     const int64_t tot = (int64_t)M * N;
+    prof::Scope ps(CHOL_K_REDUCE, st, (double)tot * (used + 2) * sizeof(T));
     hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N, used,
                        (const T *)part, C, ldc);
     CHOL_LAUNCH_CHECK();
@@ -517,7 +523,8 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
 template <typename T>
 static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
                                       int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t sc,
-                                      hipStream_t sx, hipEvent_t e_tile, hipEvent_t e_wide, int *sched_x)
+                                      hipStream_t sx, hipEvent_t e_tile, hipEvent_t e_wide, int *sched_x,
+                                      int cap_x)
 {
     chol_status s;
     const int64_t K = (n + nb - 1) / nb;
@@ -569,8 +576,8 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
             if (stream_join(sx, sc, e_tile) != hipSuccess)
                 return CHOL_ERR_HIP;
             {
-                prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 0.0);
                 const int64_t tot = (int64_t)kn * kb;
+                prof::Scope ps(CHOL_K_REDUCE, sx, 3.0 * tot * sizeof(T));
                 hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, sx,
                                    kn, kb, 1, (const T *)slot, Wp, ldw);
                 CHOL_LAUNCH_CHECK();
@@ -592,14 +599,17 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 p.M = kb; p.N = kb; p.K = (int)m;
                 p.a = Wp; p.lda = ldw;
                 p.b = Lp; p.ldb = ldl;
-                prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, sx, (double)m * kb * (kb + 1));
                 int64_t chunk;
                 const int splits = tile_splits(m, chunk);
                 p.kchunk = (int)chunk;
                 p.part = part_b;
-                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sx)) != CHOL_OK)
-                    return s;
+                {
+                    prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, sx, 2.0 * m * kb * kb);
+                    if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sx)) != CHOL_OK)
+                        return s;
+                }
                 const int64_t tot = (int64_t)kb * kb;
+                prof::Scope ps(CHOL_K_REDUCE, sx, (double)tot * (splits + 2) * sizeof(T));
                 hipLaunchKernelGGL((k_splitk_reduce_lower<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256),
                                    0, sx, kb, splits, (const T *)part_b, Wkk, ldw);
                 CHOL_LAUNCH_CHECK();
@@ -621,10 +631,10 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         // first term of tile column k-1: rows and columns from tile column k on,
         // the block Wb_kk left out
         if (k >= 1 && m > 0) {
-            prof::Scope ps(CHOL_K_ADJ_TRAILING, sx, 2.0 * nb * ((double)(m + kb) * (m + kb) - (double)kb * kb));
+            const double flops = 2.0 * nb * ((double)(m + kb) * (m + kb) - (double)kb * kb);
             if ((s = sym_product<T>((int)(m + kb), nb, (int)(m + kb), Wkk, ldw, L + k0 * ldl + j0, ldl,
-                                    Wb + k0 * ldw + j0, ldw, kb, part_x, SIDE_SPLIT_MAX, 256, sched_x, sx)) !=
-                CHOL_OK)
+                                    Wb + k0 * ldw + j0, ldw, kb, part_x, SIDE_SPLIT_MAX, 256, sched_x, cap_x,
+                                    flops, sx)) != CHOL_OK)
                 return s;
         }
     }
@@ -646,7 +656,7 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
     if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
         return CHOL_ERR_HIP;
     const chol_status s = blocked_adjoint_on<T>(n, L, ldl, adjL, ldal, adjA, ldaa, accumulate, nb, ws, sd->chain,
-                                                sd->x, sd->ev[0], sd->ev[1], sd->sched);
+                                                sd->x, sd->ev[0], sd->ev[1], sd->sched, 2 * sd->wide_cus);
     const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
                         stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
     if (s != CHOL_OK)

@@ -49,6 +49,7 @@ template <typename T> struct GemmArgs {
     int splits;          // split count (C_PARTIAL)
     int excl;            // OP_SYM A operand: entries (m, k) with m < excl and
                          // k < excl read as zero (a block left out of the product)
+    int cap;             // persistent grid size with `sched` (0: two blocks per CU of 240)
     int *sched;          // non-null: blocks take (split, tile) items from this
                          // device counter pair (item, finished blocks), which
                          // must be zero at launch and is zero again afterwards
@@ -603,11 +604,9 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
     const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
     if (p.sched) {
-        // persistent blocks, all resident at once: two per CU on all but 16
-        // CUs, whose slots stay free for the one-block kernels of the other
-        // library stream
+        // persistent blocks, all resident at once (two per CU the stream may use)
         const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1);
-        const unsigned grid = (unsigned)std::min<int64_t>(items, 2 * (256 - 16));
+        const unsigned grid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
         hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3(grid), dim3(NT), 0, st, p);
     } else {
         hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1)),

@@ -15,11 +15,18 @@ Side *side_resources()
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
         return nullptr;
     Side &s = g_side[dev];
-    std::call_once(g_once[dev], [&s]() {
+    std::call_once(g_once[dev], [&s, dev]() {
         if (hipStreamCreateWithFlags(&s.chain, hipStreamNonBlocking) != hipSuccess)
+            return;
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             return;
         if (hipStreamCreateWithFlags(&s.x, hipStreamNonBlocking) != hipSuccess)
             return;
+        // persistent grids of the wide stream leave RESERVED_CUS CUs' worth of
+        // block slots free (restricting the stream with a CU mask instead was
+        // measured slower: its launches cost more)
+        s.wide_cus = cus > 4 * RESERVED_CUS ? cus - RESERVED_CUS : cus;
         for (auto &e : s.ev)
             if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
                 return;

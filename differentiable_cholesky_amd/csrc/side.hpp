@@ -3,10 +3,11 @@
 // next tile column (stream `chain`).  Both are created on first use per
 // device and kept for the life of the process, at default priority and
 // non-blocking with respect to the null stream; work is ordered against the
-// caller's stream and between the two streams by events only.  A small device
-// buffer of zeroed work counters is allocated with them (once per device).  The large
-// products are launched with at most one wave of blocks, short of a few
-// block slots that stay free for the one-block kernels.
+// caller's stream and between the two streams by events only.  The large
+// products on the wide stream run as persistent grids of two blocks per CU on
+// all but RESERVED_CUS compute units' worth of block slots, which stay free
+// for the chain's one-block kernels.  A small device buffer of zeroed work
+// counters is allocated with them (once per device).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,16 +16,18 @@
 
 namespace chol {
 
+constexpr int RESERVED_CUS = 16;
+
 struct Side {
     hipStream_t chain = nullptr;   // one-block kernels
     hipStream_t x = nullptr;       // kernels that span the matrix
     hipEvent_t ev[6] = {};
     int *sched = nullptr;          // device counters of dynamically scheduled products
                                    // (SCHED_SLOTS slots of 2 ints, 64 bytes apart)
+    int wide_cus = 0;              // CUs' worth of block slots the persistent grids use
     std::mutex mu;                 // one blocked call enqueues on these resources at a time
     bool ok = false;
 };
-
 constexpr int SCHED_SLOTS = 4;
 constexpr int SCHED_STRIDE = 16;   // ints between slots
 

@@ -46,7 +46,6 @@ template <int G_, int E_> struct TileShape {
     static constexpr int LPM = G * G;                     // lanes per matrix
     static constexpr int THREADS = LPM < 64 ? 64 : LPM;   // one wavefront at least
     static constexpr int MPB = THREADS / LPM;             // matrices per block
-    static constexpr bool UNROLL = false;                 // unroll the lane loop of each step
 };
 
 // Waves per SIMD the register allocation aims for (the scheduler otherwise
@@ -166,11 +165,10 @@ __device__ __forceinline__ void vec_load_lower(float (&dst)[E][E], const float *
     }
 }
 
-// Store rows of one fp32 tile from the cyclic layout.  src(a, b) gives the
-// value of entry (lr + 4a, lc + 4b).  mode 0 writes the whole row (entries
-// right of the diagonal must already be zero in src); mode 1 writes only
-// entries on or left of the diagonal.
-template <int E, int MODE, typename F>
+// Store whole rows of one fp32 tile from the cyclic layout.  src(a, b) gives
+// the value of entry (lr + 4a, lc + 4b); entries right of the diagonal must
+// already be zero in src.
+template <int E, typename F>
 __device__ __forceinline__ void vec_store(float *M, int64_t ld, bool mv, int lr, int lc, F &&src)
 {
 #pragma unroll
@@ -180,7 +178,7 @@ __device__ __forceinline__ void vec_store(float *M, int64_t ld, bool mv, int lr,
         for (int qq = 0; qq < E / 4; ++qq) {
             const int q = lc + 4 * qq;
             if (16 * qq > 4 * a + 3) {
-                if (MODE == 0 && mv)
+                if (mv)
                     *reinterpret_cast<float4 *>(M + (int64_t)r * ld + 4 * q) = make_float4(0.f, 0.f, 0.f, 0.f);
                 continue;
             }
@@ -189,18 +187,8 @@ __device__ __forceinline__ void vec_store(float *M, int64_t ld, bool mv, int lr,
             for (int c = 0; c < 4; ++c)
                 w[c] = src(a, c + 4 * qq);
             quad_transpose(w, lc);
-            if (!mv)
-                continue;
-            float *dst = M + (int64_t)r * ld + 4 * q;
-            if (MODE == 0 || 4 * q + 3 <= r) {
-                *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
-            } else if (4 * q <= r) {
-                dst[0] = w[0];
-                if (4 * q + 1 <= r)
-                    dst[1] = w[1];
-                if (4 * q + 2 <= r)
-                    dst[2] = w[2];
-            }
+            if (mv)
+                *reinterpret_cast<float4 *>(M + (int64_t)r * ld + 4 * q) = make_float4(w[0], w[1], w[2], w[3]);
         }
     }
 }
@@ -247,7 +235,7 @@ k_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
 #pragma unroll
     for (int t_ = 0; t_ < E; ++t_) {
         const int jb = t_;
-#pragma unroll(S::UNROLL ? G : 1)
+#pragma unroll 1
         for (int u_ = 0; u_ < G; ++u_) {
             const int jr = u_;
             const int j = jb * G + jr;
@@ -294,7 +282,7 @@ k_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
 
     // registers -> global: lower triangle and zeroed upper triangle
     if constexpr (VEC) {
-        vec_store<E, 0>(L + (mv ? mat * sL : 0), ldl, mv, lr, lc, [&](int a, int b) {
+        vec_store<E>(L + (mv ? mat * sL : 0), ldl, mv, lr, lc, [&](int a, int b) {
             return (b < a || (b == a && lc <= lr)) ? x[a][b] : 0.f;
         });
         if (mv && lr == 0 && lc == 0)
@@ -321,7 +309,7 @@ k_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
 // step publishes the one row of L it needs and the vector it produces.
 // adj_A may be adj_L itself when accumulate == 0.
 // ------------------------------------------------------------------------
-template <typename T, int G, int E, bool VEC>
+template <typename T, int G, int E>
 __global__ void __launch_bounds__((TileShape<G, E>::THREADS))
 __attribute__((amdgpu_waves_per_eu(TileWaves<T, G, E>::adjoint)))
 k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
@@ -342,19 +330,9 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
     const int64_t mat = (int64_t)blockIdx.x * MPB + g;
     const bool mv = mat < batch;
 
-    static_assert(!VEC || (G == 4 && E % 4 == 0 && sizeof(T) == 4), "16-byte path: fp32, G = 4");
     // global -> registers: L (identity padding) and tril(adj_L) (zero padding)
     T lw[E][E], bw[E][E];
-    if constexpr (VEC) {
-        vec_load_lower<E>(lw, L + (mv ? mat * sL : 0), ldl, mv, lr, lc);
-        __builtin_amdgcn_sched_barrier(0);     // keep the two tiles' raw loads from all being live at once
-        vec_load_lower<E>(bw, adjL + (mv ? mat * sAL : 0), ldal, mv, lr, lc);
-        if (!mv && lr == lc) {
-#pragma unroll
-            for (int a = 0; a < E; ++a)
-                lw[a][a] = T(1);
-        }
-    } else {
+    {
         const T *Lm = L + (mv ? mat * sL : 0);
         const T *Bm = adjL + (mv ? mat * sAL : 0);
 #pragma unroll
@@ -388,7 +366,7 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
 #pragma unroll
     for (int t_ = 0; t_ < E; ++t_) {
         const int kb = t_;
-#pragma unroll(S::UNROLL ? G : 1)
+#pragma unroll 1
         for (int u_ = 0; u_ < G; ++u_) {
             const int kr = u_;
             const int k = kb * G + kr;
@@ -438,7 +416,7 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
 #pragma unroll
     for (int t_ = 0; t_ < E; ++t_) {
         const int jb = E - 1 - t_;
-#pragma unroll(S::UNROLL ? G : 1)
+#pragma unroll 1
         for (int u_ = 0; u_ < G; ++u_) {
             const int jr = G - 1 - u_;
             const int j = jb * G + jr;
@@ -478,8 +456,7 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
 
     // the accumulated output is read while Z is solved
     T acc[E][E];
-    if constexpr (!VEC) {
-      if (accumulate && mv) {
+    if (accumulate && mv) {
         const T *Gm = adjA + mat * sAA;
 #pragma unroll
         for (int a = 0; a < E; ++a)
@@ -488,7 +465,6 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
                 const int i = lr + G * a, k = lc + G * b;
                 acc[a][b] = (i < n && k <= i) ? Gm[(int64_t)i * ldaa + k] : T(0);
             }
-      }
     }
 
     // Z = L^{-T} V (L^T Z = V), lower part, rows i = NP-1 .. 0:
@@ -496,7 +472,7 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
 #pragma unroll
     for (int t_ = 0; t_ < E; ++t_) {
         const int ib = E - 1 - t_;
-#pragma unroll(S::UNROLL ? G : 1)
+#pragma unroll 1
         for (int u_ = 0; u_ < G; ++u_) {
             const int ir = G - 1 - u_;
             const int i = ib * G + ir;
@@ -530,18 +506,7 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
     }
 
     // G = Phi(Z): halve the diagonal; lower triangle only
-    if constexpr (VEC) {
-        // (16-byte path: the accumulated output is read only now, which keeps
-        // its registers out of the solve)
-        if (accumulate)
-            vec_load_lower<E>(acc, adjA + (mv ? mat * sAA : 0), ldaa, mv, lr, lc);
-        vec_store<E, 1>(adjA + (mv ? mat * sAA : 0), ldaa, mv, lr, lc, [&](int a, int b) {
-            if (b > a)
-                return 0.f;
-            const float gv = (b == a && lc == lr) ? p[a][b] * 0.5f : p[a][b];
-            return accumulate ? acc[a][b] + gv : gv;
-        });
-    } else if (mv) {
+    if (mv) {
         T *Gm = adjA + mat * sAA;
 #pragma unroll
         for (int a = 0; a < E; ++a)
@@ -750,16 +715,7 @@ static chol_status launch_adj_tile(int n, int64_t batch, const T *L, int64_t ldl
 {
     typedef TileShape<G, E> S;
     const int64_t blocks = (batch + S::MPB - 1) / S::MPB;
-    if constexpr (sizeof(T) == 4 && G == 4 && E % 4 == 0) {
-        if (n == S::NP && rows_aligned16(L, ldl, sL) && rows_aligned16(adjL, ldal, sAL) &&
-            rows_aligned16(adjA, ldaa, sAA)) {
-            hipLaunchKernelGGL((k_potrf_adj_tile<T, G, E, true>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
-                               n, batch, L, ldl, sL, adjL, ldal, sAL, adjA, ldaa, sAA, accumulate);
-            CHOL_LAUNCH_CHECK();
-            return CHOL_OK;
-        }
-    }
-    hipLaunchKernelGGL((k_potrf_adj_tile<T, G, E, false>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
+    hipLaunchKernelGGL((k_potrf_adj_tile<T, G, E>), dim3((unsigned)blocks), dim3(S::THREADS), 0, st,
                        n, batch, L, ldl, sL, adjL, ldal, sAL, adjA, ldaa, sAA, accumulate);
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;

@@ -189,12 +189,13 @@ typedef enum {
     CHOL_K_DIAG_INVERSE = 3,     /* blocked: inverse of diagonal tiles; flops: kb^3 / 3 per tile */
     CHOL_K_PANEL_SOLVE = 4,      /* blocked: L_ik = W_ik L_kk^-T; flops: m * kb^2 */
     CHOL_K_TRAILING_UPDATE = 5,  /* blocked: lower trailing update; flops: m (m + 1) kb */
-    CHOL_K_ADJ_TRAILING = 6,     /* adjoint: Wb_panel -= Sym(Wb22) L_panel; flops: 2 m^2 kb */
+    CHOL_K_ADJ_TRAILING = 6,     /* adjoint: split partials of Sym(Wb22) L_panel; flops: 2 m^2 kb */
     CHOL_K_ADJ_PANEL = 7,        /* adjoint: X = Wb_panel L_kk^-1; flops: m * kb^2 */
-    CHOL_K_ADJ_DIAG_UPDATE = 8,  /* adjoint: Wb_kk -= tril(X^T L_panel); flops: m * kb (kb + 1) */
+    CHOL_K_ADJ_DIAG_UPDATE = 8,  /* adjoint: split partials of X^T L_panel; flops: 2 m kb^2 */
     CHOL_K_ADJ_DIAG = 9,         /* adjoint of the factor on a diagonal tile; flops: 2 kb^3 / 3 */
     CHOL_K_ELEMENTWISE = 10,     /* triangle copies, zeroing, accumulation; bytes moved */
-    CHOL_K_COUNT = 11
+    CHOL_K_REDUCE = 11,          /* sums of split partial products into their target; bytes moved */
+    CHOL_K_COUNT = 12
 } chol_kernel_family;
 
 #define CHOL_PROFILE_ALL 0xffffffffu

@@ -332,7 +332,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
 //   [part_c: 2 * nb * nb]                   the tile adjoint's scratch tiles
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static const int TILE_SPLIT_MAX = 256;   // splits of tile-sized products with a long contraction
-static const int SIDE_SPLIT_MAX = 16;    // splits of the large symmetric product
+static const int SIDE_SPLIT_MAX = 32;    // splits of the large symmetric product
 
 size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
 {
@@ -372,13 +372,29 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
     p.a = S; p.lda = lds;
     p.b = B; p.ldb = ldb;
     p.c = C; p.ldc = ldc;
-    // about four (split, tile) items per block slot, taken dynamically by
-    // persistent blocks, so that blocks slowed by a neighbour take fewer
+    // (split, tile) items are taken by `cap` persistent blocks; pick the split
+    // count that minimises the estimated time: rounds of items x chunk length
+    // (a last round that is only partly full costs a whole chunk time) plus
+    // the partials each split writes and the reduction reads back, expressed
+    // in contraction elements (a 128 x 128 block advances 16 of them in about
+    // 5 us; the partial traffic moves at about 5 TB/s)
     const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t want = 4 * (int64_t)cap;
-    int splits = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (want + tiles - 1) / tiles));
-    splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, K / min_chunk));
-    p.kchunk = split_chunk(K, splits);
+    const double per_split = (double)M * N * 2.0 * sizeof(T) / 5e12 / (5e-6 / 16);
+    double best_t = -1;
+    int kchunk = K;
+    for (int sp = 1; sp <= max_splits; ++sp) {
+        const int c = split_chunk(K, sp);
+        if (sp > 1 && c < min_chunk)
+            break;
+        const int used = (K + c - 1) / c;
+        const int64_t items = tiles * used;
+        const double t = (double)((items + cap - 1) / cap) * c + per_split * used;
+        if (best_t < 0 || t < best_t) {
+            best_t = t;
+            kchunk = c;
+        }
+    }
+    p.kchunk = kchunk;
     const int used = (K + p.kchunk - 1) / p.kchunk;
     p.part = part;
     p.sched = sched;
@@ -415,6 +431,10 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
+    // this one-block kernel is on the critical path of the sweep and shares
+    // its CU with blocks of the trailing product: its waves win instruction
+    // arbitration on their SIMDs
+    __builtin_amdgcn_s_setprio(3);
     __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
     acc_t acc[4][4];
     auto zero = [&]() {
@@ -516,10 +536,10 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
 //   Sym(G(k)) L[tile k, tile j]:  needs the tile adjoint G(k) = the final Wb_kk.
 // The wide stream sx runs, per tile column k: the reduction that adds the
 // second term of tile column k (from tile column k+1's tile adjoint), the
-// panel-solve adjoint X(k) = Wb_panel(k) Linv_k, the tile-sized product
-// Wb_kk -= tril(X^T L_panel), and then -- while the one-block stream sc runs
-// the tile adjoint G(k), ending with the second term of tile column k-1 --
-// the first term of tile column k-1 as one symmetric product.
+// panel-solve adjoint X(k) = Wb_panel(k) Linv_k, and then the first term of
+// tile column k-1 as one symmetric product, while the chain stream sc runs
+// the tile-sized product Wb_kk -= tril(X^T L_panel) and the tile adjoint G(k),
+// ending with the second term of tile column k-1.
 template <typename T>
 static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
                                       int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t sc,
@@ -593,33 +613,34 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 if ((s = gemm<T, OP_MK, OP_KM_LOWER, C_STORE>(p, 1, sx)) != CHOL_OK)
                     return s;
             }
-            // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows
-            {
-                GemmArgs<T> p{};
-                p.M = kb; p.N = kb; p.K = (int)m;
-                p.a = Wp; p.lda = ldw;
-                p.b = Lp; p.ldb = ldl;
-                int64_t chunk;
-                const int splits = tile_splits(m, chunk);
-                p.kchunk = (int)chunk;
-                p.part = part_b;
-                {
-                    prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, sx, 2.0 * m * kb * kb);
-                    if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sx)) != CHOL_OK)
-                        return s;
-                }
-                const int64_t tot = (int64_t)kb * kb;
-                prof::Scope ps(CHOL_K_REDUCE, sx, (double)tot * (splits + 2) * sizeof(T));
-                hipLaunchKernelGGL((k_splitk_reduce_lower<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256),
-                                   0, sx, kb, splits, (const T *)part_b, Wkk, ldw);
-                CHOL_LAUNCH_CHECK();
-            }
         }
-        // tile adjoint of tile column k on sc; its last stage is the second
-        // term of tile column k-1
+        // from here on sc: R2b (it only feeds the tile adjoint), then the tile
+        // adjoint of tile column k, whose last stage is the second term of
+        // tile column k-1; meanwhile sx goes on with the symmetric product
         const int64_t j0 = k0 - nb;                 // previous tile column (if k >= 1)
         if (stream_join(sc, sx, e_wide) != hipSuccess)
             return CHOL_ERR_HIP;
+        if (m > 0) {
+            // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows
+            GemmArgs<T> p{};
+            p.M = kb; p.N = kb; p.K = (int)m;
+            p.a = Wp; p.lda = ldw;
+            p.b = Lp; p.ldb = ldl;
+            int64_t chunk;
+            const int splits = tile_splits(m, chunk);
+            p.kchunk = (int)chunk;
+            p.part = part_b;
+            {
+                prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, sc, 2.0 * m * kb * kb);
+                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sc)) != CHOL_OK)
+                    return s;
+            }
+            const int64_t tot = (int64_t)kb * kb;
+            prof::Scope ps(CHOL_K_REDUCE, sc, (double)tot * (splits + 2) * sizeof(T));
+            hipLaunchKernelGGL((k_splitk_reduce_lower<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256),
+                               0, sc, kb, splits, (const T *)part_b, Wkk, ldw);
+            CHOL_LAUNCH_CHECK();
+        }
         {
             prof::Scope ps(CHOL_K_ADJ_DIAG, sc, 2.0 * kb * kb * kb / 3 + (k >= 1 ? 2.0 * kb * kb * nb : 0.0));
             const T *Lnext = (k >= 1) ? L + k0 * ldl + j0 : nullptr;
@@ -633,7 +654,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         if (k >= 1 && m > 0) {
             const double flops = 2.0 * nb * ((double)(m + kb) * (m + kb) - (double)kb * kb);
             if ((s = sym_product<T>((int)(m + kb), nb, (int)(m + kb), Wkk, ldw, L + k0 * ldl + j0, ldl,
-                                    Wb + k0 * ldw + j0, ldw, kb, part_x, SIDE_SPLIT_MAX, 256, sched_x, cap_x,
+                                    Wb + k0 * ldw + j0, ldw, kb, part_x, SIDE_SPLIT_MAX, 128, sched_x, cap_x,
                                     flops, sx)) != CHOL_OK)
                 return s;
         }

@@ -581,6 +581,9 @@ __global__ void __launch_bounds__(256)
 k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base)
 {
     constexpr int G = 16, E = 8, NP = G * E;
+    // on the critical path of the factorisation, beside blocks of the trailing
+    // update: its waves win instruction arbitration on their SIMDs
+    __builtin_amdgcn_s_setprio(3);
     __shared__ T colbuf[2 * NP];
     __shared__ T rowbuf[2 * NP];
     const int tid = threadIdx.x, lr = tid / G, lc = tid % G;

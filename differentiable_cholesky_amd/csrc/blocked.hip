@@ -449,7 +449,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     {
         Operand<T, OP_KM_LOWER> A{L, ldl, 0, kb, 0};
         Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, 0};
-        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, false>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -469,7 +469,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     {
         Operand<T, OP_SYM> A{s1, lds_scr, 0, kb, 0};
         Operand<T, OP_KM_LOWER> B{inv, ldi, 0, kb, 0};
-        tile_mma<T, OP_SYM, OP_KM_LOWER, false, false>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_SYM, OP_KM_LOWER, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -489,7 +489,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     {
         Operand<T, OP_KM_LOWER> A{inv, ldi, 0, kb, 0};
         Operand<T, OP_KM> B{s2, lds_scr, 0, kb, 0};
-        tile_mma<T, OP_KM_LOWER, OP_KM, false, false>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_KM_LOWER, OP_KM, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -512,7 +512,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     {
         Operand<T, OP_SYM> A{Wb, ldw, 0, kb, 0};
         Operand<T, OP_KM> B{Lnext, ldl, 0, nj, 0};
-        tile_mma<T, OP_SYM, OP_KM, false, false>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_SYM, OP_KM, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)

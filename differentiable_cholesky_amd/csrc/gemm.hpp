@@ -26,6 +26,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -399,25 +400,29 @@ __device__ __forceinline__ void mma_general(typename Acc<T>::type (&acc)[4][4], 
 // BK * Pitch<T>::v elements).  Called by all 256 threads of the block.  When
 // every chunk can take the 16-byte path, the range is cut into runs of chunks
 // on which both operands keep one layout each (pipelined); otherwise the tile
-// takes the general loop.
-template <typename T, int AOP, int BOP, bool NEG, bool RUNS>
+// takes the general loop.  PATH fixes at compile time which of the two the
+// kernel carries (the host knows for plain operands and aligned sizes).
+enum { PATH_GENERAL = 0,   // every tile through the general loop
+       PATH_RUNS = 1,      // every chunk of every tile is on the 16-byte path
+       PATH_MIXED = 2 };   // decided per tile
+
+template <typename T, int AOP, int BOP, bool NEG, int PATH>
 __device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
                                          const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
-    // products whose operands are rarely on the 16-byte path, and those that
-    // start their accumulators from C (the extra registers of the pipelined
-    // runs would not fit beside them), always take the general loop
-    if constexpr (!RUNS) {
+    if constexpr (PATH == PATH_GENERAL) {
         mma_general<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, lds);
         return;
     }
-    // any chunk that needs the per-element path sends the whole tile down the
-    // general loop (kept apart so the fast runs stay lean in registers)
-    for (int k = kbeg; k < kend; k += BK) {
-        if (A.fast_lay(k, kend) < 0 || B.fast_lay(k, kend) < 0) {
-            mma_general<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, lds);
-            return;
+    if constexpr (PATH == PATH_MIXED) {
+        // any chunk that needs the per-element path sends the whole tile down
+        // the general loop (kept apart so the fast runs stay lean in registers)
+        for (int k = kbeg; k < kend; k += BK) {
+            if (A.fast_lay(k, kend) < 0 || B.fast_lay(k, kend) < 0) {
+                mma_general<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, lds);
+                return;
+            }
         }
     }
     int k = kbeg;
@@ -457,7 +462,7 @@ __device__ __forceinline__ void acc_pos(int i, int j, int v, int &row, int &col)
 }
 
 // One 128 x 128 output tile (I, J) over the contraction range [kbeg, kend).
-template <typename T, int AOP, int BOP, int CM>
+template <typename T, int AOP, int BOP, int CM, int PATH>
 __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, int split, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
@@ -489,8 +494,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
 
     Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
     Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec, 0};
-    constexpr bool PLAIN = (AOP == OP_MK || AOP == OP_KM || AOP == OP_SYM) && (BOP == OP_MK || BOP == OP_KM);
-    tile_mma<T, AOP, BOP, FROM_C, PLAIN && !FROM_C>(acc, A, B, kbeg, kend, lds);
+    tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, kbeg, kend, lds);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -530,7 +534,13 @@ __device__ __forceinline__ void tile_of(int t, int tri, int TJ, int &I, int &J)
     }
 }
 
-template <typename T, int AOP, int BOP, int CM>
+// SCHED: which tile schedules the kernel carries.  The lower trailing update
+// gets a dynamic-only kernel (dropping the static path avoids register
+// spills there); the other products measured as fast or faster with both
+// compiled in (the choice is then made at run time from p.sched).
+enum { SCHED_BOTH = 0, SCHED_DYN = 1, SCHED_STATIC = 2 };
+
+template <typename T, int AOP, int BOP, int CM, int PATH, int SCHED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm(GemmArgs<T> p)
 {
@@ -539,7 +549,7 @@ k_gemm(GemmArgs<T> p)
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
     const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
 
-    if (!p.sched) {
+    if (SCHED == SCHED_STATIC || (SCHED == SCHED_BOTH && !p.sched)) {
         // static: one tile per block, tiles spread over the XCDs in contiguous ranges
         int I, J;
         tile_of(gemm_detail::xcd_tile(blockIdx.x, nt), p.tri, TJ, I, J);
@@ -548,7 +558,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = blockIdx.y * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM>(p, I, J, blockIdx.y, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, PATH>(p, I, J, blockIdx.y, kbeg, kend, lds);
         return;
     }
 
@@ -572,7 +582,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = split * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM>(p, I, J, split, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, PATH>(p, I, J, split, kbeg, kend, lds);
     }
     // the last block to finish returns the counters to zero for the next launch
     if (threadIdx.x == 0) {
@@ -603,14 +613,41 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     p.splits = splits;
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
     const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
+    // which K-loop path the kernel carries: plain operands whose every chunk
+    // is on the 16-byte path take only the pipelined runs; the symmetric
+    // operand (whose chunks crossing the diagonal need the per-element path)
+    // and plain operands with ragged sizes decide per tile; the rest, and the
+    // products that seed their accumulators from C (short contractions, where
+    // the general loop's deeper A prefetch measured faster), take only the
+    // general loop
+    constexpr bool FROM_C = (CM == C_SUB || CM == C_SUB_LOWER);
+    constexpr bool PLAIN_A = (AOP == OP_MK || AOP == OP_KM) && !FROM_C;
+    constexpr bool PLAIN_B = BOP == OP_MK || BOP == OP_KM;
+    const bool all_fast = p.vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0 &&
+                          (CM != C_PARTIAL || p.kchunk % BK == 0);
+    const dim3 sgrid((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1));
+    unsigned dgrid = 0;
     if (p.sched) {
         // persistent blocks, all resident at once (two per CU the stream may use)
         const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1);
-        const unsigned grid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
-        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3(grid), dim3(NT), 0, st, p);
+        dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
+    }
+    auto launch = [&](auto path_c) {
+        constexpr int PATH = decltype(path_c)::value;
+        if (p.sched && CM == C_SUB_LOWER)
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, PATH, SCHED_DYN>), dim3(dgrid), dim3(NT), 0, st, p);
+        else if (p.sched)
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, PATH, SCHED_BOTH>), dim3(dgrid), dim3(NT), 0, st, p);
+        else
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, PATH, SCHED_BOTH>), sgrid, dim3(NT), 0, st, p);
+    };
+    if constexpr (PLAIN_A && PLAIN_B) {
+        (void)all_fast;
+        launch(std::integral_constant<int, PATH_MIXED>());
+    } else if constexpr (AOP == OP_SYM && PLAIN_B && !FROM_C) {
+        launch(std::integral_constant<int, PATH_MIXED>());
     } else {
-        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM>), dim3((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1)),
-                           dim3(NT), 0, st, p);
+        launch(std::integral_constant<int, PATH_GENERAL>());
     }
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;

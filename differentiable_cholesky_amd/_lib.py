@@ -28,10 +28,27 @@ class CholError(RuntimeError):
         self.status = status
 
 
+def _hip_runtimes() -> set[str]:
+    """Files of the HIP runtime mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:  # pragma: no cover - not Linux
+        return set()
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libchol.so not built at {LIB_PATH}; run `python -m differentiable_cholesky_amd.build`")
+        raise ImportError(f"libchol.so not built at {LIB_PATH}; run `python differentiable_cholesky_amd/build.py`")
+    # The tensors and streams handed to the library belong to torch's HIP
+    # runtime, so the library must run on that same runtime.  torch ships its
+    # own copy; loading torch first makes the dynamic loader bind libchol.so to
+    # it instead of mapping a second runtime that owns no device state.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError("libchol.so and torch are bound to different HIP runtimes: " + ", ".join(sorted(runtimes)))
     i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     st = ctypes.c_int
     lib.chol_potrf.restype = st
@@ -50,6 +67,10 @@ def _load() -> ctypes.CDLL:
     lib.chol_status_string.argtypes = [st]
     lib.chol_abi_version.restype = ctypes.c_int
     lib.chol_abi_version.argtypes = []
+    lib.chol_last_hip_error.restype = ctypes.c_int
+    lib.chol_last_hip_error.argtypes = []
+    lib.chol_last_hip_error_string.restype = ctypes.c_char_p
+    lib.chol_last_hip_error_string.argtypes = []
     lib.chol_profile_start.restype = st
     lib.chol_profile_start.argtypes = [ctypes.c_uint32]
     lib.chol_profile_stop.restype = st
@@ -73,7 +94,10 @@ def status_string(status: int) -> str:
 
 def _check(status: int):
     if status != CHOL_OK:
-        raise CholError(status, status_string(status))
+        msg = status_string(status)
+        if status == CHOL_ERR_HIP:
+            msg += f" (HIP error {lib.chol_last_hip_error()}: {lib.chol_last_hip_error_string().decode()})"
+        raise CholError(status, msg)
 
 
 # --------------------------------------------------------------- tensors ----
@@ -213,3 +237,11 @@ def chol_status_string(status: int) -> str:
 
 def chol_abi_version() -> int:
     return int(lib.chol_abi_version())
+
+
+def chol_last_hip_error() -> int:
+    return int(lib.chol_last_hip_error())
+
+
+def chol_last_hip_error_string() -> str:
+    return lib.chol_last_hip_error_string().decode()

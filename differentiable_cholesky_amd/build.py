@@ -1,6 +1,7 @@
 """Build libchol.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: ``python -m differentiable_cholesky_amd.build`` or ``build()``.
+Usage: ``python differentiable_cholesky_amd/build.py`` (runs without importing
+the package, so a stale or missing library does not get in the way).
 Objects are compiled in parallel, then linked into
 ``differentiable_cholesky_amd/libchol.so``.
 """

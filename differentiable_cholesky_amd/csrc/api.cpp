@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "../../include/libchol.h"
+#include "common.hpp"
 #include "profile.hpp"
 
 namespace chol {
@@ -71,6 +72,13 @@ bool nb_ok(int64_t nb) { return nb >= 0 && nb <= CHOL_MAX_NB; }
 
 } // namespace
 
+// The library checks each launch with hipGetLastError(), whose status is
+// sticky per host thread: a status left by unrelated HIP calls made earlier on
+// this thread (for example an event query that found work still pending) would
+// be taken for a failed launch.  Every entry point that launches clears it
+// first.
+static inline void clear_stale_status() { (void)hipGetLastError(); }
+
 extern "C" {
 
 int chol_abi_version(void) { return LIBCHOL_ABI_VERSION; }
@@ -85,6 +93,13 @@ const char *chol_status_string(chol_status s)
     case CHOL_ERR_HIP: return "CHOL_ERR_HIP: a HIP launch failed";
     }
     return "unknown chol_status";
+}
+
+int chol_last_hip_error(void) { return chol::g_last_hip_error.load(std::memory_order_relaxed); }
+
+const char *chol_last_hip_error_string(void)
+{
+    return hipGetErrorString((hipError_t)chol::g_last_hip_error.load(std::memory_order_relaxed));
 }
 
 chol_status chol_potrf(chol_dtype dt, int64_t n, const void *A, int64_t lda, void *L, int64_t ldl,
@@ -104,6 +119,7 @@ chol_status chol_potrf(chol_dtype dt, int64_t n, const void *A, int64_t lda, voi
     if (info && overlap(extent(info, 1, 1, 1, 0, 4), extent(L, n, ldl, 1, 0, es)))
         return CHOL_ERR_INVALID_VALUE;
     hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
     const int b = nb ? (int)nb : DEFAULT_NB;
     if (dt == CHOL_F64) {
         if (n <= CHOL_SMALL_MAX_N)
@@ -136,6 +152,7 @@ chol_status chol_potrf_batched(chol_dtype dt, int64_t n, int64_t batch, const vo
     if (info && overlap(extent(info, 1, 1, batch, 1, 4), extent(L, n, ldl, batch, strideL, es)))
         return CHOL_ERR_INVALID_VALUE;
     hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
     chol::prof::Scope ps(CHOL_K_SMALL_FACTOR, st, 2.0 * batch * ((double)n * (n + 1) / 2) * es);
     if (dt == CHOL_F64)
         return chol::small_potrf<double>((int)n, batch, (const double *)A, lda, strideA, (double *)L, ldl,
@@ -179,6 +196,7 @@ chol_status chol_potrf_adjoint(chol_dtype dt, int64_t n, const void *L, int64_t 
     if (overlap(extent(L, n, ldl, 1, 0, es), extent(adjA, n, ldaa, 1, 0, es)))
         return CHOL_ERR_INVALID_VALUE;
     hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
     if (n <= CHOL_SMALL_MAX_N) {
         if (dt == CHOL_F64)
             return chol::small_potrf_adjoint<double>((int)n, 1, (const double *)L, ldl, 0, (const double *)adjL,
@@ -226,6 +244,7 @@ chol_status chol_potrf_adjoint_batched(chol_dtype dt, int64_t n, int64_t batch, 
     if (overlap(extent(L, n, ldl, batch, strideL, es), extent(adjA, n, ldaa, batch, strideAA, es)))
         return CHOL_ERR_INVALID_VALUE;
     hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
     chol::prof::Scope ps(CHOL_K_SMALL_ADJOINT, st,
                          (accumulate ? 4.0 : 3.0) * batch * ((double)n * (n + 1) / 2) * es);
     if (dt == CHOL_F64)
@@ -244,6 +263,7 @@ chol_status chol_wave_dot_fwd_adj(chol_dtype dt, int64_t n, const void *a, const
     if (!y || !ybar || (n > 0 && (!a || !b || !abar || !bbar)))
         return CHOL_ERR_INVALID_VALUE;
     hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
     if (dt == CHOL_F64)
         return chol::wave_dot<double>((int)n, (const double *)a, (const double *)b, (double *)y,
                                       (const double *)ybar, (double *)abar, (double *)bbar, staging, st);

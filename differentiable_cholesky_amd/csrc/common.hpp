@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/libchol.h"
 
 namespace chol {
@@ -49,9 +51,22 @@ __device__ __forceinline__ f4_t mfma16x16x4(float a, float b, f4_t c)
 }
 
 // ------------------------------------------------------ launch checking ----
+// The HIP error behind the most recent CHOL_ERR_HIP (process-wide, for
+// diagnostics: chol_last_hip_error()).
+inline std::atomic<int> g_last_hip_error{0};
+
+// Records e if it is an error; true if it is.
+inline bool hip_failed(hipError_t e)
+{
+    if (e == hipSuccess)
+        return false;
+    g_last_hip_error.store((int)e, std::memory_order_relaxed);
+    return true;
+}
+
 #define CHOL_LAUNCH_CHECK()                                  \
     do {                                                     \
-        if (hipGetLastError() != hipSuccess)                 \
+        if (chol::hip_failed(hipGetLastError()))             \
             return CHOL_ERR_HIP;                             \
     } while (0)
 

@@ -1,5 +1,7 @@
 #include "side.hpp"
 
+#include "common.hpp"
+
 
 namespace chol {
 
@@ -12,28 +14,36 @@ std::once_flag g_once[MAX_DEVICES];
 Side *side_resources()
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+    if (hip_failed(hipGetDevice(&dev)))
         return nullptr;
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        hip_failed(hipErrorInvalidDevice);
+        return nullptr;
+    }
     Side &s = g_side[dev];
     std::call_once(g_once[dev], [&s, dev]() {
-        if (hipStreamCreateWithFlags(&s.chain, hipStreamNonBlocking) != hipSuccess)
+        if (hip_failed(hipStreamCreateWithFlags(&s.chain, hipStreamNonBlocking)))
             return;
         int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        if (hip_failed(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)))
             return;
-        if (hipStreamCreateWithFlags(&s.x, hipStreamNonBlocking) != hipSuccess)
+        if (cus <= 0) {
+            hip_failed(hipErrorInvalidDevice);
+            return;
+        }
+        if (hip_failed(hipStreamCreateWithFlags(&s.x, hipStreamNonBlocking)))
             return;
         // persistent grids of the wide stream leave RESERVED_CUS CUs' worth of
         // block slots free (restricting the stream with a CU mask instead was
         // measured slower: its launches cost more)
         s.wide_cus = cus > 4 * RESERVED_CUS ? cus - RESERVED_CUS : cus;
         for (auto &e : s.ev)
-            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+            if (hip_failed(hipEventCreateWithFlags(&e, hipEventDisableTiming)))
                 return;
         const size_t bytes = sizeof(int) * SCHED_SLOTS * SCHED_STRIDE;
-        if (hipMalloc((void **)&s.sched, bytes) != hipSuccess)
+        if (hip_failed(hipMalloc((void **)&s.sched, bytes)))
             return;
-        if (hipMemset(s.sched, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        if (hip_failed(hipMemset(s.sched, 0, bytes)) || hip_failed(hipDeviceSynchronize()))
             return;
         s.ok = true;
     });
@@ -43,9 +53,11 @@ Side *side_resources()
 hipError_t stream_join(hipStream_t waiter, hipStream_t src, hipEvent_t ev)
 {
     hipError_t e = hipEventRecord(ev, src);
-    if (e != hipSuccess)
+    if (hip_failed(e))
         return e;
-    return hipStreamWaitEvent(waiter, ev, 0);
+    e = hipStreamWaitEvent(waiter, ev, 0);
+    hip_failed(e);
+    return e;
 }
 
 } // namespace chol

@@ -208,6 +208,12 @@ const char *chol_status_string(chol_status status);
 /* LIBCHOL_ABI_VERSION of the loaded library. */
 int chol_abi_version(void);
 
+/* Diagnostics: the hipError_t code (0 if none so far) of the HIP call whose
+ * failure made the most recent call return CHOL_ERR_HIP, process-wide, and
+ * HIP's description of it (static string, never NULL). */
+int chol_last_hip_error(void);
+const char *chol_last_hip_error_string(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,3 +129,16 @@ def test_binding_rejects_cpu_tensors():
     A = torch.eye(4, dtype=torch.float64)
     with pytest.raises(ValueError):
         dc.chol_potrf(A, L=A.clone(), info=torch.zeros(1, dtype=torch.int32))
+
+
+def test_library_binds_to_torch_hip_runtime():
+    # importing the package with no earlier torch import must still leave one
+    # HIP runtime in the process: the one torch's tensors and streams live in
+    import subprocess
+    import sys
+    root = _lib.HERE.rsplit("/", 1)[0]
+    code = ("import sys; sys.path.insert(0, %r); import differentiable_cholesky_amd as d; "
+            "print(len(d._lib._hip_runtimes()))" % root)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

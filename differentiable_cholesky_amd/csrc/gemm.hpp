@@ -345,6 +345,62 @@ __device__ __forceinline__ void mma_run(typename Acc<T>::type (&acc)[4][4], cons
     }
 }
 
+// mma_run with A's loads two chunks ahead (A is the operand streamed from
+// HBM; B stays one chunk ahead).  The loop takes chunks in pairs so the two A
+// register sets alternate without copies; with an odd count the last pair
+// skips only its second chunk's matrix-core work, and every load stays
+// unconditional (indices past the run repeat its last chunk).
+template <typename T, int AOP, int BOP, int LA, int LB, bool NEG>
+__device__ __forceinline__ void mma_run2(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
+                                         const Operand<T, BOP> &B, int k0, int nc, T *lds)
+{
+    constexpr int SZ = BK * Pitch<T>::v;
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int wm = wave / 2, wn = wave % 2;
+    auto kc = [&](int c) { return k0 + (c < nc ? c : nc - 1) * BK; };
+    Vec8<T> a0, a1, b;
+    A.template fetch_fast<LA>(a0, tid, k0);
+    B.template fetch_fast<LB>(b, tid, k0);
+    __syncthreads();                      // earlier users of the LDS buffers are done
+    Operand<T, AOP>::template stash_lay<LA>(a0, lds, tid);
+    Operand<T, BOP>::template stash_lay<LB>(b, lds + SZ, tid);
+    A.template fetch_fast<LA>(a1, tid, kc(1));
+    B.template fetch_fast<LB>(b, tid, kc(1));
+    A.template fetch_fast<LA>(a0, tid, kc(2));
+    __syncthreads();
+    T *const L0 = lds, *const L1 = lds + 2 * SZ;
+    for (int c = 0; c < nc; c += 2) {
+        // chunk c from L0; chunk c+1 (a1, b) into L1; a1 <- chunk c+3
+        chunk_mma<T, NEG>(acc, L0, L0 + SZ, lane, wm, wn);
+        Operand<T, AOP>::template stash_lay<LA>(a1, L1, tid);
+        Operand<T, BOP>::template stash_lay<LB>(b, L1 + SZ, tid);
+        A.template fetch_fast<LA>(a1, tid, kc(c + 3));
+        B.template fetch_fast<LB>(b, tid, kc(c + 2));
+        __syncthreads();
+        // chunk c+1 from L1; chunk c+2 (a0, b) into L0; a0 <- chunk c+4
+        if (c + 1 < nc)
+            chunk_mma<T, NEG>(acc, L1, L1 + SZ, lane, wm, wn);
+        Operand<T, AOP>::template stash_lay<LA>(a0, L0, tid);
+        Operand<T, BOP>::template stash_lay<LB>(b, L0 + SZ, tid);
+        A.template fetch_fast<LA>(a0, tid, kc(c + 4));
+        B.template fetch_fast<LB>(b, tid, kc(c + 3));
+        __syncthreads();
+    }
+}
+
+#ifndef CHOL_RUN_DEPTH
+#define CHOL_RUN_DEPTH 2
+#endif
+template <typename T, int AOP, int BOP, int LA, int LB, bool NEG>
+__device__ __forceinline__ void run_chunks(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
+                                           const Operand<T, BOP> &B, int k0, int nc, T *lds)
+{
+    if constexpr (CHOL_RUN_DEPTH == 2)
+        mma_run2<T, AOP, BOP, LA, LB, NEG>(acc, A, B, k0, nc, lds);
+    else
+        mma_run<T, AOP, BOP, LA, LB, NEG>(acc, A, B, k0, nc, lds);
+}
+
 // The K loop through the general path, chunk by chunk, for tiles with edges,
 // diagonal crossings or masks: every chunk is fetched by the path it needs
 // (16-byte or per element).  A's loads run two chunks ahead, B's one.
@@ -395,6 +451,41 @@ __device__ __forceinline__ void mma_general(typename Acc<T>::type (&acc)[4][4], 
 
 } // namespace gemm_detail
 
+// Pipelined runs over [kbeg, kend) where every chunk is on the 16-byte path
+// (klim is the contraction bound the chunks are classified against): the range
+// is cut where an operand's staging layout changes.
+template <typename T, int AOP, int BOP, bool NEG>
+__device__ __forceinline__ void tile_runs(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
+                                          const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, int klim, T *lds)
+{
+    using namespace gemm_detail;
+    int k = kbeg;
+    while (k < kend) {
+        const int la = A.fast_lay(k, klim), lb = B.fast_lay(k, klim);
+        int nc = 1;
+        while (k + nc * BK < kend && A.fast_lay(k + nc * BK, klim) == la && B.fast_lay(k + nc * BK, klim) == lb)
+            ++nc;
+        // only the layout pairs the operand kinds can produce are instantiated
+        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_MK)) {
+            if (la == LAY_MK && lb == LAY_MK)
+                run_chunks<T, AOP, BOP, LAY_MK, LAY_MK, NEG>(acc, A, B, k, nc, lds);
+        }
+        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_KM)) {
+            if (la == LAY_MK && lb == LAY_KM)
+                run_chunks<T, AOP, BOP, LAY_MK, LAY_KM, NEG>(acc, A, B, k, nc, lds);
+        }
+        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_MK)) {
+            if (la == LAY_KM && lb == LAY_MK)
+                run_chunks<T, AOP, BOP, LAY_KM, LAY_MK, NEG>(acc, A, B, k, nc, lds);
+        }
+        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_KM)) {
+            if (la == LAY_KM && lb == LAY_KM)
+                run_chunks<T, AOP, BOP, LAY_KM, LAY_KM, NEG>(acc, A, B, k, nc, lds);
+        }
+        k += nc * BK;
+    }
+}
+
 // The K loop of one 128 x 128 tile: acc += (NEG ? -A : A) B over k in
 // [kbeg, kend), operands staged through `lds` (2 buffers x 2 operands x
 // BK * Pitch<T>::v elements).  Called by all 256 threads of the block.  When
@@ -416,40 +507,29 @@ __device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], con
         return;
     }
     if constexpr (PATH == PATH_MIXED) {
-        // any chunk that needs the per-element path sends the whole tile down
-        // the general loop (kept apart so the fast runs stay lean in registers)
+        // the chunks that need the per-element path (a diagonal crossing, an
+        // edge, a mask) span [g0, g1); they go through the general loop and
+        // the runs of 16-byte chunks before and after stay pipelined.  The
+        // three loops follow each other in straight-line code, which keeps
+        // the pipelined runs as lean in registers as in a kernel without the
+        // general loop.
+        int g0 = kend, g1 = kend;
         for (int k = kbeg; k < kend; k += BK) {
             if (A.fast_lay(k, kend) < 0 || B.fast_lay(k, kend) < 0) {
-                mma_general<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, lds);
-                return;
+                if (g0 == kend)
+                    g0 = k;
+                g1 = min(k + BK, kend);
             }
         }
+        if (g0 > kbeg)
+            tile_runs<T, AOP, BOP, NEG>(acc, A, B, kbeg, g0, kend, lds);
+        if (g1 > g0)
+            mma_general<T, AOP, BOP, NEG>(acc, A, B, g0, g1, lds);
+        if (kend > g1)
+            tile_runs<T, AOP, BOP, NEG>(acc, A, B, g1, kend, kend, lds);
+        return;
     }
-    int k = kbeg;
-    while (k < kend) {
-        const int la = A.fast_lay(k, kend), lb = B.fast_lay(k, kend);
-        int nc = 1;
-        while (k + nc * BK < kend && A.fast_lay(k + nc * BK, kend) == la && B.fast_lay(k + nc * BK, kend) == lb)
-            ++nc;
-        // only the layout pairs the operand kinds can produce are instantiated
-        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_MK)) {
-            if (la == LAY_MK && lb == LAY_MK)
-                mma_run<T, AOP, BOP, LAY_MK, LAY_MK, NEG>(acc, A, B, k, nc, lds);
-        }
-        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_KM)) {
-            if (la == LAY_MK && lb == LAY_KM)
-                mma_run<T, AOP, BOP, LAY_MK, LAY_KM, NEG>(acc, A, B, k, nc, lds);
-        }
-        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_MK)) {
-            if (la == LAY_KM && lb == LAY_MK)
-                mma_run<T, AOP, BOP, LAY_KM, LAY_MK, NEG>(acc, A, B, k, nc, lds);
-        }
-        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_KM)) {
-            if (la == LAY_KM && lb == LAY_KM)
-                mma_run<T, AOP, BOP, LAY_KM, LAY_KM, NEG>(acc, A, B, k, nc, lds);
-        }
-        k += nc * BK;
-    }
+    tile_runs<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, kend, lds);
 }
 
 // Position of accumulator element (i, j, v) of this thread inside the 128 x 128 tile.
@@ -613,15 +693,12 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     p.splits = splits;
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
     const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
-    // which K-loop path the kernel carries: plain operands whose every chunk
-    // is on the 16-byte path take only the pipelined runs; the symmetric
-    // operand (whose chunks crossing the diagonal need the per-element path)
-    // and plain operands with ragged sizes decide per tile; the rest, and the
-    // products that seed their accumulators from C (short contractions, where
-    // the general loop's deeper A prefetch measured faster), take only the
+    // which K-loop path the kernel carries: products of plain operands and
+    // of the symmetric operand decide per tile which chunks take the
+    // pipelined runs (all of them unless the tile has edges, diagonal
+    // crossings or masks); the masked triangular operands take only the
     // general loop
-    constexpr bool FROM_C = (CM == C_SUB || CM == C_SUB_LOWER);
-    constexpr bool PLAIN_A = (AOP == OP_MK || AOP == OP_KM) && !FROM_C;
+    constexpr bool PLAIN_A = AOP == OP_MK || AOP == OP_KM;
     constexpr bool PLAIN_B = BOP == OP_MK || BOP == OP_KM;
     const bool all_fast = p.vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0 &&
                           (CM != C_PARTIAL || p.kchunk % BK == 0);
@@ -644,7 +721,7 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     if constexpr (PLAIN_A && PLAIN_B) {
         (void)all_fast;
         launch(std::integral_constant<int, PATH_MIXED>());
-    } else if constexpr (AOP == OP_SYM && PLAIN_B && !FROM_C) {
+    } else if constexpr (AOP == OP_SYM && PLAIN_B) {
         launch(std::integral_constant<int, PATH_MIXED>());
     } else {
         launch(std::integral_constant<int, PATH_GENERAL>());

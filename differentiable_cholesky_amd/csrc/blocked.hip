@@ -209,13 +209,27 @@ static inline int split_chunk(int64_t K, int splits)
 }
 
 // ------------------------------------------------------------- forward ----
-// Two library streams: `sx` runs every kernel that spans the matrix -- panel
-// solve, update of the next tile column, update of the rest -- in order; `sc`
-// runs only the one-block kernels of the next tile column (diagonal factor and
-// its inverse); the update of the rest runs as persistent blocks that leave a
-// few block slots free, so those kernels start at once beside it:
-//   sx: [wait diag(k)] solve(k) -> next(k) -> {record} -> rest(k) -> ...
-//   sc: [wait next(k)] diag(k+1) + inverse(k+1) -> {record diag(k+1)}
+// Two library streams: `sx` runs every kernel that spans the matrix (panel
+// solves and trailing updates) in order; `sc` runs only the one-block kernels
+// of the next tile column (diagonal factor and its inverse), beside the wide
+// update that follows it on sx.
+//
+// The trailing update is deferred so that most of it contracts over two
+// panels at once (a 256-deep product reads and writes the trailing triangle
+// half as often as two 128-deep ones).  Panel j is L[rows below tile j, tile
+// column j]; panels j-1 and j sit side by side in L, so the pair is one
+// two-tile-wide operand.  At step k (tile column k factored on sc, its panel
+// solved on sx):
+//   next(k):  tile column k+1 receives every panel it still lacks: k alone at
+//             odd k; k-1 and k at even k > 0 (panel 0 alone at k = 0);
+//             at even k the same launch also updates tile column k+2,
+//             which needs the same panels;
+//   then sc factors tile column k+1 while sx continues with
+//     even k: the first half of the tiles of the triangle right of tile
+//             column k+2, with the same panels as next(k);
+//     odd k:  the second half of that triangle (panels k-2, k-1).
+// Every tile column thus has all earlier panels applied before it is factored,
+// and the two streams never touch the same tiles at the same time.
 template <typename T>
 static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info,
                                     int nb, hipStream_t sc, hipStream_t sx, hipEvent_t e_diag, hipEvent_t e_next,
@@ -232,15 +246,54 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         const int64_t k0 = k * nb;
         const int kb = (int)std::min<int64_t>(nb, n - k0);
         const double kb3 = (double)kb * kb * kb;
-        chol_status r;
-        // the factor of the tile and, if a panel follows, its inverse (written
-        // transposed into the tile's strict upper triangle for the panel solve)
         const bool inv = k0 + kb < n;
         prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, inv ? 2 * kb3 / 3 : kb3 / 3);
         return diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, k == 0 ? 1 : 2, k0, inv, sc);
     };
+    // lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T with Q = panels f .. f+np-1
+    // (tile columns f .. f+np-1 of L); tri: the whole trailing triangle W[c:, c:]
+    // instead, restricted to the 128 x 128 tiles t0 .. t0+tn-1 (row-major over
+    // the lower tiles), taken by persistent blocks
+    auto lower_update = [&](int64_t c, int64_t w, int64_t f, int np, bool tri, int t0, int tn) -> chol_status {
+        const int64_t M = n - c;
+        const int Kd = np * nb;
+        GemmArgs<T> p{};
+        p.M = (int)M; p.N = (int)(tri ? M : w); p.K = Kd;
+        p.a = L + c * ldl + f * nb; p.lda = ldl;
+        p.b = L + c * ldl + f * nb; p.ldb = ldl;
+        p.c = L + c * ldl + c; p.ldc = ldl;
+        double flops;
+        if (tri) {
+            p.tri = 1;
+            p.t0 = t0;
+            p.tn = tn;
+            p.sched = sched_x;
+            p.cap = cap_x;
+            // tiles of the window: full ones 2*128*128*Kd flops, diagonal ones
+            // the lower half (rows of the last tile row may be short)
+            flops = 0;
+            int64_t r = 0, t = 0;
+            while (t + r + 1 <= t0) { t += r + 1; ++r; }
+            for (int64_t q = t0, cc = t0 - t; q < (int64_t)t0 + tn; ++q) {
+                const double hr = (double)std::min<int64_t>(128, M - r * 128);
+                flops += (cc == r) ? hr * (hr + 1) * Kd : 2.0 * hr * 128 * Kd;
+                if (++cc > r) { cc = 0; ++r; }
+            }
+        } else {
+            flops = (double)w * (w + 1) * Kd + 2.0 * (M - w) * w * Kd;
+        }
+        prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, flops);
+        return gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx);
+    };
+    auto tri_tiles = [&](int64_t c) -> int {
+        const int64_t TI = (n - c + 127) / 128;
+        return (int)(TI * (TI + 1) / 2);
+    };
     if ((s = diag_step(0)) != CHOL_OK)
         return s;
+    // second half of a triangle update left for the next step
+    int64_t pend_c = -1, pend_f = 0;
+    int pend_np = 0, pend_t0 = 0, pend_tn = 0;
     for (int64_t k = 0; k < K; ++k) {
         const int64_t k0 = k * nb;
         const int kb = (int)std::min<int64_t>(nb, n - k0);
@@ -261,41 +314,39 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             if ((s = gemm<T, OP_MK, OP_KM_INVT, C_STORE>(p, 1, sx)) != CHOL_OK)
                 return s;
         }
-        const T *P = L + r0 * ldl + k0;          // solved panel, m x kb
-        const int kn = (int)std::min<int64_t>(nb, m);
-        const int64_t m2 = m - kn;
-        // next tile column: W[r0:, r0:r0+kn] (lower part) -= P P[0:kn]^T
-        {
-            GemmArgs<T> p{};
-            p.M = (int)m; p.N = kn; p.K = kb;
-            p.a = P; p.lda = ldl;
-            p.b = P; p.ldb = ldl;
-            p.c = L + r0 * ldl + r0; p.ldc = ldl;
-            prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, (double)kn * (kn + 1) * kb + 2.0 * m2 * kn * kb);
-            if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx)) != CHOL_OK)
-                return s;
-        }
+        const bool even = (k % 2) == 0;
+        const int np = (even && k > 0) ? 2 : 1;
+        const int64_t f = k + 1 - np;
+        // at even k the next two tile columns take the same panels: one launch
+        // covers both (its tile above the diagonal is left alone by the
+        // lower-only store), in the time of one, as its blocks fit on the chip
+        const int64_t kn = std::min<int64_t>(even ? 2 * (int64_t)nb : nb, m);
+        if ((s = lower_update(r0, kn, f, np, false, 0, 0)) != CHOL_OK)
+            return s;
         // the next tile column's one-block kernels start on sc ...
         if (stream_join(sc, sx, e_next) != hipSuccess)
             return CHOL_ERR_HIP;
         if ((s = diag_step(k + 1)) != CHOL_OK)
             return s;
-        // ... while sx updates the rest: lower part of W[r0+kn:, r0+kn:] -= P2 P2^T
-        if (m2 > 0) {
-            const T *P2 = P + (int64_t)kn * ldl;
-            GemmArgs<T> p{};
-            p.M = (int)m2; p.N = (int)m2; p.K = kb;
-            p.a = P2; p.lda = ldl;
-            p.b = P2; p.ldb = ldl;
-            p.c = L + (r0 + kn) * ldl + r0 + kn; p.ldc = ldl;
-            p.tri = 1;
-            p.sched = sched_x;
-            p.cap = cap_x;
-            prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, (double)m2 * (m2 + 1) * kb);
-            if ((s = gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx)) != CHOL_OK)
+        // ... while sx updates further right
+        if (even) {
+            const int64_t c3 = r0 + 2 * (int64_t)nb;
+            if (c3 < n) {
+                const int tiles = tri_tiles(c3), h = (tiles + 1) / 2;
+                if ((s = lower_update(c3, 0, f, np, true, 0, h)) != CHOL_OK)
+                    return s;
+                if (tiles > h) {
+                    pend_c = c3; pend_f = f; pend_np = np; pend_t0 = h; pend_tn = tiles - h;
+                }
+            }
+        } else if (pend_c >= 0) {
+            if ((s = lower_update(pend_c, 0, pend_f, pend_np, true, pend_t0, pend_tn)) != CHOL_OK)
                 return s;
+            pend_c = -1;
         }
     }
+    if (pend_c >= 0 && (s = lower_update(pend_c, 0, pend_f, pend_np, true, pend_t0, pend_tn)) != CHOL_OK)
+        return s;
     if (stream_join(sc, sx, e_next) != hipSuccess)
         return CHOL_ERR_HIP;
     return tri_op<T, TRI_ZERO_UPPER>(n, nullptr, 0, L, ldl, sc);

@@ -50,6 +50,8 @@ template <typename T> struct GemmArgs {
     int splits;          // split count (C_PARTIAL)
     int excl;            // OP_SYM A operand: entries (m, k) with m < excl and
                          // k < excl read as zero (a block left out of the product)
+    int t0, tn;          // tile window: tiles t0 .. t0 + tn - 1 of the (row-major
+                         // or lower-triangular) tile grid; tn == 0: every tile
     int cap;             // persistent grid size with `sched` (0: two blocks per CU of 240)
     int *sched;          // non-null: blocks take (split, tile) items from this
                          // device counter pair (item, finished blocks), which
@@ -627,12 +629,12 @@ k_gemm(GemmArgs<T> p)
     using namespace gemm_detail;
     __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
-    const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
+    const int nt = p.tn ? p.tn : (p.tri ? TI * (TI + 1) / 2 : TI * TJ);
 
     if (SCHED == SCHED_STATIC || (SCHED == SCHED_BOTH && !p.sched)) {
         // static: one tile per block, tiles spread over the XCDs in contiguous ranges
         int I, J;
-        tile_of(gemm_detail::xcd_tile(blockIdx.x, nt), p.tri, TJ, I, J);
+        tile_of(p.t0 + gemm_detail::xcd_tile(blockIdx.x, nt), p.tri, TJ, I, J);
         int kbeg = 0, kend = p.K;
         if (CM == C_PARTIAL) {
             kbeg = blockIdx.y * p.kchunk;
@@ -656,7 +658,7 @@ k_gemm(GemmArgs<T> p)
             break;
         const int split = it / nt;
         int I, J;
-        tile_of(it % nt, p.tri, TJ, I, J);
+        tile_of(p.t0 + it % nt, p.tri, TJ, I, J);
         int kbeg = 0, kend = p.K;
         if (CM == C_PARTIAL) {
             kbeg = split * p.kchunk;
@@ -692,7 +694,12 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     p.vec = aligned16(p.a, p.lda) && aligned16(p.b, p.ldb);
     p.splits = splits;
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
-    const int nt = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
+    const int nt_all = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
+    if (p.t0 < 0 || p.tn < 0 || p.t0 + (p.tn ? p.tn : nt_all) > nt_all)
+        return CHOL_ERR_INVALID_VALUE;
+    const int nt = p.tn ? p.tn : nt_all;
+    if (nt == 0)
+        return CHOL_OK;
     // which K-loop path the kernel carries: products of plain operands and
     // of the symmetric operand decide per tile which chunks take the
     // pipelined runs (all of them unless the tile has edges, diagonal

@@ -86,7 +86,9 @@ static chol_status tri_op(int64_t n, const T *src, int64_t lds, T *dst, int64_t 
 //   out_mode 0: strict lower of X written transposed into the tile's strict
 //               upper triangle in W (the factor's upper triangle is free
 //               scratch until it is zeroed at the end).
-//   out_mode 1: X (lower) written to ws + t*ws_stride with leading dim ws_ld.
+//   out_mode 1: X written to ws + t*ws_stride with leading dim ws_ld, the
+//               zeros above its diagonal included (the kb x kb block), so
+//               that products can read it as a plain operand.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_trinv(int64_t n_total, int nb, int64_t tile0, int64_t step, T *W, int64_t ld, int out_mode, T *ws,
@@ -153,19 +155,25 @@ k_trinv(int64_t n_total, int nb, int64_t tile0, int64_t step, T *W, int64_t ld, 
         }
     }
 
+    if (out_mode == 0) {
+#pragma unroll
+        for (int a = 0; a < E; ++a)
+#pragma unroll
+            for (int b = 0; b < a + 1; ++b) {
+                const int i = lr + G * a, j = lc + G * b;
+                if (i < kb && j < i)
+                    W[(k0 + j) * ld + k0 + i] = x[a][b];
+            }
+        return;
+    }
+    T *X = ws + (int64_t)blockIdx.x * ws_stride;
 #pragma unroll
     for (int a = 0; a < E; ++a)
 #pragma unroll
-        for (int b = 0; b <= a; ++b) {
+        for (int b = 0; b < E; ++b) {
             const int i = lr + G * a, j = lc + G * b;
-            if (i >= kb || j > i)
-                continue;
-            if (out_mode == 0) {
-                if (i > j)
-                    W[(k0 + j) * ld + k0 + i] = x[a][b];
-            } else {
-                ws[(int64_t)blockIdx.x * ws_stride + (int64_t)i * ws_ld + j] = x[a][b];
-            }
+            if (i < kb && j < kb)
+                X[(int64_t)i * ws_ld + j] = (b <= a && j <= i) ? x[a][b] : T(0);
         }
 }
 
@@ -466,17 +474,31 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
 }
 
 // Adjoint of chol on one kb x kb diagonal tile (kb <= 128), in place on the
-// lower triangle of Wb, from the tile's factor L and its inverse Linv:
-//   P = Phi(L^T tril(Wb))     lower triangle, into scratch s1
-//   V = Sym(P) Linv           Sym(P) = P + P^T = Psi (diagonal M_ii); into s2
-//   G = Phi(Linv^T V)         lower triangle, into Wb
+// lower triangle of Wb, from the tile's factor L and its inverse Linv (stored
+// with its zeros, kb x kb, leading dimension ldi):
+//   M = L^T tril(Wb)          Psi = Phi(M) + Phi(M)^T (lower part of M mirrored,
+//                             diagonal M_ii), written whole into scratch s1
+//   V = Psi Linv              into s2
+//   Z = Linv^T V              G = Phi(Z) into Wb (lower); Z is symmetric, and
+//                             Sym(G) = G + G^T (lower part of Z mirrored) goes
+//                             whole into s1
 // and, when `slot` is given, the one term of the previous tile column's
 // trailing-update adjoint that needs G:  slot = Sym(G) Lnext  (kb x nj, row
 // major), with Lnext = L[this tile's rows, previous tile column].
 // Each stage is one 128 x 128 x 128 matrix-core product of the whole block;
 // between stages the block's global writes are made visible by the barrier.
+// Only the first stage reads masked triangles (of the caller's L and Wb); the
+// others read plain whole operands and take the pipelined K loop.
 template <typename T>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__device__ __forceinline__ int vec_ok(const T *p, int64_t ld)
+{
+    return ((uintptr_t)p % 16 == 0) && (ld % (16 / (int64_t)sizeof(T)) == 0);
+}
+
+// At most 256 registers per wave: the kernel has to fit on a CU beside a
+// block of the persistent trailing product (which holds the other half).
+template <typename T>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv, int64_t ldi, T *s1, T *s2,
                int64_t lds_scr, const T *Lnext, int nj, T *slot)
 {
@@ -495,6 +517,24 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = acc_t{0, 0, 0, 0};
     };
+    // the lower part of the accumulated (symmetric) block mirrored whole into s1
+    auto mirror_to_s1 = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    int r, c;
+                    acc_pos<T>(i, j, v, r, c);
+                    if (r < kb && c <= r) {
+                        s1[(int64_t)r * lds_scr + c] = acc[i][j][v];
+                        s1[(int64_t)c * lds_scr + r] = acc[i][j][v];
+                    }
+                }
+    };
+    const int vs = vec_ok(s1, lds_scr) && vec_ok(s2, lds_scr);
+    const int vi = vec_ok(inv, ldi);
     // stage 1: M = L^T tril(Wb); A(r, t) = L[t][r] (t >= r), B(t, c) = Wb[t][c] (t >= c)
     zero();
     {
@@ -502,25 +542,15 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
         Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, 0};
         tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                int r, c;
-                acc_pos<T>(i, j, v, r, c);
-                if (r < kb && c <= r)
-                    s1[(int64_t)r * lds_scr + c] = (r == c) ? T(0.5) * acc[i][j][v] : acc[i][j][v];
-            }
+    mirror_to_s1();
     __threadfence_block();
     __syncthreads();
-    // stage 2: V = Sym(P) Linv; B(t, c) = Linv[t][c] (t >= c)
+    // stage 2: V = Psi Linv; A(r, t) = Psi[r][t], B(t, c) = Linv[t][c]
     zero();
     {
-        Operand<T, OP_SYM> A{s1, lds_scr, 0, kb, 0};
-        Operand<T, OP_KM_LOWER> B{inv, ldi, 0, kb, 0};
-        tile_mma<T, OP_SYM, OP_KM_LOWER, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_MK> A{s1, lds_scr, 0, kb, vs};
+        Operand<T, OP_KM> B{inv, ldi, 0, kb, vs && vi};
+        tile_mma<T, OP_MK, OP_KM, false, PATH_MIXED>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -535,12 +565,12 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
             }
     __threadfence_block();
     __syncthreads();
-    // stage 3: Z = Linv^T V; A(r, t) = Linv[t][r] (t >= r), B(t, c) = V[t][c]
+    // stage 3: Z = Linv^T V; A(r, t) = Linv[t][r], B(t, c) = V[t][c]
     zero();
     {
-        Operand<T, OP_KM_LOWER> A{inv, ldi, 0, kb, 0};
-        Operand<T, OP_KM> B{s2, lds_scr, 0, kb, 0};
-        tile_mma<T, OP_KM_LOWER, OP_KM, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_KM> A{inv, ldi, 0, kb, vs && vi};
+        Operand<T, OP_KM> B{s2, lds_scr, 0, kb, vs && vi};
+        tile_mma<T, OP_KM, OP_KM, false, PATH_MIXED>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -555,15 +585,15 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
             }
     if (!slot)
         return;
+    mirror_to_s1();
     __threadfence_block();
     __syncthreads();
-    // stage 4: slot = Sym(G) Lnext; A = Sym of the lower triangle just written,
-    // B(t, c) = Lnext[t][c]
+    // stage 4: slot = Sym(G) Lnext; A(r, t) = Sym(G)[r][t], B(t, c) = Lnext[t][c]
     zero();
     {
-        Operand<T, OP_SYM> A{Wb, ldw, 0, kb, 0};
-        Operand<T, OP_KM> B{Lnext, ldl, 0, nj, 0};
-        tile_mma<T, OP_SYM, OP_KM, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_MK> A{s1, lds_scr, 0, kb, vs};
+        Operand<T, OP_KM> B{Lnext, ldl, 0, nj, vs && vec_ok(Lnext, ldl)};
+        tile_mma<T, OP_MK, OP_KM, false, PATH_MIXED>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -653,7 +683,8 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                                    kn, kb, 1, (const T *)slot, Wp, ldw);
                 CHOL_LAUNCH_CHECK();
             }
-            // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block)
+            // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block;
+            // the stored inverse carries its zeros, so it is a plain operand)
             {
                 GemmArgs<T> p{};
                 p.M = (int)m; p.N = kb; p.K = kb;
@@ -661,7 +692,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 p.b = invk; p.ldb = nb;
                 p.c = Wp; p.ldc = ldw;
                 prof::Scope ps(CHOL_K_ADJ_PANEL, sx, (double)m * kb * kb);
-                if ((s = gemm<T, OP_MK, OP_KM_LOWER, C_STORE>(p, 1, sx)) != CHOL_OK)
+                if ((s = gemm<T, OP_MK, OP_KM, C_STORE>(p, 1, sx)) != CHOL_OK)
                     return s;
             }
         }

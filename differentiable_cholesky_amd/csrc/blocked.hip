@@ -32,8 +32,11 @@
 namespace chol {
 
 template <typename T>
-chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, bool inverse,
-                       hipStream_t st);
+chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, T *inv,
+                       int64_t ldinv, hipStream_t st);
+
+// edge of a diagonal-tile inverse slot in the library's side buffer
+static constexpr int MAX_TILE = CHOL_MAX_NB;
 
 // ------------------------------------------------------------ elementwise ----
 enum { TRI_COPY_LOWER = 0, TRI_ZERO_UPPER = 1, TRI_ADD_LOWER = 2 };
@@ -241,7 +244,7 @@ static inline int split_chunk(int64_t K, int splits)
 template <typename T>
 static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info,
                                     int nb, hipStream_t sc, hipStream_t sx, hipEvent_t e_diag, hipEvent_t e_next,
-                                    int *sched_x, int cap_x)
+                                    int *sched_x, int cap_x, T *inv2)
 {
     chol_status s;
     if (A != L) {
@@ -249,14 +252,18 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             return s;
     }
     const int64_t K = (n + nb - 1) / nb;
-    // diagonal factor (and inverse, if a panel follows) of tile column k, on sc
+    // diagonal factor (and, if a panel follows, its inverse into slot k % 2 of
+    // inv2: the panel solve of tile column k reads it while tile column k+1 is
+    // factored into the other slot) of tile column k, on sc
+    auto inv_slot = [&](int64_t k) { return inv2 + (k & 1) * (int64_t)MAX_TILE * MAX_TILE; };
     auto diag_step = [&](int64_t k) -> chol_status {
         const int64_t k0 = k * nb;
         const int kb = (int)std::min<int64_t>(nb, n - k0);
         const double kb3 = (double)kb * kb * kb;
         const bool inv = k0 + kb < n;
         prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, inv ? 2 * kb3 / 3 : kb3 / 3);
-        return diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, k == 0 ? 1 : 2, k0, inv, sc);
+        return diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, k == 0 ? 1 : 2, k0, inv ? inv_slot(k) : nullptr,
+                             MAX_TILE, sc);
     };
     // lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T with Q = panels f .. f+np-1
     // (tile columns f .. f+np-1 of L); tri: the whole trailing triangle W[c:, c:]
@@ -308,18 +315,18 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         const int64_t r0 = k0 + kb, m = n - r0;
         if (m == 0)
             break;
-        T *Wkk = L + k0 * ldl + k0;
         if (stream_join(sx, sc, e_diag) != hipSuccess)
             return CHOL_ERR_HIP;
-        // panel: L_ik = W_ik * Linv^T  (in place; one block spans the full panel width)
+        // panel: L_ik = W_ik * Linv^T  (in place; one block spans the full panel
+        // width; Linv is read whole from its slot, element (j, t) = Linv[j][t])
         {
             GemmArgs<T> p{};
             p.M = (int)m; p.N = kb; p.K = kb;
             p.a = L + r0 * ldl + k0; p.lda = ldl;
-            p.b = Wkk; p.ldb = ldl;
+            p.b = inv_slot(k); p.ldb = MAX_TILE;
             p.c = L + r0 * ldl + k0; p.ldc = ldl;
             prof::Scope ps(CHOL_K_PANEL_SOLVE, sx, (double)m * kb * kb);
-            if ((s = gemm<T, OP_MK, OP_KM_INVT, C_STORE>(p, 1, sx)) != CHOL_OK)
+            if ((s = gemm<T, OP_MK, OP_MK, C_STORE>(p, 1, sx)) != CHOL_OK)
                 return s;
         }
         const bool even = (k % 2) == 0;
@@ -373,7 +380,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
     if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
         return CHOL_ERR_HIP;
     const chol_status s = blocked_potrf_on<T>(n, A, lda, L, ldl, info, nb, sd->chain, sd->x, sd->ev[0], sd->ev[1],
-                                              sd->sched, 2 * sd->wide_cus);
+                                              sd->sched, 2 * sd->wide_cus, (T *)sd->fwd_inv);
     const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
                         stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
     if (s != CHOL_OK)

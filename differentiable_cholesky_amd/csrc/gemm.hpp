@@ -11,9 +11,6 @@
 //            (the adjoint of a lower-triangle-only trailing update reads the
 //            gradient this way)
 //   OP_KM_LOWER  OP_KM with entries k < m replaced by 0
-//   OP_KM_INVT   element (m, k) = X(m, k) of X = Linv where the tile p holds
-//            L's diagonal and Linv^T in its strict upper triangle:
-//            p[k][m] for k < m, 1 / p[m][m] for k == m, 0 for k > m
 //
 // Design for gfx950: a 256-thread block computes a 128 x 128 tile as 2 x 2
 // wavefronts of 64 x 64, each a 4 x 4 grid of 16x16x4 MFMA steps.  K advances
@@ -32,7 +29,7 @@
 
 namespace chol {
 
-enum { OP_MK = 0, OP_KM = 1, OP_SYM = 2, OP_KM_LOWER = 3, OP_KM_INVT = 4 };
+enum { OP_MK = 0, OP_KM = 1, OP_SYM = 2, OP_KM_LOWER = 3 };
 enum { C_SUB = 0,        // C -= AB
        C_SUB_LOWER = 1,  // C -= AB where row >= col
        C_STORE = 2,      // C  = AB
@@ -82,13 +79,6 @@ __device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim
         return p[(int64_t)k * ld + m];
     if (OP == OP_KM_LOWER)
         return k >= m ? p[(int64_t)k * ld + m] : T(0);
-    if (OP == OP_KM_INVT) {
-        if (k < m)
-            return p[(int64_t)k * ld + m];
-        if (k == m)
-            return T(1) / p[(int64_t)m * ld + m];
-        return T(0);
-    }
     // OP_SYM
     if (m > k)
         return p[(int64_t)m * ld + k];
@@ -159,8 +149,6 @@ struct Operand {
             return !(m0 >= k0 + BK || m0 + BM <= k0) || (m0 < excl && k0 < excl);
         if (OP == OP_KM_LOWER)
             return !(k0 >= m0 + BM - 1);         // plain only if every k >= every m
-        if (OP == OP_KM_INVT)
-            return !(k0 + BK - 1 < m0);          // plain only if every k < every m
         return false;
     }
 

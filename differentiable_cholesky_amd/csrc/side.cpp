@@ -43,6 +43,8 @@ Side *side_resources()
         const size_t bytes = sizeof(int) * SCHED_SLOTS * SCHED_STRIDE;
         if (hip_failed(hipMalloc((void **)&s.sched, bytes)))
             return;
+        if (hip_failed(hipMalloc(&s.fwd_inv, 2 * CHOL_MAX_NB * CHOL_MAX_NB * sizeof(double))))
+            return;
         if (hip_failed(hipMemset(s.sched, 0, bytes)) || hip_failed(hipDeviceSynchronize()))
             return;
         s.ok = true;

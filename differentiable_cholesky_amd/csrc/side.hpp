@@ -24,6 +24,8 @@ struct Side {
     hipEvent_t ev[6] = {};
     int *sched = nullptr;          // device counters of dynamically scheduled products
                                    // (SCHED_SLOTS slots of 2 ints, 64 bytes apart)
+    void *fwd_inv = nullptr;       // two CHOL_MAX_NB-edge fp64 tiles: inverses of the factor's
+                                   // diagonal tiles, alternating between tile columns
     int wide_cus = 0;              // CUs' worth of block slots the persistent grids use
     std::mutex mu;                 // one blocked call enqueues on these resources at a time
     bool ok = false;

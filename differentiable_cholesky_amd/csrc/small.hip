@@ -572,13 +572,12 @@ k_wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar, T *bbar,
 // the trailing matrix, the lanes of row j of X scale it by 1 / L_jj and publish
 // it, and every row t > j takes R_t -= L_tj X_j, with L_tj already in
 // registers from the factor step.  No tile-sized LDS buffer is needed, so the
-// kernel fits beside the blocks of a running matrix-core product.  X's strict
-// lower triangle is written transposed into the tile's strict upper triangle,
-// where the panel solve of the blocked factorisation reads it (that triangle
-// is cleared at the end of the factorisation).
+// kernel fits beside the blocks of a running matrix-core product.  X is
+// written whole (n x n, zeros above its diagonal) to Xo, where the panel
+// solve of the blocked factorisation reads it as a plain operand.
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base)
+k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, T *Xo, int64_t ldx)
 {
     constexpr int G = 16, E = 8, NP = G * E;
     // on the critical path of the factorisation, beside blocks of the trailing
@@ -667,17 +666,18 @@ k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t 
         }
     }
 
-    // L (lower) and X^T (strict upper)
+    // L (lower triangle of the tile) and X (whole, to Xo)
 #pragma unroll
     for (int a = 0; a < E; ++a)
 #pragma unroll
-        for (int b = 0; b <= a; ++b) {
+        for (int b = 0; b < E; ++b) {
             const int i = lr + G * a, k = lc + G * b;
-            if (i < n && k <= i) {
+            if (i >= n || k >= n)
+                continue;
+            const bool low = b <= a && k <= i;
+            if (low)
                 W[(int64_t)i * ld + k] = x[a][b];
-                if (k < i)
-                    W[(int64_t)k * ld + i] = y[a][b];
-            }
+            Xo[(int64_t)i * ldx + k] = low ? y[a][b] : T(0);
         }
     if (tid == 0)
         write_info(info, 0, fail, info_mode, info_base);
@@ -741,13 +741,15 @@ chol_status small_potrf(int n, int64_t batch, const T *A, int64_t lda, int64_t s
 }
 
 // Diagonal tile of the blocked factor: n <= 128, one 256-thread block; with
-// `inverse`, the tile's inverse is also formed (transposed, strict upper).
+// `inv`, the tile's inverse is also formed, whole (zeros above its diagonal),
+// into inv with leading dimension ldinv.
 template <typename T>
-chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, bool inverse,
-                       hipStream_t st)
+chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, T *inv,
+                       int64_t ldinv, hipStream_t st)
 {
-    if (inverse) {
-        hipLaunchKernelGGL((k_potrf_inv_tile<T>), dim3(1), dim3(256), 0, st, n, W, ld, info, info_mode, info_base);
+    if (inv) {
+        hipLaunchKernelGGL((k_potrf_inv_tile<T>), dim3(1), dim3(256), 0, st, n, W, ld, info, info_mode, info_base,
+                           inv, ldinv);
         CHOL_LAUNCH_CHECK();
         return CHOL_OK;
     }
@@ -784,7 +786,8 @@ chol_status wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar
 #define CHOL_INST(T)                                                                                      \
     template chol_status small_potrf<T>(int, int64_t, const T *, int64_t, int64_t, T *, int64_t, int64_t, \
                                         int32_t *, int, int64_t, hipStream_t);                            \
-    template chol_status diag_potrf<T>(int, T *, int64_t, int32_t *, int, int64_t, bool, hipStream_t);    \
+    template chol_status diag_potrf<T>(int, T *, int64_t, int32_t *, int, int64_t, T *, int64_t,          \
+                                       hipStream_t);                                                      \
     template chol_status small_potrf_adjoint<T>(int, int64_t, const T *, int64_t, int64_t, const T *,     \
                                                 int64_t, int64_t, T *, int64_t, int64_t, int, hipStream_t); \
     template chol_status wave_dot<T>(int, const T *, const T *, T *, const T *, T *, T *, int, hipStream_t);

@@ -37,6 +37,11 @@ chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, in
 
 // edge of a diagonal-tile inverse slot in the library's side buffer
 static constexpr int MAX_TILE = CHOL_MAX_NB;
+// depth of the forward's deferred trailing update: the far triangle is
+// updated with DEFER panels at once (at n = 16384 the factor took 42.7, 41.9,
+// 41.4, 43.9 and 45.9 ms with depths 2, 3, 4, 6 and 8: deeper groups add
+// narrow 128-deep updates of the columns inside the group)
+static constexpr int DEFER = 4;
 
 // ------------------------------------------------------------ elementwise ----
 enum { TRI_COPY_LOWER = 0, TRI_ZERO_UPPER = 1, TRI_ADD_LOWER = 2 };
@@ -225,20 +230,20 @@ static inline int split_chunk(int64_t K, int splits)
 // of the next tile column (diagonal factor and its inverse), beside the wide
 // update that follows it on sx.
 //
-// The trailing update is deferred so that most of it contracts over two
-// panels at once (a 256-deep product reads and writes the trailing triangle
-// half as often as two 128-deep ones).  Panel j is L[rows below tile j, tile
-// column j]; panels j-1 and j sit side by side in L, so the pair is one
-// two-tile-wide operand.  At step k (tile column k factored on sc, its panel
-// solved on sx):
-//   next(k):  tile column k+1 receives every panel it still lacks: k alone at
-//             odd k; k-1 and k at even k > 0 (panel 0 alone at k = 0);
-//             at even k the same launch also updates tile column k+2,
-//             which needs the same panels;
-//   then sc factors tile column k+1 while sx continues with
-//     even k: the first half of the tiles of the triangle right of tile
-//             column k+2, with the same panels as next(k);
-//     odd k:  the second half of that triangle (panels k-2, k-1).
+// The trailing update is deferred so that most of it contracts over DEFER
+// panels at once (a product DEFER*nb deep reads and writes the trailing
+// triangle once where DEFER products nb deep would each do so).  Panel j is
+// L[rows below tile j, tile column j]; consecutive panels sit side by side in
+// L, so a run of them is one wide operand.  The steps form groups of DEFER;
+// at step k = g + j of the group starting at g (tile column k factored on sc,
+// its panel solved on sx):
+//   j = 0:  tile columns k+1 .. k+DEFER receive the DEFER panels they lack
+//           (those of the previous group; panel 0 alone at k = 0), in one
+//           launch;
+//   j > 0:  tile columns k+1 .. g+DEFER receive panel k;
+//   then sc factors tile column k+1 while sx updates part j of DEFER of the
+//   group's far triangle (right of tile column g+DEFER) with the same panels
+//   as step g.
 // Every tile column thus has all earlier panels applied before it is factored,
 // and the two streams never touch the same tiles at the same time.
 template <typename T>
@@ -306,9 +311,10 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
     };
     if ((s = diag_step(0)) != CHOL_OK)
         return s;
-    // second half of a triangle update left for the next step
-    int64_t pend_c = -1, pend_f = 0;
-    int pend_np = 0, pend_t0 = 0, pend_tn = 0;
+    // the far triangle of the current group: its first tile column, panels,
+    // and tile count (fcol < 0: none)
+    int64_t fcol = -1, ff = 0;
+    int fnp = 0, ftiles = 0;
     for (int64_t k = 0; k < K; ++k) {
         const int64_t k0 = k * nb;
         const int kb = (int)std::min<int64_t>(nb, n - k0);
@@ -329,39 +335,42 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             if ((s = gemm<T, OP_MK, OP_MK, C_STORE>(p, 1, sx)) != CHOL_OK)
                 return s;
         }
-        const bool even = (k % 2) == 0;
-        const int np = (even && k > 0) ? 2 : 1;
+        // the tile columns up to the end of the group take the panels they
+        // still lack: at the group's first step the next DEFER columns take
+        // the DEFER panels of the previous group's steps (panel 0 alone at
+        // k = 0); at step j of the group, the DEFER - j columns left in the
+        // group take panel k
+        const int j = (int)(k % DEFER);
+        const int np = j == 0 ? (k == 0 ? 1 : DEFER) : 1;
         const int64_t f = k + 1 - np;
-        // at even k the next two tile columns take the same panels: one launch
-        // covers both (its tile above the diagonal is left alone by the
-        // lower-only store), in the time of one, as its blocks fit on the chip
-        const int64_t kn = std::min<int64_t>(even ? 2 * (int64_t)nb : nb, m);
-        if ((s = lower_update(r0, kn, f, np, false, 0, 0)) != CHOL_OK)
+        const int64_t w = std::min<int64_t>((int64_t)(j == 0 ? DEFER : DEFER - j) * nb, m);
+        if ((s = lower_update(r0, w, f, np, false, 0, 0)) != CHOL_OK)
             return s;
         // the next tile column's one-block kernels start on sc ...
         if (stream_join(sc, sx, e_next) != hipSuccess)
             return CHOL_ERR_HIP;
         if ((s = diag_step(k + 1)) != CHOL_OK)
             return s;
-        // ... while sx updates further right
-        if (even) {
-            const int64_t c3 = r0 + 2 * (int64_t)nb;
-            if (c3 < n) {
-                const int tiles = tri_tiles(c3), h = (tiles + 1) / 2;
-                if ((s = lower_update(c3, 0, f, np, true, 0, h)) != CHOL_OK)
-                    return s;
-                if (tiles > h) {
-                    pend_c = c3; pend_f = f; pend_np = np; pend_t0 = h; pend_tn = tiles - h;
-                }
+        // ... while sx updates part j of the group's far triangle (right of
+        // the group's columns) with the group's panels
+        if (j == 0) {
+            fcol = r0 + (int64_t)DEFER * nb;
+            if (fcol < n) {
+                ff = f;
+                fnp = np;
+                ftiles = tri_tiles(fcol);
+            } else {
+                fcol = -1;
             }
-        } else if (pend_c >= 0) {
-            if ((s = lower_update(pend_c, 0, pend_f, pend_np, true, pend_t0, pend_tn)) != CHOL_OK)
+        }
+        if (fcol >= 0) {
+            const int t0 = (int)((int64_t)ftiles * j / DEFER), t1 = (int)((int64_t)ftiles * (j + 1) / DEFER);
+            if (t1 > t0 && (s = lower_update(fcol, 0, ff, fnp, true, t0, t1 - t0)) != CHOL_OK)
                 return s;
-            pend_c = -1;
+            if (j == DEFER - 1)
+                fcol = -1;
         }
     }
-    if (pend_c >= 0 && (s = lower_update(pend_c, 0, pend_f, pend_np, true, pend_t0, pend_tn)) != CHOL_OK)
-        return s;
     if (stream_join(sc, sx, e_next) != hipSuccess)
         return CHOL_ERR_HIP;
     return tri_op<T, TRI_ZERO_UPPER>(n, nullptr, 0, L, ldl, sc);

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     chol_potrf_adjoint_batched,
     chol_potrf_adjoint_workspace_size,
     chol_potrf_batched,
+    chol_potrf_plan,
     chol_status_string,
     chol_wave_dot_fwd_adj,
     header_entry_points,

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.chol_status_string.argtypes = [st]
     lib.chol_abi_version.restype = ctypes.c_int
     lib.chol_abi_version.argtypes = []
+    lib.chol_potrf_plan.restype = ctypes.c_int64
+    lib.chol_potrf_plan.argtypes = [i64, i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), i64]
     lib.chol_last_hip_error.restype = ctypes.c_int
     lib.chol_last_hip_error.argtypes = []
     lib.chol_last_hip_error_string.restype = ctypes.c_char_p
@@ -233,6 +235,24 @@ def chol_wave_dot_fwd_adj(a, b, ybar, abar=None, bbar=None, staging: int = 0, st
 
 def chol_status_string(status: int) -> str:
     return status_string(status)
+
+
+PLAN_FIELDS = ("kind", "stream", "k", "c", "w", "f", "np", "t0", "tn", "slot")
+
+
+def chol_potrf_plan(n: int, nb: int = 0, copy: bool = True):
+    """The blocked factorisation's schedule for an n x n matrix (host only, no
+    GPU call): an int64 array with one row per operation, columns PLAN_FIELDS."""
+    import numpy as np
+    count = lib.chol_potrf_plan(n, nb, int(bool(copy)), None, 0)
+    if count < 0:
+        raise CholError(CHOL_ERR_INVALID_VALUE, f"chol_potrf_plan: invalid n={n} or nb={nb}")
+    out = np.zeros((count, len(PLAN_FIELDS)), dtype=np.int64)
+    if count:
+        got = lib.chol_potrf_plan(n, nb, int(bool(copy)),
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), count)
+        assert got == count
+    return out
 
 
 def chol_abi_version() -> int:

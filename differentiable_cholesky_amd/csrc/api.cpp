@@ -8,6 +8,7 @@
 
 #include "../../include/libchol.h"
 #include "common.hpp"
+#include "plan.hpp"
 #include "profile.hpp"
 
 namespace chol {
@@ -93,6 +94,21 @@ const char *chol_status_string(chol_status s)
     case CHOL_ERR_HIP: return "CHOL_ERR_HIP: a HIP launch failed";
     }
     return "unknown chol_status";
+}
+
+int64_t chol_potrf_plan(int64_t n, int64_t nb, int copy, int64_t *ops, int64_t cap)
+{
+    if (n < 0 || !nb_ok(nb) || cap < 0 || (cap > 0 && !ops))
+        return -1;
+    const std::vector<chol::FwdOp> plan = chol::forward_plan(n, nb ? (int)nb : DEFAULT_NB, copy != 0);
+    const int64_t count = (int64_t)plan.size();
+    for (int64_t i = 0; i < count && i < cap; ++i) {
+        const chol::FwdOp &o = plan[(size_t)i];
+        int64_t *r = ops + i * CHOL_PLAN_FIELDS;
+        r[0] = o.kind; r[1] = o.stream; r[2] = o.k; r[3] = o.c; r[4] = o.w;
+        r[5] = o.f; r[6] = o.np; r[7] = o.t0; r[8] = o.tn; r[9] = o.slot;
+    }
+    return count;
 }
 
 int chol_last_hip_error(void) { return chol::g_last_hip_error.load(std::memory_order_relaxed); }

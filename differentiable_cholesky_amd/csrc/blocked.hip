@@ -28,6 +28,7 @@
 #include "gemm.hpp"
 #include "profile.hpp"
 #include "side.hpp"
+#include "plan.hpp"
 
 namespace chol {
 
@@ -37,11 +38,6 @@ chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, in
 
 // edge of a diagonal-tile inverse slot in the library's side buffer
 static constexpr int MAX_TILE = CHOL_MAX_NB;
-// depth of the forward's deferred trailing update: the far triangle is
-// updated with DEFER panels at once (at n = 16384 the factor took 42.7, 41.9,
-// 41.4, 43.9 and 45.9 ms with depths 2, 3, 4, 6 and 8: deeper groups add
-// narrow 128-deep updates of the columns inside the group)
-static constexpr int DEFER = 4;
 
 // ------------------------------------------------------------ elementwise ----
 enum { TRI_COPY_LOWER = 0, TRI_ZERO_UPPER = 1, TRI_ADD_LOWER = 2 };
@@ -228,48 +224,15 @@ static inline int split_chunk(int64_t K, int splits)
 // Two library streams: `sx` runs every kernel that spans the matrix (panel
 // solves and trailing updates) in order; `sc` runs only the one-block kernels
 // of the next tile column (diagonal factor and its inverse), beside the wide
-// update that follows it on sx.
-//
-// The trailing update is deferred so that most of it contracts over DEFER
-// panels at once (a product DEFER*nb deep reads and writes the trailing
-// triangle once where DEFER products nb deep would each do so).  Panel j is
-// L[rows below tile j, tile column j]; consecutive panels sit side by side in
-// L, so a run of them is one wide operand.  The steps form groups of DEFER;
-// at step k = g + j of the group starting at g (tile column k factored on sc,
-// its panel solved on sx):
-//   j = 0:  tile columns k+1 .. k+DEFER receive the DEFER panels they lack
-//           (those of the previous group; panel 0 alone at k = 0), in one
-//           launch;
-//   j > 0:  tile columns k+1 .. g+DEFER receive panel k;
-//   then sc factors tile column k+1 while sx updates part j of DEFER of the
-//   group's far triangle (right of tile column g+DEFER) with the same panels
-//   as step g.
-// Every tile column thus has all earlier panels applied before it is factored,
-// and the two streams never touch the same tiles at the same time.
+// update that follows it on sx.  The order of the launches, the deferred
+// trailing update and the joins between the streams are the host-side plan of
+// plan.cpp; this executor launches that plan as it stands.
 template <typename T>
 static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl, int32_t *info,
                                     int nb, hipStream_t sc, hipStream_t sx, hipEvent_t e_diag, hipEvent_t e_next,
                                     int *sched_x, int cap_x, T *inv2)
 {
-    chol_status s;
-    if (A != L) {
-        if ((s = tri_op<T, TRI_COPY_LOWER>(n, A, lda, L, ldl, sc)) != CHOL_OK)
-            return s;
-    }
-    const int64_t K = (n + nb - 1) / nb;
-    // diagonal factor (and, if a panel follows, its inverse into slot k % 2 of
-    // inv2: the panel solve of tile column k reads it while tile column k+1 is
-    // factored into the other slot) of tile column k, on sc
-    auto inv_slot = [&](int64_t k) { return inv2 + (k & 1) * (int64_t)MAX_TILE * MAX_TILE; };
-    auto diag_step = [&](int64_t k) -> chol_status {
-        const int64_t k0 = k * nb;
-        const int kb = (int)std::min<int64_t>(nb, n - k0);
-        const double kb3 = (double)kb * kb * kb;
-        const bool inv = k0 + kb < n;
-        prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, inv ? 2 * kb3 / 3 : kb3 / 3);
-        return diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, k == 0 ? 1 : 2, k0, inv ? inv_slot(k) : nullptr,
-                             MAX_TILE, sc);
-    };
+    auto slot_ptr = [&](int slot) { return inv2 + (int64_t)slot * MAX_TILE * MAX_TILE; };
     // lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T with Q = panels f .. f+np-1
     // (tile columns f .. f+np-1 of L); tri: the whole trailing triangle W[c:, c:]
     // instead, restricted to the 128 x 128 tiles t0 .. t0+tn-1 (row-major over
@@ -305,75 +268,60 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, flops);
         return gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx);
     };
-    auto tri_tiles = [&](int64_t c) -> int {
-        const int64_t TI = (n - c + 127) / 128;
-        return (int)(TI * (TI + 1) / 2);
-    };
-    if ((s = diag_step(0)) != CHOL_OK)
-        return s;
-    // the far triangle of the current group: its first tile column, panels,
-    // and tile count (fcol < 0: none)
-    int64_t fcol = -1, ff = 0;
-    int fnp = 0, ftiles = 0;
-    for (int64_t k = 0; k < K; ++k) {
-        const int64_t k0 = k * nb;
-        const int kb = (int)std::min<int64_t>(nb, n - k0);
-        const int64_t r0 = k0 + kb, m = n - r0;
-        if (m == 0)
+    const std::vector<FwdOp> plan = forward_plan(n, nb, A != L);
+    for (const FwdOp &o : plan) {
+        chol_status s = CHOL_OK;
+        switch (o.kind) {
+        case FWD_COPY:
+            s = tri_op<T, TRI_COPY_LOWER>(n, A, lda, L, ldl, sc);
             break;
-        if (stream_join(sx, sc, e_diag) != hipSuccess)
-            return CHOL_ERR_HIP;
-        // panel: L_ik = W_ik * Linv^T  (in place; one block spans the full panel
-        // width; Linv is read whole from its slot, element (j, t) = Linv[j][t])
-        {
+        case FWD_DIAG: {
+            const int64_t k0 = o.k * nb;
+            const int kb = (int)std::min<int64_t>(nb, n - k0);
+            const double kb3 = (double)kb * kb * kb;
+            prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, o.slot >= 0 ? 2 * kb3 / 3 : kb3 / 3);
+            s = diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, o.k == 0 ? 1 : 2, k0,
+                              o.slot >= 0 ? slot_ptr(o.slot) : nullptr, MAX_TILE, sc);
+            break;
+        }
+        case FWD_PANEL: {
+            // L_ik = W_ik * Linv^T  (in place; one block spans the full panel
+            // width; Linv is read whole from its slot, element (j, t) = Linv[j][t])
+            const int64_t k0 = o.k * nb;
+            const int kb = (int)std::min<int64_t>(nb, n - k0);
+            const int64_t r0 = k0 + kb, m = n - r0;
             GemmArgs<T> p{};
             p.M = (int)m; p.N = kb; p.K = kb;
             p.a = L + r0 * ldl + k0; p.lda = ldl;
-            p.b = inv_slot(k); p.ldb = MAX_TILE;
+            p.b = slot_ptr(o.slot); p.ldb = MAX_TILE;
             p.c = L + r0 * ldl + k0; p.ldc = ldl;
             prof::Scope ps(CHOL_K_PANEL_SOLVE, sx, (double)m * kb * kb);
-            if ((s = gemm<T, OP_MK, OP_MK, C_STORE>(p, 1, sx)) != CHOL_OK)
-                return s;
+            s = gemm<T, OP_MK, OP_MK, C_STORE>(p, 1, sx);
+            break;
         }
-        // the tile columns up to the end of the group take the panels they
-        // still lack: at the group's first step the next DEFER columns take
-        // the DEFER panels of the previous group's steps (panel 0 alone at
-        // k = 0); at step j of the group, the DEFER - j columns left in the
-        // group take panel k
-        const int j = (int)(k % DEFER);
-        const int np = j == 0 ? (k == 0 ? 1 : DEFER) : 1;
-        const int64_t f = k + 1 - np;
-        const int64_t w = std::min<int64_t>((int64_t)(j == 0 ? DEFER : DEFER - j) * nb, m);
-        if ((s = lower_update(r0, w, f, np, false, 0, 0)) != CHOL_OK)
+        case FWD_UPDATE:
+            s = lower_update(o.c, o.w, o.f, o.np, false, 0, 0);
+            break;
+        case FWD_TRI:
+            s = lower_update(o.c, 0, o.f, o.np, true, o.t0, o.tn);
+            break;
+        case FWD_JOIN: {
+            hipEvent_t ev = o.slot == 0 ? e_diag : e_next;
+            const bool wide = o.stream == FWD_WIDE;
+            if (stream_join(wide ? sx : sc, wide ? sc : sx, ev) != hipSuccess)
+                s = CHOL_ERR_HIP;
+            break;
+        }
+        case FWD_ZERO_UPPER:
+            s = tri_op<T, TRI_ZERO_UPPER>(n, nullptr, 0, L, ldl, sc);
+            break;
+        default:
+            s = CHOL_ERR_INVALID_VALUE;
+        }
+        if (s != CHOL_OK)
             return s;
-        // the next tile column's one-block kernels start on sc ...
-        if (stream_join(sc, sx, e_next) != hipSuccess)
-            return CHOL_ERR_HIP;
-        if ((s = diag_step(k + 1)) != CHOL_OK)
-            return s;
-        // ... while sx updates part j of the group's far triangle (right of
-        // the group's columns) with the group's panels
-        if (j == 0) {
-            fcol = r0 + (int64_t)DEFER * nb;
-            if (fcol < n) {
-                ff = f;
-                fnp = np;
-                ftiles = tri_tiles(fcol);
-            } else {
-                fcol = -1;
-            }
-        }
-        if (fcol >= 0) {
-            const int t0 = (int)((int64_t)ftiles * j / DEFER), t1 = (int)((int64_t)ftiles * (j + 1) / DEFER);
-            if (t1 > t0 && (s = lower_update(fcol, 0, ff, fnp, true, t0, t1 - t0)) != CHOL_OK)
-                return s;
-            if (j == DEFER - 1)
-                fcol = -1;
-        }
     }
-    if (stream_join(sc, sx, e_next) != hipSuccess)
-        return CHOL_ERR_HIP;
-    return tri_op<T, TRI_ZERO_UPPER>(n, nullptr, 0, L, ldl, sc);
+    return CHOL_OK;
 }
 
 template <typename T>

@@ -1,0 +1,102 @@
+#include "plan.hpp"
+
+#include <algorithm>
+
+namespace chol {
+
+// The trailing update is deferred so that most of it contracts over DEFER
+// panels at once (a product DEFER*nb deep reads and writes the trailing
+// triangle once where DEFER products nb deep would each do so).  Panel j is
+// L[rows below tile j, tile column j]; consecutive panels sit side by side in
+// L, so a run of them is one wide operand.  The steps form groups of DEFER;
+// at step k = g + j of the group starting at g (tile column k factored on the
+// chain stream, its panel solved on the wide stream):
+//   j = 0:  tile columns k+1 .. k+DEFER receive the DEFER panels they lack
+//           (those of the previous group; panel 0 alone at k = 0), in one
+//           launch;
+//   j > 0:  tile columns k+1 .. g+DEFER receive panel k;
+//   then the chain stream factors tile column k+1 while the wide stream
+//   updates part j of DEFER of the group's far triangle (right of tile column
+//   g+DEFER) with the same panels as step g.
+// The diagonal tiles' inverses alternate between two slots: the panel solve
+// of tile column k reads slot k % 2 while tile column k+1 is factored into
+// the other one.
+std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy)
+{
+    std::vector<FwdOp> ops;
+    if (n <= 0 || nb <= 0)
+        return ops;
+    auto op = [&](int kind, int stream) -> FwdOp & {
+        ops.push_back(FwdOp{kind, stream, 0, 0, 0, 0, 0, 0, 0, -1});
+        return ops.back();
+    };
+    const int64_t K = (n + nb - 1) / nb;
+    auto diag = [&](int64_t k) {
+        FwdOp &o = op(FWD_DIAG, FWD_CHAIN);
+        o.k = k;
+        o.slot = (k * nb + std::min<int64_t>(nb, n - k * nb) < n) ? (int)(k & 1) : -1;
+    };
+    auto tri_tiles = [&](int64_t c) -> int {
+        const int64_t TI = (n - c + 127) / 128;
+        return (int)(TI * (TI + 1) / 2);
+    };
+    if (copy)
+        op(FWD_COPY, FWD_CHAIN);
+    diag(0);
+    // the far triangle of the current group: first column, panels, tile count
+    int64_t fcol = -1, ff = 0;
+    int fnp = 0, ftiles = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t k0 = k * nb;
+        const int64_t r0 = k0 + std::min<int64_t>(nb, n - k0), m = n - r0;
+        if (m == 0)
+            break;
+        op(FWD_JOIN, FWD_WIDE).slot = 0;
+        {
+            FwdOp &o = op(FWD_PANEL, FWD_WIDE);
+            o.k = k;
+            o.slot = (int)(k & 1);
+        }
+        const int j = (int)(k % FWD_DEFER);
+        const int np = j == 0 ? (k == 0 ? 1 : FWD_DEFER) : 1;
+        const int64_t f = k + 1 - np;
+        {
+            FwdOp &o = op(FWD_UPDATE, FWD_WIDE);
+            o.c = r0;
+            o.w = std::min<int64_t>((int64_t)(j == 0 ? FWD_DEFER : FWD_DEFER - j) * nb, m);
+            o.f = f;
+            o.np = np;
+        }
+        op(FWD_JOIN, FWD_CHAIN).slot = 1;
+        diag(k + 1);
+        if (j == 0) {
+            fcol = r0 + (int64_t)FWD_DEFER * nb;
+            if (fcol < n) {
+                ff = f;
+                fnp = np;
+                ftiles = tri_tiles(fcol);
+            } else {
+                fcol = -1;
+            }
+        }
+        if (fcol >= 0) {
+            const int t0 = (int)((int64_t)ftiles * j / FWD_DEFER);
+            const int t1 = (int)((int64_t)ftiles * (j + 1) / FWD_DEFER);
+            if (t1 > t0) {
+                FwdOp &o = op(FWD_TRI, FWD_WIDE);
+                o.c = fcol;
+                o.f = ff;
+                o.np = fnp;
+                o.t0 = t0;
+                o.tn = t1 - t0;
+            }
+            if (j == FWD_DEFER - 1)
+                fcol = -1;
+        }
+    }
+    op(FWD_JOIN, FWD_CHAIN).slot = 1;
+    op(FWD_ZERO_UPPER, FWD_CHAIN);
+    return ops;
+}
+
+} // namespace chol

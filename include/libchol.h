@@ -208,6 +208,35 @@ const char *chol_status_string(chol_status status);
 /* LIBCHOL_ABI_VERSION of the loaded library. */
 int chol_abi_version(void);
 
+/*
+ * chol_potrf_plan -- the schedule chol_potrf's blocked path (n >
+ * CHOL_SMALL_MAX_N) enqueues for an n x n matrix with tile size nb, so that it
+ * can be checked on the host.  It is the right-looking factorisation of the
+ * page's blocked algorithm with the trailing update deferred to groups of
+ * panels.  Host only: calls no GPU function.
+ *   ops  [out] host, cap rows of CHOL_PLAN_FIELDS int64 each (may be NULL if
+ *              cap == 0), one row per operation in enqueue order:
+ *     kind    0 copy lower(A) into L (chain stream)
+ *             1 factor diagonal tile k (chain); slot >= 0: its inverse is
+ *               written whole into inverse slot `slot`
+ *             2 panel solve of tile column k below its diagonal tile (wide
+ *               stream), reading inverse slot `slot`
+ *             3 lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T with Q the
+ *               tile columns f .. f+np-1 of L (wide)
+ *             4 the lower 128 x 128 tiles t0 .. t0+tn-1 (row-major) of the
+ *               trailing triangle W[c:, c:] -= Q Q^T, same Q (wide)
+ *             5 `stream` waits for every operation enqueued so far on the
+ *               other stream
+ *             6 clear the strict upper triangle of L (chain)
+ *     stream  0 chain, 1 wide;  then k, c, w, f, np, t0, tn, slot (element
+ *             offsets and counts; unused fields 0, unused slot -1)
+ *   copy nonzero when A and L are different buffers.
+ * Returns the number of operations (rows beyond cap are not written), or -1
+ * for n < 0 or nb outside 0 .. CHOL_MAX_NB (0 picks 128).
+ */
+#define CHOL_PLAN_FIELDS 10
+int64_t chol_potrf_plan(int64_t n, int64_t nb, int copy, int64_t *ops, int64_t cap);
+
 /* Diagnostics: the hipError_t code (0 if none so far) of the HIP call whose
  * failure made the most recent call return CHOL_ERR_HIP, process-wide, and
  * HIP's description of it (static string, never NULL). */

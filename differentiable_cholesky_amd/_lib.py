@@ -68,7 +68,7 @@ def _load() -> ctypes.CDLL:
     lib.chol_abi_version.restype = ctypes.c_int
     lib.chol_abi_version.argtypes = []
     lib.chol_potrf_plan.restype = ctypes.c_int64
-    lib.chol_potrf_plan.argtypes = [i64, i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), i64]
+    lib.chol_potrf_plan.argtypes = [i64, i64, ctypes.c_int, i64, ctypes.POINTER(ctypes.c_int64), i64]
     lib.chol_last_hip_error.restype = ctypes.c_int
     lib.chol_last_hip_error.argtypes = []
     lib.chol_last_hip_error_string.restype = ctypes.c_char_p
@@ -240,16 +240,21 @@ def chol_status_string(status: int) -> str:
 PLAN_FIELDS = ("kind", "stream", "k", "c", "w", "f", "np", "t0", "tn", "slot")
 
 
-def chol_potrf_plan(n: int, nb: int = 0, copy: bool = True):
+# block slots of the persistent trailing-update grid on a 256-CU MI355X
+# (two blocks per CU on all but 16 CUs)
+PLAN_SLOTS_MI355X = 480
+
+
+def chol_potrf_plan(n: int, nb: int = 0, copy: bool = True, slots: int = PLAN_SLOTS_MI355X):
     """The blocked factorisation's schedule for an n x n matrix (host only, no
     GPU call): an int64 array with one row per operation, columns PLAN_FIELDS."""
     import numpy as np
-    count = lib.chol_potrf_plan(n, nb, int(bool(copy)), None, 0)
+    count = lib.chol_potrf_plan(n, nb, int(bool(copy)), slots, None, 0)
     if count < 0:
-        raise CholError(CHOL_ERR_INVALID_VALUE, f"chol_potrf_plan: invalid n={n} or nb={nb}")
+        raise CholError(CHOL_ERR_INVALID_VALUE, f"chol_potrf_plan: invalid n={n}, nb={nb} or slots={slots}")
     out = np.zeros((count, len(PLAN_FIELDS)), dtype=np.int64)
     if count:
-        got = lib.chol_potrf_plan(n, nb, int(bool(copy)),
+        got = lib.chol_potrf_plan(n, nb, int(bool(copy)), slots,
                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), count)
         assert got == count
     return out

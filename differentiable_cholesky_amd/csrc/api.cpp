@@ -96,11 +96,12 @@ const char *chol_status_string(chol_status s)
     return "unknown chol_status";
 }
 
-int64_t chol_potrf_plan(int64_t n, int64_t nb, int copy, int64_t *ops, int64_t cap)
+int64_t chol_potrf_plan(int64_t n, int64_t nb, int copy, int64_t slots, int64_t *ops, int64_t cap)
 {
-    if (n < 0 || !nb_ok(nb) || cap < 0 || (cap > 0 && !ops))
+    if (n < 0 || !nb_ok(nb) || slots < 0 || slots > INT32_MAX || cap < 0 || (cap > 0 && !ops))
         return -1;
-    const std::vector<chol::FwdOp> plan = chol::forward_plan(n, nb ? (int)nb : DEFAULT_NB, copy != 0);
+    const std::vector<chol::FwdOp> plan =
+        chol::forward_plan(n, nb ? (int)nb : DEFAULT_NB, copy != 0, (int)slots);
     const int64_t count = (int64_t)plan.size();
     for (int64_t i = 0; i < count && i < cap; ++i) {
         const chol::FwdOp &o = plan[(size_t)i];

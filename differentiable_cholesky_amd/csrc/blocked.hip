@@ -181,21 +181,30 @@ k_trinv(int64_t n_total, int nb, int64_t tile0, int64_t step, T *W, int64_t ld, 
         }
 }
 
-// C_lower(n x n) -= sum_s part[s] (lower entries only)
+// C_lower(n x n) -= sum_s part[s] (lower entries only).  A block takes 64
+// consecutive entries; its four waves each sum every fourth split (wave w:
+// splits w, w+4, ...), and the four sums are added in wave order, so the
+// result does not depend on scheduling.  With up to 128 partials of a
+// 128 x 128 tile this spreads the reads over 256 blocks instead of leaving
+// one thread per entry to walk all of them.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_splitk_reduce_lower(int n, int splits, const T *part, T *c, int64_t ldc)
 {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)n * n)
-        return;
+    __shared__ T sums[4][64];
+    const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+    const int64_t tot = (int64_t)n * n;
+    const int64_t idx = (int64_t)blockIdx.x * 64 + lane;
     const int r = (int)(idx / n), col = (int)(idx % n);
-    if (col > r)
-        return;
+    const bool live = idx < tot && col <= r;
     T s = T(0);
-    for (int q = 0; q < splits; ++q)
-        s += part[(int64_t)q * n * n + idx];
-    c[(int64_t)r * ldc + col] -= s;
+    if (live)
+        for (int q = w; q < splits; q += 4)
+            s += part[(int64_t)q * tot + idx];
+    sums[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && live)
+        c[(int64_t)r * ldc + col] -= ((sums[0][lane] + sums[1][lane]) + sums[2][lane]) + sums[3][lane];
 }
 
 // C(M x N) -= sum_s part[s] (all entries), part row-major M x N per split
@@ -268,7 +277,7 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, flops);
         return gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx);
     };
-    const std::vector<FwdOp> plan = forward_plan(n, nb, A != L);
+    const std::vector<FwdOp> plan = forward_plan(n, nb, A != L, cap_x);
     for (const FwdOp &o : plan) {
         chol_status s = CHOL_OK;
         switch (o.kind) {
@@ -350,11 +359,13 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
 //   [Wb    : n * n]                         running gradient (absent when formed in adj_A)
 //   [inv   : K * nb * nb]                   inverses of the diagonal tiles of L
 //   [part_x: SIDE_SPLIT_MAX * n * nb]       split partials of the large symmetric product
-//   [part_b: (TILE_SPLIT_MAX + 1) * nb * nb] split partials of tile-sized products, plus
-//                                           the slot the tile adjoint adds
+//   [part_b: (ceil(n / 128) + 1) * nb * nb] one partial of the tile column's diagonal
+//                                           update per 128-row tile of its panel, plus the
+//                                           slot the tile adjoint adds
 //   [part_c: 2 * nb * nb]                   the tile adjoint's scratch tiles
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-static const int TILE_SPLIT_MAX = 256;   // splits of tile-sized products with a long contraction
+// partials of the diagonal update: one per 128-row tile of the longest panel
+static inline int64_t panel_tiles(int64_t n) { return (n + 127) / 128; }
 static const int SIDE_SPLIT_MAX = 32;    // splits of the large symmetric product
 
 size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
@@ -365,17 +376,9 @@ size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
         s += align256((size_t)n * n * esize);
     s += align256((size_t)K * nb * nb * esize);
     s += align256((size_t)SIDE_SPLIT_MAX * n * nb * esize);
-    s += align256((size_t)(TILE_SPLIT_MAX + 1) * nb * nb * esize);
+    s += align256((size_t)(panel_tiles(n) + 1) * nb * nb * esize);
     s += align256((size_t)2 * nb * nb * esize);
     return s;
-}
-
-// Split count and chunk for a tile-sized product with contraction length K.
-static inline int tile_splits(int64_t K, int64_t &chunk)
-{
-    int splits = (int)std::max<int64_t>(1, std::min<int64_t>(TILE_SPLIT_MAX, (K + 127) / 128));
-    chunk = split_chunk(K, splits);
-    return (int)((K + chunk - 1) / chunk);
 }
 
 // C (M x N) -= Sym(S)[0:M, 0:K] B with S symmetric stored as its lower triangle
@@ -610,9 +613,9 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
     T *part_x = (T *)w;
     w += align256((size_t)SIDE_SPLIT_MAX * n * nb * sizeof(T));
     T *part_b = (T *)w;
-    w += align256((size_t)(TILE_SPLIT_MAX + 1) * nb * nb * sizeof(T));
+    w += align256((size_t)(panel_tiles(n) + 1) * nb * nb * sizeof(T));
     T *part_c = (T *)w;
-    T *slot = part_b + (int64_t)TILE_SPLIT_MAX * nb * nb;   // Sym(G(k)) L[tile k, tile k-1]
+    T *slot = part_b + panel_tiles(n) * nb * nb;   // Sym(G(k)) L[tile k, tile k-1]
 
     if ((const T *)Wb != adjL) {
         if ((s = tri_op<T, TRI_COPY_LOWER>(n, adjL, ldal, Wb, ldw, sx)) != CHOL_OK)
@@ -667,15 +670,15 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         if (stream_join(sc, sx, e_wide) != hipSuccess)
             return CHOL_ERR_HIP;
         if (m > 0) {
-            // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows
+            // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows into
+            // 128-row chunks, the partials summed in chunk order
             GemmArgs<T> p{};
             p.M = kb; p.N = kb; p.K = (int)m;
             p.a = Wp; p.lda = ldw;
             p.b = Lp; p.ldb = ldl;
-            int64_t chunk;
-            const int splits = tile_splits(m, chunk);
-            p.kchunk = (int)chunk;
+            p.kchunk = 128;
             p.part = part_b;
+            const int splits = (int)((m + 127) / 128);
             {
                 prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, sc, 2.0 * m * kb * kb);
                 if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sc)) != CHOL_OK)
@@ -683,7 +686,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
             }
             const int64_t tot = (int64_t)kb * kb;
             prof::Scope ps(CHOL_K_REDUCE, sc, (double)tot * (splits + 2) * sizeof(T));
-            hipLaunchKernelGGL((k_splitk_reduce_lower<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256),
+            hipLaunchKernelGGL((k_splitk_reduce_lower<T>), dim3((unsigned)((tot + 63) / 64)), dim3(256),
                                0, sc, kb, splits, (const T *)part_b, Wkk, ldw);
             CHOL_LAUNCH_CHECK();
         }

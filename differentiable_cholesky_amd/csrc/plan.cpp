@@ -18,10 +18,16 @@ namespace chol {
 //   then the chain stream factors tile column k+1 while the wide stream
 //   updates part j of DEFER of the group's far triangle (right of tile column
 //   g+DEFER) with the same panels as step g.
+// The far triangle's tiles are taken by `slots` persistent blocks, each tile
+// the same long product (DEFER*nb deep), so a launch lasts a whole number of
+// rounds of tiles however few tiles its last round holds.  The parts are
+// therefore cut at multiples of `slots` tiles: the group's rounds are shared
+// out among its DEFER launches and only one launch ends in a partly filled
+// round (slots <= 0: equal parts).
 // The diagonal tiles' inverses alternate between two slots: the panel solve
 // of tile column k reads slot k % 2 while tile column k+1 is factored into
 // the other one.
-std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy)
+std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
 {
     std::vector<FwdOp> ops;
     if (n <= 0 || nb <= 0)
@@ -80,8 +86,13 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy)
             }
         }
         if (fcol >= 0) {
-            const int t0 = (int)((int64_t)ftiles * j / FWD_DEFER);
-            const int t1 = (int)((int64_t)ftiles * (j + 1) / FWD_DEFER);
+            auto cut = [&](int q) -> int {
+                if (slots <= 0)
+                    return (int)((int64_t)ftiles * q / FWD_DEFER);
+                const int64_t rounds = ((int64_t)ftiles + slots - 1) / slots;
+                return (int)std::min<int64_t>(ftiles, rounds * q / FWD_DEFER * slots);
+            };
+            const int t0 = cut(j), t1 = cut(j + 1);
             if (t1 > t0) {
                 FwdOp &o = op(FWD_TRI, FWD_WIDE);
                 o.c = fcol;

@@ -38,7 +38,9 @@ struct FwdOp {
 // 128-deep updates of the columns inside the group)
 constexpr int FWD_DEFER = 4;
 
-// The operations for an n x n factor with tile size nb (copy: A is not L).
-std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy);
+// The operations for an n x n factor with tile size nb (copy: A is not L);
+// slots: block slots of the persistent grid that runs the FWD_TRI updates
+// (0: the far triangle is cut into equal parts).
+std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots);
 
 } // namespace chol

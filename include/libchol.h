@@ -231,11 +231,17 @@ int chol_abi_version(void);
  *     stream  0 chain, 1 wide;  then k, c, w, f, np, t0, tn, slot (element
  *             offsets and counts; unused fields 0, unused slot -1)
  *   copy nonzero when A and L are different buffers.
+ *   slots  block slots of the persistent grid that takes the tiles of the
+ *          kind-4 operations: each group's far triangle is cut at multiples
+ *          of it, so that only one of the group's launches ends in a partly
+ *          filled round of tiles (0: equal parts).  chol_potrf uses two
+ *          blocks per CU on all but 16 CUs of the device (480 on a 256-CU
+ *          MI355X), or on all of them with 64 CUs or fewer.
  * Returns the number of operations (rows beyond cap are not written), or -1
- * for n < 0 or nb outside 0 .. CHOL_MAX_NB (0 picks 128).
+ * for n < 0, slots < 0 or nb outside 0 .. CHOL_MAX_NB (0 picks 128).
  */
 #define CHOL_PLAN_FIELDS 10
-int64_t chol_potrf_plan(int64_t n, int64_t nb, int copy, int64_t *ops, int64_t cap);
+int64_t chol_potrf_plan(int64_t n, int64_t nb, int copy, int64_t slots, int64_t *ops, int64_t cap);
 
 /* Diagnostics: the hipError_t code (0 if none so far) of the HIP call whose
  * failure made the most recent call return CHOL_ERR_HIP, process-wide, and

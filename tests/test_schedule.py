@@ -38,9 +38,9 @@ def _mask(C, rows, cols, lower_only):
     return m
 
 
-def _check(n, nb, plan=None):
+def _check(n, nb, plan=None, slots=480):
     if plan is None:
-        plan = dc.chol_potrf_plan(n, nb, copy=True)
+        plan = dc.chol_potrf_plan(n, nb, copy=True, slots=slots)
     nbe = nb or 128
     g = math.gcd(nbe, 128)
     C = _cells(n, g)
@@ -138,13 +138,37 @@ def _check(n, nb, plan=None):
 @pytest.mark.parametrize("n,nb", [(65, 32), (100, 32), (127, 64), (128, 64), (129, 128), (200, 64),
                                   (255, 128), (256, 128), (300, 16), (384, 128), (513, 128), (700, 64),
                                   (1000, 0), (1030, 32), (1300, 128), (2100, 96)])
-def test_forward_schedule(n, nb):
-    _check(n, nb)
+@pytest.mark.parametrize("slots", [0, 5, 480])
+def test_forward_schedule(n, nb, slots):
+    # slots 0: equal parts; 5: far triangles cut at multiples of 5 tiles, with
+    # empty parts where a group has fewer rounds than parts; 480: MI355X
+    _check(n, nb, slots=slots)
 
 
 def test_forward_schedule_benchmark_size():
     # the schedule the n = 16384 benchmark runs (128 tile columns)
     _check(16384, 128)
+
+
+def test_far_triangle_cut_at_whole_rounds():
+    # each group's far triangle: parts in order, covering its tiles once, and
+    # every part but the group's last one a whole number of rounds
+    slots = 480
+    plan = dc.chol_potrf_plan(16384, 128, copy=True, slots=slots)
+    groups = {}
+    for row in plan:
+        if row[0] == TRI:
+            groups.setdefault((row[3], row[5], row[6]), []).append((row[7], row[8]))
+    assert groups
+    for (c, f, np_), parts in groups.items():
+        T = (16384 - c + 127) // 128
+        tiles = T * (T + 1) // 2
+        assert parts[0][0] == 0 and sum(tn for _, tn in parts) == tiles
+        for (t0, tn), (t1, _) in zip(parts, parts[1:]):
+            assert t0 + tn == t1
+        for t0, tn in parts[:-1]:
+            assert tn % slots == 0, (c, parts)
+        assert len(parts) <= 4
 
 
 def _mutants(plan):
@@ -180,7 +204,8 @@ def test_schedule_check_catches_planted_mistakes(n, nb):
 
 
 def test_plan_argument_errors():
-    assert _lib.lib.chol_potrf_plan(-1, 0, 1, None, 0) == -1
-    assert _lib.lib.chol_potrf_plan(100, 129, 1, None, 0) == -1
-    assert _lib.lib.chol_potrf_plan(100, -1, 1, None, 0) == -1
-    assert _lib.lib.chol_potrf_plan(0, 0, 1, None, 0) == 0
+    assert _lib.lib.chol_potrf_plan(-1, 0, 1, 480, None, 0) == -1
+    assert _lib.lib.chol_potrf_plan(100, 129, 1, 480, None, 0) == -1
+    assert _lib.lib.chol_potrf_plan(100, -1, 1, 480, None, 0) == -1
+    assert _lib.lib.chol_potrf_plan(100, 0, 1, -1, None, 0) == -1
+    assert _lib.lib.chol_potrf_plan(0, 0, 1, 480, None, 0) == 0

@@ -33,8 +33,10 @@
 // writes entries it read itself (in-place calls need no ordering between
 // lanes).  Per-step broadcasts -- a column of the trailing matrix, a row of L,
 // a solved row or column -- go through small double-buffered LDS vectors in
-// which column c of a row sits at (c % G) * E + c / G, so that every lane reads
-// the E entries it needs as one contiguous run.
+// which column c of a row sits at (c % G) * (E + 1) + c / G, so that every lane
+// reads the E entries it needs as one contiguous run; the one padding slot per
+// lane column puts the runs of different lane columns (and, with the padded
+// per-matrix stride, of different matrices in a wave) on different LDS banks.
 #include "common.hpp"
 
 namespace chol {
@@ -46,6 +48,8 @@ template <int G_, int E_> struct TileShape {
     static constexpr int LPM = G * G;                     // lanes per matrix
     static constexpr int THREADS = LPM < 64 ? 64 : LPM;   // one wavefront at least
     static constexpr int MPB = THREADS / LPM;             // matrices per block
+    static constexpr int EP = E + 1;                      // LDS slots per lane column (one pad)
+    static constexpr int VS = G * EP;                     // LDS vector stride per matrix
 };
 
 // Waves per SIMD the register allocation aims for (the scheduler otherwise
@@ -203,8 +207,8 @@ k_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
              T *L, int64_t ldl, int64_t sL, int32_t *info, int info_mode, int64_t info_base)
 {
     typedef TileShape<G, E> S;
-    constexpr int NP = S::NP, MPB = S::MPB;
-    __shared__ T colbuf[2 * MPB * NP];
+    constexpr int MPB = S::MPB, EP = S::EP, VS = S::VS;
+    __shared__ T colbuf[2 * MPB * VS];
 
     const int tid = threadIdx.x;
     const int g = tid / S::LPM;
@@ -239,22 +243,22 @@ k_potrf_tile(int n, int64_t batch, const T *A, int64_t lda, int64_t sA,
         for (int u_ = 0; u_ < G; ++u_) {
             const int jr = u_;
             const int j = jb * G + jr;
-            T *cb = colbuf + ((j & 1) * MPB + g) * NP;
+            T *cb = colbuf + ((j & 1) * MPB + g) * VS;
             // owners of column j publish it (unscaled); rows lr + G*a
             if (lc == jr) {
     #pragma unroll
                 for (int a = jb; a < E; ++a)
-                    cb[lr * E + a] = x[a][jb];
+                    cb[lr * EP + a] = x[a][jb];
             }
             __syncthreads();
-            const T d = cb[jr * E + jb];
+            const T d = cb[jr * EP + jb];
             T u[E], v[E];
     #pragma unroll
             for (int a = jb; a < E; ++a)
-                u[a] = cb[lr * E + a];
+                u[a] = cb[lr * EP + a];
     #pragma unroll
             for (int b = jb; b < E; ++b)
-                v[b] = cb[lc * E + b];
+                v[b] = cb[lc * EP + b];
             if (!(d > T(0)) && fail == 0)
                 fail = j + 1;
             T sq, rs;
@@ -317,10 +321,12 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
                  T *adjA, int64_t ldaa, int64_t sAA, int accumulate)
 {
     typedef TileShape<G, E> S;
-    constexpr int NP = S::NP, MPB = S::MPB;
+    // unpadded vectors (column c at (c % G) * E + c / G): the padded layout of
+    // the factor measured slower here
+    constexpr int NP = S::NP, MPB = S::MPB, EP = E, VS = NP;
     static_assert(S::LPM <= 64, "one matrix per wavefront at most (lane shuffles)");
-    __shared__ T rowb[2 * MPB * NP];    // a row of L
-    __shared__ T vecb[2 * MPB * NP];    // a row of adj_L, a column of V or a row of Z
+    __shared__ T rowb[2 * MPB * VS];    // a row of L
+    __shared__ T vecb[2 * MPB * VS];    // a row of adj_L, a column of V or a row of Z
     __shared__ T dinv[MPB * NP];        // 1 / L_jj
 
     const int tid = threadIdx.x;
@@ -370,23 +376,23 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
         for (int u_ = 0; u_ < G; ++u_) {
             const int kr = u_;
             const int k = kb * G + kr;
-            T *rb = rowb + ((k & 1) * MPB + g) * NP;
-            T *vb = vecb + ((k & 1) * MPB + g) * NP;
+            T *rb = rowb + ((k & 1) * MPB + g) * VS;
+            T *vb = vecb + ((k & 1) * MPB + g) * VS;
             if (lr == kr) {
     #pragma unroll
                 for (int b = 0; b < E; ++b) {
-                    rb[lc * E + b] = (b <= kb) ? lw[kb][b] : T(0);
-                    vb[lc * E + b] = (b <= kb) ? bw[kb][b] : T(0);
+                    rb[lc * EP + b] = (b <= kb) ? lw[kb][b] : T(0);
+                    vb[lc * EP + b] = (b <= kb) ? bw[kb][b] : T(0);
                 }
             }
             __syncthreads();
             T lk[E], ak[E];
     #pragma unroll
             for (int a = 0; a <= kb; ++a)
-                lk[a] = rb[lr * E + a];          // L[k][lr + G a]
+                lk[a] = rb[lr * EP + a];          // L[k][lr + G a]
     #pragma unroll
             for (int b = 0; b <= kb; ++b)
-                ak[b] = vb[lc * E + b];          // adjL[k][lc + G b]
+                ak[b] = vb[lc * EP + b];          // adjL[k][lc + G b]
     #pragma unroll
             for (int a = 0; a <= kb; ++a)
     #pragma unroll
@@ -420,29 +426,29 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
         for (int u_ = 0; u_ < G; ++u_) {
             const int jr = G - 1 - u_;
             const int j = jb * G + jr;
-            T *rb = rowb + ((j & 1) * MPB + g) * NP;
-            T *vb = vecb + ((j & 1) * MPB + g) * NP;
+            T *rb = rowb + ((j & 1) * MPB + g) * VS;
+            T *vb = vecb + ((j & 1) * MPB + g) * VS;
             if (lc == jr) {
                 const T r = dinv[g * NP + j];
     #pragma unroll
                 for (int a = 0; a < E; ++a) {
                     p[a][jb] *= r;
-                    vb[lr * E + a] = p[a][jb];
+                    vb[lr * EP + a] = p[a][jb];
                 }
             }
             if (lr == jr) {
     #pragma unroll
                 for (int b = 0; b <= jb; ++b)
-                    rb[lc * E + b] = lw[jb][b];
+                    rb[lc * EP + b] = lw[jb][b];
             }
             __syncthreads();
             T u[E], lj[E];
     #pragma unroll
             for (int a = 0; a < E; ++a)
-                u[a] = vb[lr * E + a];           // V[lr + G a][j]
+                u[a] = vb[lr * EP + a];           // V[lr + G a][j]
     #pragma unroll
             for (int b = 0; b <= jb; ++b)
-                lj[b] = rb[lc * E + b];          // L[j][lc + G b]; zero right of j
+                lj[b] = rb[lc * EP + b];          // L[j][lc + G b]; zero right of j
             if (lc == jr)
                 lj[jb] = T(0);                   // the solved column itself
     #pragma unroll
@@ -476,25 +482,25 @@ k_potrf_adj_tile(int n, int64_t batch, const T *L, int64_t ldl, int64_t sL,
         for (int u_ = 0; u_ < G; ++u_) {
             const int ir = G - 1 - u_;
             const int i = ib * G + ir;
-            T *rb = rowb + ((i & 1) * MPB + g) * NP;
-            T *vb = vecb + ((i & 1) * MPB + g) * NP;
+            T *rb = rowb + ((i & 1) * MPB + g) * VS;
+            T *vb = vecb + ((i & 1) * MPB + g) * VS;
             if (lr == ir) {
                 const T r = dinv[g * NP + i];
     #pragma unroll
                 for (int b = 0; b <= ib; ++b) {
                     p[ib][b] *= r;
-                    vb[lc * E + b] = p[ib][b];
-                    rb[lc * E + b] = lw[ib][b];
+                    vb[lc * EP + b] = p[ib][b];
+                    rb[lc * EP + b] = lw[ib][b];
                 }
             }
             __syncthreads();
             T w[E], li[E];
     #pragma unroll
             for (int b = 0; b <= ib; ++b)
-                w[b] = vb[lc * E + b];           // Z[i][lc + G b]
+                w[b] = vb[lc * EP + b];           // Z[i][lc + G b]
     #pragma unroll
             for (int a = 0; a <= ib; ++a)
-                li[a] = rb[lr * E + a];          // L[i][lr + G a]; zero right of i
+                li[a] = rb[lr * EP + a];          // L[i][lr + G a]; zero right of i
             if (lr == ir)
                 li[ib] = T(0);                   // the solved row itself
     #pragma unroll
@@ -579,12 +585,12 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, T *Xo, int64_t ldx)
 {
-    constexpr int G = 16, E = 8, NP = G * E;
+    constexpr int G = 16, E = 8, EP = E + 1, VS = G * EP;
     // on the critical path of the factorisation, beside blocks of the trailing
     // update: its waves win instruction arbitration on their SIMDs
     __builtin_amdgcn_s_setprio(3);
-    __shared__ T colbuf[2 * NP];
-    __shared__ T rowbuf[2 * NP];
+    __shared__ T colbuf[2 * VS];
+    __shared__ T rowbuf[2 * VS];
     const int tid = threadIdx.x, lr = tid / G, lc = tid % G;
 
     T x[E][E], y[E][E];
@@ -605,22 +611,22 @@ k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t 
 #pragma unroll 1
         for (int jr = 0; jr < G; ++jr) {
             const int j = jb * G + jr;
-            T *cb = colbuf + (j & 1) * NP;
-            T *rb = rowbuf + (j & 1) * NP;
+            T *cb = colbuf + (j & 1) * VS;
+            T *rb = rowbuf + (j & 1) * VS;
             if (lc == jr) {
 #pragma unroll
                 for (int a = jb; a < E; ++a)
-                    cb[lr * E + a] = x[a][jb];
+                    cb[lr * EP + a] = x[a][jb];
             }
             __syncthreads();
-            const T d = cb[jr * E + jb];
+            const T d = cb[jr * EP + jb];
             T u[E], v[E];
 #pragma unroll
             for (int a = jb; a < E; ++a)
-                u[a] = cb[lr * E + a];
+                u[a] = cb[lr * EP + a];
 #pragma unroll
             for (int b = jb; b < E; ++b)
-                v[b] = cb[lc * E + b];
+                v[b] = cb[lc * EP + b];
             if (!(d > T(0)) && fail == 0)
                 fail = j + 1;
             T sq, rs;
@@ -647,14 +653,14 @@ k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t 
 #pragma unroll
                 for (int b = 0; b <= jb; ++b) {
                     y[jb][b] *= rs;
-                    rb[lc * E + b] = y[jb][b];
+                    rb[lc * EP + b] = y[jb][b];
                 }
             }
             __syncthreads();
             T w[E];
 #pragma unroll
             for (int b = 0; b <= jb; ++b)
-                w[b] = rb[lc * E + b];
+                w[b] = rb[lc * EP + b];
             // R_t -= L_tj X_j for rows t = lr + G a > j (u is zero elsewhere)
 #pragma unroll
             for (int a = jb; a < E; ++a) {

@@ -574,13 +574,15 @@ k_wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar, T *bbar,
 // ------------------------------------------------------------------------
 // Diagonal tile of the blocked factor with its inverse (one 128-edge tile per
 // 256-thread block, lane grid 16 x 16).  The inverse X = L^{-1} is built row
-// by row alongside the factor: after factor step j has published column j of
-// the trailing matrix, the lanes of row j of X scale it by 1 / L_jj and publish
-// it, and every row t > j takes R_t -= L_tj X_j, with L_tj already in
-// registers from the factor step.  No tile-sized LDS buffer is needed, so the
-// kernel fits beside the blocks of a running matrix-core product.  X is
-// written whole (n x n, zeros above its diagonal) to Xo, where the panel
-// solve of the blocked factorisation reads it as a plain operand.
+// by row alongside the factor: once L_jj is known, the lanes of row j of X
+// scale it by 1 / L_jj and publish it, and every row t > j takes
+// R_t -= L_tj X_j, with L_tj kept in registers from factor step j.  The
+// inverse runs one step behind the factor, so that the column of factor step
+// j and the row j-1 of X are published together and each step needs one
+// barrier.  No tile-sized LDS buffer is needed, so the kernel fits beside the
+// blocks of a running matrix-core product.  X is written whole (n x n, zeros
+// above its diagonal) to Xo, where the panel solve of the blocked
+// factorisation reads it as a plain operand.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t info_base, T *Xo, int64_t ldx)
@@ -605,6 +607,34 @@ k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t 
             y[a][b] = (i == k) ? T(1) : T(0);
         }
 
+    // row p of X (block pb, lane row pr): X_p = R_p / L_pp, published at the
+    // lane columns; after the barrier every row t > p takes R_t -= L_tp X_p
+    T lt[E];                  // L_tp for this lane's rows t = lr + G a (zero for t <= p)
+    T rs_p = T(0);            // 1 / L_pp
+#pragma unroll
+    for (int a = 0; a < E; ++a)
+        lt[a] = T(0);
+    auto publish_row = [&](int pb, int pr, T *rb) {
+        if (lr == pr) {
+#pragma unroll
+            for (int b = 0; b <= pb; ++b) {
+                y[pb][b] *= rs_p;
+                rb[lc * EP + b] = y[pb][b];
+            }
+        }
+    };
+    auto apply_row = [&](int pb, const T *rb) {
+        T w[E];
+#pragma unroll
+        for (int b = 0; b <= pb; ++b)
+            w[b] = rb[lc * EP + b];
+#pragma unroll
+        for (int a = pb; a < E; ++a)
+#pragma unroll
+            for (int b = 0; b <= pb; ++b)
+                y[a][b] -= lt[a] * w[b];
+    };
+
     int fail = 0;
 #pragma unroll
     for (int jb = 0; jb < E; ++jb) {
@@ -612,13 +642,22 @@ k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t 
         for (int jr = 0; jr < G; ++jr) {
             const int j = jb * G + jr;
             T *cb = colbuf + (j & 1) * VS;
-            T *rb = rowbuf + (j & 1) * VS;
+            T *rb = rowbuf + ((j + 1) & 1) * VS;   // row j - 1 of X
             if (lc == jr) {
 #pragma unroll
                 for (int a = jb; a < E; ++a)
                     cb[lr * EP + a] = x[a][jb];
             }
+            // row j - 1 of X: in block jb - 1 at lane row G - 1 when jr == 0
+            if (jr > 0)
+                publish_row(jb, jr - 1, rb);
+            else if (jb > 0)
+                publish_row(jb - 1, G - 1, rb);
             __syncthreads();
+            if (jr > 0)
+                apply_row(jb, rb);
+            else if (jb > 0)
+                apply_row(jb - 1, rb);
             const T d = cb[jr * EP + jb];
             T u[E], v[E];
 #pragma unroll
@@ -648,28 +687,18 @@ k_potrf_inv_tile(int n, T *W, int64_t ld, int32_t *info, int info_mode, int64_t 
                 for (int b = jb; b <= a; ++b)
                     x[a][b] -= ua * v[b];
             }
-            // row j of X: X_j = R_j / L_jj, published at the lane columns
-            if (lr == jr) {
+            // L_tj for the inverse step of row j (next iteration)
 #pragma unroll
-                for (int b = 0; b <= jb; ++b) {
-                    y[jb][b] *= rs;
-                    rb[lc * EP + b] = y[jb][b];
-                }
-            }
-            __syncthreads();
-            T w[E];
-#pragma unroll
-            for (int b = 0; b <= jb; ++b)
-                w[b] = rb[lc * EP + b];
-            // R_t -= L_tj X_j for rows t = lr + G a > j (u is zero elsewhere)
-#pragma unroll
-            for (int a = jb; a < E; ++a) {
-                const T ltj = u[a] * rs;
-#pragma unroll
-                for (int b = 0; b <= jb; ++b)
-                    y[a][b] -= ltj * w[b];
-            }
+            for (int a = jb; a < E; ++a)
+                lt[a] = u[a] * rs;
+            rs_p = rs;
         }
+    }
+    // the last row of X has no rows below it: only its scaling is left
+    if (lr == G - 1) {
+#pragma unroll
+        for (int b = 0; b < E; ++b)
+            y[E - 1][b] *= rs_p;
     }
 
     // L (lower triangle of the tile) and X (whole, to Xo)

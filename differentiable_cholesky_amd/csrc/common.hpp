@@ -49,6 +49,20 @@ __device__ __forceinline__ f4_t mfma16x16x4(float a, float b, f4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// acc += (NEG ? -a : a) b.  The f64 instruction carries negate modifiers for
+// its operands (its last field; neg:[1,0,0] negates a), so the negation costs
+// no vector instruction; in the f32 instruction that field selects a lane
+// broadcast instead, so a is negated by hand there.
+template <bool NEG>
+__device__ __forceinline__ d4_t mfma16x16x4_s(double a, double b, d4_t c)
+{
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, NEG ? 1 : 0);
+}
+template <bool NEG>
+__device__ __forceinline__ f4_t mfma16x16x4_s(float a, float b, f4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(NEG ? -a : a, b, c, 0, 0, 0);
+}
 
 // ------------------------------------------------------ launch checking ----
 // The HIP error behind the most recent CHOL_ERR_HIP (process-wide, for

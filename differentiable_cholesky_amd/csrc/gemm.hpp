@@ -284,11 +284,8 @@ __device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], co
         const int kr = kk + lane / 16;
         T af[4], bf[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
             af[i] = SA[kr * PITCH + wm * 64 + i * 16 + lane % 16];
-            if (NEG)
-                af[i] = -af[i];
-        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             bf[j] = SB[kr * PITCH + wn * 64 + j * 16 + lane % 16];
@@ -296,7 +293,7 @@ __device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], co
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = mfma16x16x4(af[i], bf[j], acc[i][j]);
+                acc[i][j] = mfma16x16x4_s<NEG>(af[i], bf[j], acc[i][j]);
     }
 }
 

@@ -98,6 +98,14 @@ __device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim
 template <typename T> struct Vec8 { T v[8]; };
 enum { LAY_MK = 0, LAY_KM = 1 };
 
+// LDS pitch of a chunk staged on the 16-byte path with layout LAY.  fp64
+// row-panel chunks (LAY_MK) take an odd pitch: a wave's 8-byte writes then
+// fall on distinct banks in every group of 16 lanes (with the even pitch,
+// lanes whose k differs by 8 collided); k-major chunks keep the even pitch
+// their 16-byte writes need.
+template <typename T, int LAY> struct LayPitch { static constexpr int v = Pitch<T>::v; };
+template <> struct LayPitch<double, LAY_MK> { static constexpr int v = 129; };
+
 // staging layouts an operand kind can use on the 16-byte path
 constexpr bool can_lay(int op, int lay)
 {
@@ -191,7 +199,7 @@ struct Operand {
                 MP::mk(tid, j, m, k);
             else
                 MP::km(tid, j, m, k);
-            S[k * Pitch<T>::v + m] = r.v[j];
+            S[k * LayPitch<T, LAY>::v + m] = r.v[j];
         }
     }
 
@@ -273,22 +281,22 @@ __device__ __forceinline__ int xcd_tile(int b, int nt)
 
 namespace gemm_detail {
 
-// acc += (NEG ? -A : B) over one chunk staged at SA (A) and SB (B) in LDS
-template <typename T, bool NEG>
+// acc += (NEG ? -A : B) over one chunk staged at SA (A, pitch PA) and SB (B,
+// pitch PB) in LDS
+template <typename T, bool NEG, int PA = Pitch<T>::v, int PB = Pitch<T>::v>
 __device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], const T *SA, const T *SB, int lane,
                                           int wm, int wn)
 {
-    constexpr int PITCH = Pitch<T>::v;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 4) {
         const int kr = kk + lane / 16;
         T af[4], bf[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            af[i] = SA[kr * PITCH + wm * 64 + i * 16 + lane % 16];
+            af[i] = SA[kr * PA + wm * 64 + i * 16 + lane % 16];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            bf[j] = SB[kr * PITCH + wn * 64 + j * 16 + lane % 16];
+            bf[j] = SB[kr * PB + wn * 64 + j * 16 + lane % 16];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -323,7 +331,7 @@ __device__ __forceinline__ void mma_run(typename Acc<T>::type (&acc)[4][4], cons
     for (int c = 0; c < nc; ++c) {
         const T *S = lds + (c & 1) * 2 * SZ;
         T *D = lds + ((c + 1) & 1) * 2 * SZ;
-        chunk_mma<T, NEG>(acc, S, S + SZ, lane, wm, wn);                   // chunk c
+        chunk_mma<T, NEG, LayPitch<T, LA>::v, LayPitch<T, LB>::v>(acc, S, S + SZ, lane, wm, wn);                   // chunk c
         Operand<T, AOP>::template stash_lay<LA>(a, D, tid);                // chunk c+1
         Operand<T, BOP>::template stash_lay<LB>(b, D + SZ, tid);
         A.template fetch_fast<LA>(a, tid, kc(c + 2));
@@ -358,7 +366,7 @@ __device__ __forceinline__ void mma_run2(typename Acc<T>::type (&acc)[4][4], con
     T *const L0 = lds, *const L1 = lds + 2 * SZ;
     for (int c = 0; c < nc; c += 2) {
         // chunk c from L0; chunk c+1 (a1, b) into L1; a1 <- chunk c+3
-        chunk_mma<T, NEG>(acc, L0, L0 + SZ, lane, wm, wn);
+        chunk_mma<T, NEG, LayPitch<T, LA>::v, LayPitch<T, LB>::v>(acc, L0, L0 + SZ, lane, wm, wn);
         Operand<T, AOP>::template stash_lay<LA>(a1, L1, tid);
         Operand<T, BOP>::template stash_lay<LB>(b, L1 + SZ, tid);
         A.template fetch_fast<LA>(a1, tid, kc(c + 3));
@@ -366,7 +374,7 @@ __device__ __forceinline__ void mma_run2(typename Acc<T>::type (&acc)[4][4], con
         __syncthreads();
         // chunk c+1 from L1; chunk c+2 (a0, b) into L0; a0 <- chunk c+4
         if (c + 1 < nc)
-            chunk_mma<T, NEG>(acc, L1, L1 + SZ, lane, wm, wn);
+            chunk_mma<T, NEG, LayPitch<T, LA>::v, LayPitch<T, LB>::v>(acc, L1, L1 + SZ, lane, wm, wn);
         Operand<T, AOP>::template stash_lay<LA>(a0, L0, tid);
         Operand<T, BOP>::template stash_lay<LB>(b, L0 + SZ, tid);
         A.template fetch_fast<LA>(a0, tid, kc(c + 4));

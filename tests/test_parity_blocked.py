@@ -95,6 +95,33 @@ def test_blocked_in_place_matches_out_of_place_bitwise():
     assert np.array_equal(np.tril(host(b)), np.tril(g0))
 
 
+def test_blocked_repeatable_bitwise():
+    # n = 6000: the far-triangle updates take several rounds of tiles from the
+    # persistent grid and the symmetric products are split over the
+    # contraction; tiles go to whichever block asks first, but every sum is
+    # formed in a fixed order, so two runs agree to the bit
+    n = 6000
+    A = workloads.gram_spd(n, seed=21, shift=1.0, device="cuda")
+    L1, i1 = dc().chol_potrf(A, nb=128)
+    L2, i2 = dc().chol_potrf(A, nb=128)
+    torch.cuda.synchronize()
+    assert int(i1.item()) == 0 and int(i2.item()) == 0
+    assert torch.equal(L1, L2)
+    anorm = A.norm().item() / np.sqrt(n)
+    for i in (0, n // 2, n - 1):
+        r = (L1[i:i + 1, :] @ L1.T - A[i:i + 1, :]).norm().item() / anorm
+        assert r <= 1e-13, (i, r)
+    adjL = torch.from_numpy(workloads.lower_normal(n, seed=22)).cuda()
+    G1 = dc().chol_potrf_adjoint(L1, adjL, accumulate=False, nb=128)
+    G2 = dc().chol_potrf_adjoint(L1, adjL, accumulate=False, nb=128)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.tril(G1), torch.tril(G2))
+    # adj_L = L gives I / 2 at any size
+    G = dc().chol_potrf_adjoint(L1, L1, accumulate=False, nb=128)
+    assert (G.diagonal() - 0.5).abs().max().item() <= 0.5e-10
+    assert torch.tril(G, -1).abs().max().item() <= 0.5e-10
+
+
 def test_blocked_leading_dimension():
     n, ld = 300, 333
     A = workloads.gram_spd(n, seed=14)

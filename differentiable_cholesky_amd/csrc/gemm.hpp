@@ -548,29 +548,63 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
     // so the epilogue is a plain store and no accumulator has to leave the
     // matrix-core registers for a read-modify-write.
     constexpr bool FROM_C = (CM == C_SUB || CM == C_SUB_LOWER);
+    // a tile inside M x N needs no per-entry bounds test: its loads of C and
+    // its stores are issued back to back, without a branch around each one
+    const bool interior = r0 + BM <= p.M && c0 + BN <= p.N;
     acc_t acc[4][4];
+    if (FROM_C && interior) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                T x = T(0);
-                if (FROM_C) {
+                for (int v = 0; v < 4; ++v) {
                     int row, col;
                     acc_pos<T>(i, j, v, row, col);
-                    row += r0;
-                    col += c0;
-                    if (row < p.M && col < p.N)
-                        x = p.c[(int64_t)row * p.ldc + col];
+                    acc[i][j][v] = p.c[(int64_t)(row + r0) * p.ldc + col + c0];
                 }
-                acc[i][j][v] = x;
-            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    T x = T(0);
+                    if (FROM_C) {
+                        int row, col;
+                        acc_pos<T>(i, j, v, row, col);
+                        row += r0;
+                        col += c0;
+                        if (row < p.M && col < p.N)
+                            x = p.c[(int64_t)row * p.ldc + col];
+                    }
+                    acc[i][j][v] = x;
+                }
+    }
 
     Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
     Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec, 0};
     tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, kbeg, kend, lds);
 
+    if (interior && (CM != C_SUB_LOWER || I > J)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    int row, col;
+                    acc_pos<T>(i, j, v, row, col);
+                    row += r0;
+                    col += c0;
+                    if (CM == C_PARTIAL)
+                        p.part[(int64_t)split * p.M * p.N + (int64_t)row * p.N + col] = acc[i][j][v];
+                    else
+                        p.c[(int64_t)row * p.ldc + col] = acc[i][j][v];
+                }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -363,6 +363,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
 //                                           update per 128-row tile of its panel, plus the
 //                                           slot the tile adjoint adds
 //   [part_c: 2 * nb * nb]                   the tile adjoint's scratch tiles
+//   [dense : K * nb * nb]                   Sym(G) of every diagonal tile, whole (nb = 128)
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // partials of the diagonal update: one per 128-row tile of the longest panel
 static inline int64_t panel_tiles(int64_t n) { return (n + 127) / 128; }
@@ -378,6 +379,7 @@ size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
     s += align256((size_t)SIDE_SPLIT_MAX * n * nb * esize);
     s += align256((size_t)(panel_tiles(n) + 1) * nb * nb * esize);
     s += align256((size_t)2 * nb * nb * esize);
+    s += align256((size_t)K * nb * nb * esize);
     return s;
 }
 
@@ -388,8 +390,8 @@ size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
 // in a fixed order, so the result does not depend on scheduling.
 template <typename T>
 static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, const T *B, int64_t ldb, T *C,
-                               int64_t ldc, int excl, T *part, int max_splits, int min_chunk, int *sched,
-                               int cap, double flops, hipStream_t st)
+                               int64_t ldc, int excl, const T *dg, T *part, int max_splits, int min_chunk,
+                               int *sched, int cap, double flops, hipStream_t st)
 {
     if (M <= 0 || N <= 0 || K <= 0)
         return CHOL_OK;
@@ -426,6 +428,7 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
     p.sched = sched;
     p.cap = cap;
     p.excl = excl;
+    p.dg = dg;
     {
         prof::Scope ps(CHOL_K_ADJ_TRAILING, st, flops);
         chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st);
@@ -448,7 +451,9 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
 //   V = Psi Linv              into s2
 //   Z = Linv^T V              G = Phi(Z) into Wb (lower); Z is symmetric, and
 //                             Sym(G) = G + G^T (lower part of Z mirrored) goes
-//                             whole into s1
+//                             whole into sg (the tile's dense copy, which the
+//                             symmetric products of later tile columns read
+//                             as their diagonal block)
 // and, when `slot` is given, the one term of the previous tile column's
 // trailing-update adjoint that needs G:  slot = Sym(G) Lnext  (kb x nj, row
 // major), with Lnext = L[this tile's rows, previous tile column].
@@ -467,7 +472,7 @@ __device__ __forceinline__ int vec_ok(const T *p, int64_t ld)
 template <typename T>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv, int64_t ldi, T *s1, T *s2,
-               int64_t lds_scr, const T *Lnext, int nj, T *slot)
+               int64_t lds_scr, const T *Lnext, int nj, T *slot, T *sg, int64_t ldsg)
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
@@ -484,8 +489,9 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = acc_t{0, 0, 0, 0};
     };
-    // the lower part of the accumulated (symmetric) block mirrored whole into s1
-    auto mirror_to_s1 = [&]() {
+    // the lower part of the accumulated (symmetric) block mirrored whole into
+    // dst (leading dimension ldd)
+    auto mirror_to = [&](T *dst, int64_t ldd) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -495,8 +501,8 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
                     int r, c;
                     acc_pos<T>(i, j, v, r, c);
                     if (r < kb && c <= r) {
-                        s1[(int64_t)r * lds_scr + c] = acc[i][j][v];
-                        s1[(int64_t)c * lds_scr + r] = acc[i][j][v];
+                        dst[(int64_t)r * ldd + c] = acc[i][j][v];
+                        dst[(int64_t)c * ldd + r] = acc[i][j][v];
                     }
                 }
     };
@@ -509,7 +515,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
         Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, 0};
         tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
     }
-    mirror_to_s1();
+    mirror_to(s1, lds_scr);
     __threadfence_block();
     __syncthreads();
     // stage 2: V = Psi Linv; A(r, t) = Psi[r][t], B(t, c) = Linv[t][c]
@@ -552,13 +558,13 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
             }
     if (!slot)
         return;
-    mirror_to_s1();
+    mirror_to(sg, ldsg);
     __threadfence_block();
     __syncthreads();
     // stage 4: slot = Sym(G) Lnext; A(r, t) = Sym(G)[r][t], B(t, c) = Lnext[t][c]
     zero();
     {
-        Operand<T, OP_MK> A{s1, lds_scr, 0, kb, vs};
+        Operand<T, OP_MK> A{sg, ldsg, 0, kb, vec_ok(sg, ldsg)};
         Operand<T, OP_KM> B{Lnext, ldl, 0, nj, vs && vec_ok(Lnext, ldl)};
         tile_mma<T, OP_MK, OP_KM, false, PATH_MIXED>(acc, A, B, 0, kb, lds);
     }
@@ -615,6 +621,10 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
     T *part_b = (T *)w;
     w += align256((size_t)(panel_tiles(n) + 1) * nb * nb * sizeof(T));
     T *part_c = (T *)w;
+    w += align256((size_t)2 * nb * nb * sizeof(T));
+    // dense Sym(G) per diagonal tile: the symmetric products read their
+    // diagonal blocks from it when the tile is the product's 128-wide tile
+    T *dense = nb == 128 ? (T *)w : nullptr;
     T *slot = part_b + panel_tiles(n) * nb * nb;   // Sym(G(k)) L[tile k, tile k-1]
 
     if ((const T *)Wb != adjL) {
@@ -693,18 +703,20 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         {
             prof::Scope ps(CHOL_K_ADJ_DIAG, sc, 2.0 * kb * kb * kb / 3 + (k >= 1 ? 2.0 * kb * kb * nb : 0.0));
             const T *Lnext = (k >= 1) ? L + k0 * ldl + j0 : nullptr;
+            T *sg = dense ? dense + k * nb * nb : part_c;
             hipLaunchKernelGGL((k_tile_adjoint<T>), dim3(1), dim3(256), 0, sc, kb, Lkk, ldl, Wkk, ldw, invk,
                                (int64_t)nb, part_c, part_c + (int64_t)nb * nb, (int64_t)nb, Lnext, nb,
-                               k >= 1 ? slot : (T *)nullptr);
+                               k >= 1 ? slot : (T *)nullptr, sg, (int64_t)nb);
             CHOL_LAUNCH_CHECK();
         }
         // first term of tile column k-1: rows and columns from tile column k on,
         // the block Wb_kk left out
         if (k >= 1 && m > 0) {
             const double flops = 2.0 * nb * ((double)(m + kb) * (m + kb) - (double)kb * kb);
+            const T *dg = dense ? dense + k * nb * nb : nullptr;   // diagonal tiles from tile k on
             if ((s = sym_product<T>((int)(m + kb), nb, (int)(m + kb), Wkk, ldw, L + k0 * ldl + j0, ldl,
-                                    Wb + k0 * ldw + j0, ldw, kb, part_x, SIDE_SPLIT_MAX, 128, sched_x, cap_x,
-                                    flops, sx)) != CHOL_OK)
+                                    Wb + k0 * ldw + j0, ldw, kb, dg, part_x, SIDE_SPLIT_MAX, 128, sched_x,
+                                    cap_x, flops, sx)) != CHOL_OK)
                 return s;
         }
     }

@@ -53,6 +53,10 @@ template <typename T> struct GemmArgs {
     int *sched;          // non-null: blocks take (split, tile) items from this
                          // device counter pair (item, finished blocks), which
                          // must be zero at launch and is zero again afterwards
+    const T *dg;         // OP_SYM A operand, optional: the symmetric 128 x 128
+                         // diagonal blocks written whole (block I at dg + I*128*128,
+                         // row-major), read on the 16-byte path instead of
+                         // assembling them from the lower triangle element by element
 };
 
 namespace gemm_detail {
@@ -585,7 +589,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
 
     Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
     Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec, 0};
-    tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, kbeg, kend, lds);
+    bool done = false;
+    if constexpr (AOP == OP_SYM && BOP == OP_KM && PATH == PATH_MIXED) {
+        // the tile's diagonal block [r0, r0 + 128) of the contraction, when it
+        // is whole, not left out and within [kbeg, kend): a plain row panel of
+        // its dense copy against B's rows shifted by r0; the parts left and
+        // right of it hold no diagonal crossing
+        const int d0 = max(kbeg, r0), d1 = min(kend, r0 + BM);
+        if (p.dg && p.vec && r0 + BM <= p.M && r0 >= p.excl && d0 < d1) {
+            if (d0 > kbeg)
+                tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, kbeg, d0, lds);
+            Operand<T, OP_MK> D{p.dg + (int64_t)I * BM * BM, BM, 0, BM, 1, 0};
+            Operand<T, OP_KM> B2{p.b + (int64_t)r0 * p.ldb, p.ldb, c0, p.N, p.vec, 0};
+            tile_runs<T, OP_MK, OP_KM, FROM_C>(acc, D, B2, d0 - r0, d1 - r0, d1 - r0, lds);
+            if (kend > d1)
+                tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, d1, kend, lds);
+            done = true;
+        }
+    }
+    if (!done)
+        tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, kbeg, kend, lds);
 
     if (interior && (CM != C_SUB_LOWER || I > J)) {
 #pragma unroll

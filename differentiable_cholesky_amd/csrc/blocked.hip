@@ -233,7 +233,8 @@ static inline int split_chunk(int64_t K, int splits)
 // Two library streams: `sx` runs every kernel that spans the matrix (panel
 // solves and trailing updates) in order; `sc` runs only the one-block kernels
 // of the next tile column (diagonal factor and its inverse), beside the wide
-// update that follows it on sx.  The order of the launches, the deferred
+// update that follows it on sx (where no such update is left, the factor
+// runs on sx itself).  The order of the launches, the deferred
 // trailing update and the joins between the streams are the host-side plan of
 // plan.cpp; this executor launches that plan as it stands.
 template <typename T>
@@ -288,9 +289,10 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             const int64_t k0 = o.k * nb;
             const int kb = (int)std::min<int64_t>(nb, n - k0);
             const double kb3 = (double)kb * kb * kb;
-            prof::Scope ps(CHOL_K_DIAG_FACTOR, sc, o.slot >= 0 ? 2 * kb3 / 3 : kb3 / 3);
+            hipStream_t ds = o.stream == FWD_WIDE ? sx : sc;
+            prof::Scope ps(CHOL_K_DIAG_FACTOR, ds, o.slot >= 0 ? 2 * kb3 / 3 : kb3 / 3);
             s = diag_potrf<T>(kb, L + k0 * ldl + k0, ldl, info, o.k == 0 ? 1 : 2, k0,
-                              o.slot >= 0 ? slot_ptr(o.slot) : nullptr, MAX_TILE, sc);
+                              o.slot >= 0 ? slot_ptr(o.slot) : nullptr, MAX_TILE, ds);
             break;
         }
         case FWD_PANEL: {

@@ -17,7 +17,9 @@ namespace chol {
 //   j > 0:  tile columns k+1 .. g+DEFER receive panel k;
 //   then the chain stream factors tile column k+1 while the wide stream
 //   updates part j of DEFER of the group's far triangle (right of tile column
-//   g+DEFER) with the same panels as step g.
+//   g+DEFER) with the same panels as step g; where that part is empty, the
+//   wide stream factors tile column k+1 itself, after the narrow update,
+//   and the two joins around the factor are left out.
 // The far triangle's tiles are taken by `slots` persistent blocks, each tile
 // the same long product (DEFER*nb deep), so a launch lasts a whole number of
 // rounds of tiles however few tiles its last round holds.  The parts are
@@ -37,8 +39,8 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
         return ops.back();
     };
     const int64_t K = (n + nb - 1) / nb;
-    auto diag = [&](int64_t k) {
-        FwdOp &o = op(FWD_DIAG, FWD_CHAIN);
+    auto diag = [&](int64_t k, int stream) {
+        FwdOp &o = op(FWD_DIAG, stream);
         o.k = k;
         o.slot = (k * nb + std::min<int64_t>(nb, n - k * nb) < n) ? (int)(k & 1) : -1;
     };
@@ -48,16 +50,18 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
     };
     if (copy)
         op(FWD_COPY, FWD_CHAIN);
-    diag(0);
+    diag(0, FWD_CHAIN);
     // the far triangle of the current group: first column, panels, tile count
     int64_t fcol = -1, ff = 0;
     int fnp = 0, ftiles = 0;
+    bool diag_wide = false;   // the last diagonal tile was factored on the wide stream
     for (int64_t k = 0; k < K; ++k) {
         const int64_t k0 = k * nb;
         const int64_t r0 = k0 + std::min<int64_t>(nb, n - k0), m = n - r0;
         if (m == 0)
             break;
-        op(FWD_JOIN, FWD_WIDE).slot = 0;
+        if (!diag_wide)
+            op(FWD_JOIN, FWD_WIDE).slot = 0;
         {
             FwdOp &o = op(FWD_PANEL, FWD_WIDE);
             o.k = k;
@@ -73,8 +77,6 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
             o.f = f;
             o.np = np;
         }
-        op(FWD_JOIN, FWD_CHAIN).slot = 1;
-        diag(k + 1);
         if (j == 0) {
             fcol = r0 + (int64_t)FWD_DEFER * nb;
             if (fcol < n) {
@@ -85,6 +87,7 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
                 fcol = -1;
             }
         }
+        int t0 = 0, t1 = 0;
         if (fcol >= 0) {
             auto cut = [&](int q) -> int {
                 if (slots <= 0)
@@ -92,18 +95,27 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
                 const int64_t rounds = ((int64_t)ftiles + slots - 1) / slots;
                 return (int)std::min<int64_t>(ftiles, rounds * q / FWD_DEFER * slots);
             };
-            const int t0 = cut(j), t1 = cut(j + 1);
-            if (t1 > t0) {
-                FwdOp &o = op(FWD_TRI, FWD_WIDE);
-                o.c = fcol;
-                o.f = ff;
-                o.np = fnp;
-                o.t0 = t0;
-                o.tn = t1 - t0;
-            }
-            if (j == FWD_DEFER - 1)
-                fcol = -1;
+            t0 = cut(j);
+            t1 = cut(j + 1);
         }
+        if (t1 > t0) {
+            op(FWD_JOIN, FWD_CHAIN).slot = 1;
+            diag(k + 1, FWD_CHAIN);
+            FwdOp &o = op(FWD_TRI, FWD_WIDE);
+            o.c = fcol;
+            o.f = ff;
+            o.np = fnp;
+            o.t0 = t0;
+            o.tn = t1 - t0;
+            diag_wide = false;
+        } else {
+            // nothing to run beside the diagonal factor: it follows the
+            // narrow update on the wide stream, with no join either way
+            diag(k + 1, FWD_WIDE);
+            diag_wide = true;
+        }
+        if (fcol >= 0 && j == FWD_DEFER - 1)
+            fcol = -1;
     }
     op(FWD_JOIN, FWD_CHAIN).slot = 1;
     op(FWD_ZERO_UPPER, FWD_CHAIN);

@@ -14,7 +14,8 @@ namespace chol {
 
 enum FwdKind {
     FWD_COPY = 0,        // chain: lower triangle of A into L
-    FWD_DIAG = 1,        // chain: factor tile column k's diagonal tile; slot >= 0: its inverse into slot
+    FWD_DIAG = 1,        // chain (or wide, with nothing beside it): factor tile column k's diagonal
+                         // tile; slot >= 0: its inverse into slot
     FWD_PANEL = 2,       // wide: panel solve of tile column k (rows below its tile), reading slot
     FWD_UPDATE = 3,      // wide: lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T, Q = panels f .. f+np-1
     FWD_TRI = 4,         // wide: lower tiles t0 .. t0+tn-1 (128 x 128, row-major) of W[c:, c:] -= Q Q^T

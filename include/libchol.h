@@ -217,8 +217,9 @@ int chol_abi_version(void);
  *   ops  [out] host, cap rows of CHOL_PLAN_FIELDS int64 each (may be NULL if
  *              cap == 0), one row per operation in enqueue order:
  *     kind    0 copy lower(A) into L (chain stream)
- *             1 factor diagonal tile k (chain); slot >= 0: its inverse is
- *               written whole into inverse slot `slot`
+ *             1 factor diagonal tile k (chain stream, or wide where no
+ *               far-triangle part runs beside it); slot >= 0: its inverse
+ *               is written whole into inverse slot `slot`
  *             2 panel solve of tile column k below its diagonal tile (wide
  *               stream), reading inverse slot `slot`
  *             3 lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T with Q the

@@ -154,62 +154,187 @@ def test_blocked_info_resets_on_success():
 
 # --------------------------------------------------- full benchmark sizes ----
 
-def _full_size_checks(n, shift, nb):
-    """Factor and adjoint at full size, checked on what the oracle can compute
-    independently: the leading m x m block (chol of A's leading block), sampled
-    rows i (last row of chol of the principal submatrix on {0..m-1, i}), a
-    sampled residual, and the adjoint identities adj_L = L => I/2 and
-    adj_L = tril(2 W L) => Phi(2 W), plus the leading-block adjoint."""
-    A = workloads.gram_spd(n, seed=workloads.SEED_MATRIX, shift=shift, device="cuda")
-    L, info = dc().chol_potrf(A, nb=nb)
-    torch.cuda.synchronize()
-    assert int(info.item()) == 0
-    m = 768
-    Ah = A[:m, :m].cpu().numpy()
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gpu_residual(L, A):
+    """||L L^T - A||_F / ||A||_F on the device (plain torch fp64 products)."""
+    R = torch.tril(L) @ torch.tril(L).T
+    R -= A
+    return (R.norm() / A.norm()).item()
+
+
+def _vjp_identity(L, adjL, G, seeds):
+    """Defining property of the adjoint, at any size: for a lower-triangular
+    direction E (symmetric perturbation E + strict(E)^T of A), the forward
+    derivative of L is dL = L Phi(L^{-1} (E + strict(E)^T) L^{-T}), and
+    <adj_L, dL> must equal sum_{i>=j} G_ij E_ij.  Computed with torch's fp64
+    triangular solves and products on the device; returns the relative
+    mismatches."""
+    out = []
+    n = L.shape[0]
+    for s in seeds:
+        g = torch.Generator(device="cpu").manual_seed(s)
+        E = torch.tril(torch.randn(n, n, generator=g, dtype=torch.float64)).to(L.device)
+        Es = E + torch.tril(E, -1).T
+        Y = torch.linalg.solve_triangular(L, Es, upper=False)            # L^{-1} Es
+        Z = torch.linalg.solve_triangular(L, Y.T.contiguous(), upper=False).T   # L^{-1} Es L^{-T}
+        del Y, Es
+        Z = torch.tril(Z)
+        Z.diagonal().mul_(0.5)
+        dL = L @ Z
+        del Z
+        lhs = (torch.tril(adjL) * dL).sum().item()
+        rhs = (torch.tril(G) * E).sum().item()
+        out.append(abs(lhs - rhs) / max(abs(lhs), 1e-300))
+        del dL, E
+    return out
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_cfg_fp64_n8192_full_elementwise():
+    """fp64 8192 x 8192, A = G G^T / 8192 + I (seed 0), adj_L = tril(N(0,1))
+    (seed 1): the whole factor and the whole lower adjoint against the oracle,
+    for the 128 tile and for a ragged 96 tile (8192 = 85 * 96 + 32).  The
+    adjoint's input is the oracle's own factor, so that both tile sizes are
+    compared with one oracle adjoint."""
+    n = 8192
+    A = workloads.gram_spd(n, seed=workloads.SEED_MATRIX, shift=1.0, device="cuda")
+    Ah = A.cpu().numpy()
+    _say(f"  n={n}: oracle factor")
     Lo, io = oracle.potrf(Ah)
     assert io == 0
-    assert_close(L[:m, :m].cpu().numpy(), Lo, 1e-10, "leading block")
-    rng = np.random.default_rng(1)
-    rows = np.sort(rng.choice(np.arange(m, n), size=6, replace=False))
-    for i in rows:
-        idx = np.r_[np.arange(m), i]
-        Asub = A[idx][:, idx].cpu().numpy()
-        Ls, _ = oracle.potrf(Asub)
-        assert_close(L[i, :m].cpu().numpy()[None, :], Ls[m, :m][None, :], 1e-10, f"row {i}")
-    # sampled residual rows: (L L^T)[i, :] vs A[i, :], scaled by the mean row norm of A
-    anorm = A.norm().item() / np.sqrt(n)
-    for i in list(rows) + [n - 1]:
-        li = L[i:i + 1, :]
-        r = (li @ L.T - A[i:i + 1, :]).norm().item() / anorm
-        assert r <= 1e-13, (i, r)
+    adjL_h = workloads.lower_normal(n, seed=workloads.SEED_ADJ)
+    _say(f"  n={n}: oracle adjoint")
+    Go = oracle.potrf_adjoint(Lo, adjL_h, accumulate=False)
+    Lo_d = dev(Lo)
+    adjL = dev(adjL_h)
+    for nb in (128, 96):
+        _say(f"  n={n} nb={nb}: GPU factor + adjoint")
+        L, info = dc().chol_potrf(A, nb=nb)
+        torch.cuda.synchronize()
+        assert int(info.item()) == 0
+        Lh = L.cpu().numpy()
+        assert_close(Lh, Lo, 1e-10, f"L nb={nb}")
+        assert np.all(np.triu(Lh, 1) == 0)
+        assert _gpu_residual(L, A) <= 1e-13
+        del L
+        G = dc().chol_potrf_adjoint(Lo_d, adjL, torch.zeros_like(A), accumulate=True, nb=nb)
+        Gh = np.tril(host(G))
+        assert np.all(np.triu(host(G), 1) == 0)
+        assert_close(Gh, np.tril(Go), 1e-10, f"adj_A nb={nb}")
+        del G
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_cfg_fp64_n16384_leading_block_and_identities():
+    """fp64 16384 x 16384, A = G G^T / 16384 + 0.1 I (seed 0).  The oracle at
+    this size takes too long, so the factor is compared with it on the leading
+    8192 block (the leading block of L is the factor of A's leading block) and
+    on sampled rows (row i of L restricted to columns < m is the last row of
+    the factor of the principal submatrix on {0..m-1, i}); the residual is
+    taken whole.  The adjoint is compared with the oracle for adj_L supported
+    on the leading 8192 block (G is then that block's own adjoint and zero
+    elsewhere), and for the benchmark's dense adj_L through the adjoint's
+    defining identity and two exact identities (adj_L = L gives I/2;
+    adj_L = tril(2 W L) gives Phi(2 W))."""
+    n, m = 16384, 8192
+    A = workloads.gram_spd(n, seed=workloads.SEED_MATRIX, shift=0.1, device="cuda")
+    _say(f"  n={n}: GPU factor")
+    L, info = dc().chol_potrf(A, nb=128)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
     assert torch.all(torch.triu(L, 1) == 0).item()
-    # adjoint identities at full size (tolerance 1e-10 relative to max|expected|)
-    G = dc().chol_potrf_adjoint(L, L, accumulate=False, nb=nb)
+    assert _gpu_residual(L, A) <= 1e-13
+    _say(f"  n={n}: oracle factor of the leading {m} block")
+    Lo, io = oracle.potrf(A[:m, :m].cpu().numpy())
+    assert io == 0
+    assert_close(L[:m, :m].cpu().numpy(), Lo, 1e-10, "leading block")
+    del Lo
+    ms = 768
+    rows = np.sort(np.random.default_rng(1).choice(np.arange(ms, n), size=6, replace=False))
+    for i in rows:
+        idx = np.r_[np.arange(ms), i]
+        Ls, _ = oracle.potrf(A[idx][:, idx].cpu().numpy())
+        assert_close(L[i, :ms].cpu().numpy()[None, :], Ls[ms, :ms][None, :], 1e-10, f"row {i}")
+    # adj_L on the leading block
+    _say(f"  n={n}: adjoint, adj_L on the leading {m} block")
+    small = workloads.lower_normal(m, seed=workloads.SEED_ADJ)
+    adjL = torch.zeros_like(L)
+    adjL[:m, :m] = dev(small)
+    G = dc().chol_potrf_adjoint(L, adjL, accumulate=False, nb=128)
+    torch.cuda.synchronize()
+    Gh = torch.tril(G[:m, :m]).cpu().numpy()
+    assert torch.tril(G)[m:, :].abs().max().item() == 0.0
+    del G
+    _say(f"  n={n}: oracle adjoint of the leading block")
+    Go = oracle.potrf_adjoint(L[:m, :m].cpu().numpy(), small, accumulate=False)
+    assert_close(Gh, Go, 1e-10, "leading-block adjoint")
+    del Gh, Go
+    # the benchmark's dense adj_L: the defining identity of the adjoint
+    _say(f"  n={n}: dense adj_L, adjoint identity")
+    adjL = dev(workloads.lower_normal(n, seed=workloads.SEED_ADJ))
+    G = dc().chol_potrf_adjoint(L, adjL, torch.zeros_like(L), accumulate=True, nb=128)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(G)).item()
+    mism = _vjp_identity(L, adjL, G, seeds=(11, 12))
+    assert max(mism) <= 1e-10, mism
+    del G, adjL
+    # exact identities
+    G = dc().chol_potrf_adjoint(L, L, accumulate=False, nb=128)
     assert (G.diagonal() - 0.5).abs().max().item() <= 0.5e-10
     assert torch.tril(G, -1).abs().max().item() <= 0.5e-10
     p, q = n - 3, n // 3
     adjL = torch.zeros_like(L)
     adjL[p, :] = 2.0 * L[q, :]
     adjL[q, :q + 1] = 2.0 * L[p, :q + 1]
-    G = dc().chol_potrf_adjoint(L, adjL, accumulate=False, nb=nb)
+    G = dc().chol_potrf_adjoint(L, adjL, accumulate=False, nb=128)
     assert abs(G[p, q].item() - 2.0) <= 2e-10
     G[p, q] = 0.0
     assert torch.tril(G).abs().max().item() <= 2e-10
-    # adj_L supported on the leading block: G is the leading block's own adjoint
-    adjL.zero_()
-    small = workloads.lower_normal(m, seed=workloads.SEED_ADJ)
-    adjL[:m, :m] = torch.from_numpy(small).cuda()
-    G = dc().chol_potrf_adjoint(L, adjL, accumulate=False, nb=nb)
-    Go = oracle.potrf_adjoint(L[:m, :m].cpu().numpy(), small, accumulate=False)
-    assert_close(torch.tril(G[:m, :m]).cpu().numpy(), Go, 1e-10, "leading-block adjoint")
-    assert torch.tril(G)[m:, :].abs().max().item() == 0.0
 
 
 @pytest.mark.slow
-def test_cfg_fp64_n8192_full_size():
-    _full_size_checks(8192, 1.0, 128)
+@pytest.mark.timeout(600)
+def test_multi_launch_far_triangle_elementwise():
+    """n = 5000, nb = 128: the far triangle of a group is cut into several
+    persistent launches (checked on the executor's own plan); the whole factor
+    and the whole adjoint (dense adj_L) are compared with the oracle."""
+    n = 5000
+    plan = dc().chol_potrf_plan(n, 128, copy=True, slots=2 * (torch.cuda.get_device_properties(0).multi_processor_count - 16))
+    tri = plan[plan[:, 0] == 4]
+    per_group = {}
+    for r in tri:
+        per_group[(int(r[3]), int(r[5]))] = per_group.get((int(r[3]), int(r[5])), 0) + 1
+    assert max(per_group.values()) >= 2, per_group
+    A = workloads.gram_spd(n, seed=n, shift=1.0)
+    L, info = dc().chol_potrf(dev(A), nb=128)
+    Lh = host(L)
+    assert int(host(info)[0]) == 0
+    Lo, _ = oracle.potrf(A)
+    assert_close(Lh, Lo, 1e-10, "L")
+    assert residual(Lh, A) <= 1e-13
+    adjL = workloads.lower_normal(n, seed=n + 1)
+    G = host(dc().chol_potrf_adjoint(dev(Lo), dev(adjL), accumulate=False, nb=128))
+    Go = oracle.potrf_adjoint(Lo, adjL, accumulate=False)
+    assert_close(np.tril(G), np.tril(Go), 1e-10, "adj_A")
 
 
-@pytest.mark.slow
-def test_cfg_fp64_n16384_full_size():
-    _full_size_checks(16384, 0.1, 128)
+# ------------------------------------------- fp32 at condition number 1e3 ----
+
+@pytest.mark.parametrize("n,nb", [(300, 64), (1000, 128)])
+def test_blocked_fp32_condition_1e3(n, nb):
+    A = workloads.spd_condition(n, 1e3, seed=n + 7, dtype=np.float32)
+    adjL = workloads.lower_normal(n, seed=n + 8, dtype=np.float32)
+    L, info = dc().chol_potrf(dev(A), nb=nb)
+    Lh = host(L)
+    assert int(host(info)[0]) == 0
+    Lo, _ = oracle.potrf(A)
+    assert_close(Lh, Lo, 2e-4, "L")
+    assert residual(Lh, A) <= 1e-5
+    G = host(dc().chol_potrf_adjoint(dev(Lh), dev(adjL), accumulate=False, nb=nb))
+    Go = oracle.potrf_adjoint(Lh, adjL, accumulate=False)
+    assert_close(np.tril(G), np.tril(Go), 2e-4, "adj_A")

@@ -82,6 +82,24 @@ def test_cfg_batched_fp32_65536_n32():
     assert_close(Gh, Go, 2e-4, "adj_A")
 
 
+@pytest.mark.parametrize("n,batch", [(8, 4096), (16, 4096), (32, 4096), (64, 1024)])
+def test_batched_fp32_condition_1e3(n, batch):
+    """fp32 tolerance clause: 2e-4 elementwise and residual 1e-5 on matrices of
+    condition number 1e3 (A = Q diag(logspace(0, -3, n)) Q^T)."""
+    A = workloads.spd_condition(n, 1e3, seed=500 + n, batch=batch, dtype=np.float32)
+    adjL = workloads.lower_normal(n, seed=600 + n, batch=batch, dtype=np.float32)
+    L, info = dc().chol_potrf_batched(dev(A))
+    Lh = host(L)
+    assert np.all(host(info) == 0)
+    Lo, io = oracle.potrf(A)
+    assert np.all(io == 0)
+    assert_close(Lh, Lo, 2e-4, "L")
+    assert np.max(residual(Lh, A)) <= 1e-5
+    G = host(dc().chol_potrf_adjoint_batched(dev(Lh), dev(adjL), accumulate=False))
+    Go = oracle.potrf_adjoint(Lh, adjL, accumulate=False)
+    assert_close(G, Go, 2e-4, "adj_A")
+
+
 # ------------------------------------------------------ ragged sizes, edges ----
 
 SIZES = [1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 17, 24, 31, 32, 33, 47, 63, 64]

@@ -16,6 +16,10 @@ benchmark configuration give; no dataset is involved):
 * ``gram_spd``      -- A = G G^T / n + shift * I, G iid N(0, 1) from a seed.
 * ``batched_spd``   -- A_b = B_b B_b^T / n + I, B iid N(0, 1) from a seed.
 * ``lower_normal``  -- a lower-triangular N(0, 1) upstream gradient adj_L.
+* ``spd_condition`` -- A = Q diag(logspace(0, -log10(kappa), n)) Q^T with Q the
+                       orthogonal factor of an iid N(0, 1) matrix: condition
+                       number exactly kappa (the fp32 tolerance applies to
+                       condition numbers up to 1e3).
 
 Random numbers come from ``numpy.random.default_rng(seed)`` (PCG64)
 ``standard_normal`` in fp64.
@@ -104,6 +108,19 @@ def lower_normal(n: int, seed: int = SEED_ADJ, batch: int | None = None, dtype=n
     rng = np.random.default_rng(seed)
     shape = (n, n) if batch is None else (batch, n, n)
     return np.tril(rng.standard_normal(shape)).astype(dtype)
+
+
+def spd_condition(n: int, kappa: float, seed: int = SEED_MATRIX, batch: int | None = None,
+                  dtype=np.float64):
+    """A = Q diag(logspace(0, -log10(kappa), n)) Q^T, Q orthogonal from the QR
+    factorisation of an iid N(0, 1) matrix; shape [n, n] or [batch, n, n].
+    Built in fp64, mirrored from the lower triangle, then cast."""
+    rng = np.random.default_rng(seed)
+    shape = (n, n) if batch is None else (batch, n, n)
+    Q, _ = np.linalg.qr(rng.standard_normal(shape))
+    d = np.logspace(0.0, -np.log10(kappa), n)
+    A = np.matmul(Q * d, np.swapaxes(Q, -1, -2))
+    return symmetrize_from_lower(A).astype(dtype)
 
 
 def spd_with_bad_pivot(n: int, col: int, value: float = -1.0, dtype=np.float64):

@@ -21,6 +21,10 @@ roofline.traffic = HBM bytes per launch of that kernel from the committed
   by a plain copy of known size, `--calibrate-copy`); null when no record
   matches the current kernel sources.
 cpu_baseline = the plain CPU oracle on a bounded sample of the same inputs.
+parity = the GPU outputs against that leg's oracle results: the factor's leading
+  block, the adjoint for adj_L supported on that block, all batched factors and
+  adjoints (max allclose and relative errors); plus the residual of the full
+  factor on sampled rows (torch products on the device).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -117,24 +121,78 @@ def roofline_of(fam: str, rec: dict, dtype_peak_tflops: float):
             "avg_launch_us": round(avg_s * 1e6, 2), "work_per_launch": round(per_launch)}
 
 
-def cpu_baseline(A_gpu, adjL_host, Ab_host, adjLb_host, ns: int):
+def _close_stats(got, ref, rel_frac):
+    """max |got - ref| / (|ref| + max|ref|) (per matrix of a stack) and the max
+    relative error over entries with |ref| >= rel_frac * max|ref|."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.ndim == 2:
+        got, ref = got[None], ref[None]
+    scale = np.max(np.abs(ref), axis=(-2, -1), keepdims=True)
+    err = np.abs(got - ref)
+    ac = float(np.max(err / np.maximum(np.abs(ref) + scale, 1e-300)))
+    big = (np.abs(ref) >= rel_frac * scale) & (scale > 0)
+    rel = float(np.max(np.where(big, err / np.maximum(np.abs(ref), 1e-300), 0.0)))
+    return {"max_allclose_err": ac, "max_rel_err": rel, "rel_over_entries_above": rel_frac}
+
+
+def cpu_baseline(dc, A_gpu, L_gpu, adjL_host, Ab_host, adjLb_host, Lb_gpu, ns: int):
+    """The oracle, timed on the host cores on a bounded sample of the benchmark's
+    inputs; its results are also the parity reference for the GPU outputs
+    (computed again outside the timed region where the benchmark's own outputs
+    are not comparable)."""
     import oracle
+    import torch
     threads = oracle.max_threads()
     A = A_gpu[:ns, :ns].cpu().numpy()
+    Lg = L_gpu[:ns, :ns].cpu().numpy()
+    adj_s = np.ascontiguousarray(adjL_host[:ns, :ns])
     t = time.perf_counter()
-    L, info = oracle.potrf(A)
-    oracle.potrf_adjoint(L, adjL_host[:ns, :ns])
+    Lo, info = oracle.potrf(A)
+    Go = oracle.potrf_adjoint(Lg, adj_s, accumulate=False)
     tb = time.perf_counter() - t
     gflops = (ns ** 3 / 3 + 2 * ns ** 3 / 3) / tb / 1e9
+    Lbg = Lb_gpu.cpu().numpy()
     t = time.perf_counter()
-    Lb, _ = oracle.potrf(Ab_host)
-    oracle.potrf_adjoint(Lb, adjLb_host, np.zeros_like(Lb))
+    Lbo, _ = oracle.potrf(Ab_host)
+    Gbo = oracle.potrf_adjoint(Lbg, adjLb_host, accumulate=False)
     tm = time.perf_counter() - t
-    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+    # GPU adjoints comparable with the oracle's: adj_L supported on the
+    # leading block (G is then that block's own adjoint), and the batched
+    # adjoint without accumulation
+    pad = torch.zeros_like(L_gpu)
+    pad[:ns, :ns] = torch.from_numpy(adj_s).to(L_gpu.device)
+    G = dc.chol_potrf_adjoint(L_gpu, pad, accumulate=False)
+    Gb = dc.chol_potrf_adjoint_batched(Lb_gpu, torch.from_numpy(adjLb_host).to(L_gpu.device), accumulate=False)
+    torch.cuda.synchronize()
+    outside = float(torch.tril(G)[ns:, :].abs().max().item()) if ns < L_gpu.shape[0] else 0.0
+    parity = {
+        "reference": "the oracle's results from this leg",
+        "factor_leading_block": dict(n=ns, **_close_stats(Lg, Lo, 1e-3)),
+        "adjoint_leading_block": dict(n=ns, max_abs_outside_block=outside,
+                                      **_close_stats(np.tril(G[:ns, :ns].cpu().numpy()), Go, 1e-3)),
+        "batched_factor": dict(batch=int(Ab_host.shape[0]), **_close_stats(Lbg, Lbo, 1e-1)),
+        "batched_adjoint": dict(batch=int(Ab_host.shape[0]), **_close_stats(Gb.cpu().numpy(), Gbo, 1e-1)),
+    }
+    del pad, G
+    base = {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"leading {ns}x{ns} block of the same fp64 A (factor + adjoint, rate with "
                       f"{ns}^3/3 + 2*{ns}^3/3 flops) and all {Ab_host.shape[0]} batched 32x32 matrices",
             "seconds": round(tb + tm, 2),
             "batched": {"value": round(Ab_host.shape[0] / tm, 1), "unit": "matrices/s"}}
+    return base, parity
+
+
+def sampled_residual(L, A, rows):
+    """||L[i, :] L^T - A[i, :]|| / (||A||_F / sqrt(n)) over sampled rows i
+    (plain torch products on the device)."""
+    import torch
+    anorm = A.norm().item() / np.sqrt(A.shape[0])
+    worst = 0.0
+    for i in rows:
+        r = (L[i:i + 1, :] @ L.T - A[i:i + 1, :]).norm().item() / anorm
+        worst = max(worst, r)
+    return worst
 
 
 def main():
@@ -300,9 +358,13 @@ def main():
         "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"], 4)}
                     for k, v in kern_all.items()},
     }
+    rows = sorted({0, n // 3, n // 2, n - 1} | set(np.random.default_rng(5).integers(0, n, 4).tolist()))
+    out["parity"] = {"residual_sampled_rows": {"rows": rows, "max": sampled_residual(L, A, rows)}}
     if not args.no_cpu_baseline:
         log(f"bench: CPU oracle baseline (sample n={args.cpu_sample_n})")
-        out["cpu_baseline"] = cpu_baseline(A, adjL_h, Ab_h, adjLb_h, min(args.cpu_sample_n, n))
+        base, par = cpu_baseline(dc, A, L, adjL_h, Ab_h, adjLb_h, Lb, min(args.cpu_sample_n, n))
+        out["cpu_baseline"] = base
+        out["parity"].update(par)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.chol_wave_dot_fwd_adj.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, i32, vp]
     lib.chol_status_string.restype = ctypes.c_char_p
     lib.chol_status_string.argtypes = [st]
+    lib.chol_init.restype = st
+    lib.chol_init.argtypes = []
     lib.chol_abi_version.restype = ctypes.c_int
     lib.chol_abi_version.argtypes = []
     lib.chol_potrf_plan.restype = ctypes.c_int64
@@ -258,6 +260,12 @@ def chol_potrf_plan(n: int, nb: int = 0, copy: bool = True, slots: int = PLAN_SL
                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), count)
         assert got == count
     return out
+
+
+def chol_init() -> None:
+    """One-time set-up on the current device (kernels loaded, library streams
+    created); optional, the first call does it otherwise."""
+    _check(lib.chol_init())
 
 
 def chol_abi_version() -> int:

@@ -10,6 +10,7 @@
 #include "common.hpp"
 #include "plan.hpp"
 #include "profile.hpp"
+#include "side.hpp"
 
 namespace chol {
 template <typename T>
@@ -26,6 +27,8 @@ template <typename T>
 chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
                             int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t st);
 size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb);
+chol_status small_load();
+chol_status blocked_load();
 template <typename T>
 chol_status wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar, T *bbar, int staging,
                      hipStream_t st);
@@ -83,6 +86,14 @@ static inline void clear_stale_status() { (void)hipGetLastError(); }
 extern "C" {
 
 int chol_abi_version(void) { return LIBCHOL_ABI_VERSION; }
+
+chol_status chol_init(void)
+{
+    clear_stale_status();
+    if (chol::small_load() != CHOL_OK || chol::blocked_load() != CHOL_OK)
+        return CHOL_ERR_HIP;
+    return chol::side_resources() ? CHOL_OK : CHOL_ERR_HIP;
+}
 
 const char *chol_status_string(chol_status s)
 {

@@ -344,8 +344,11 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
         return CHOL_ERR_HIP;
     std::lock_guard<std::mutex> lk(sd->mu);
     // both library streams start after the caller's earlier work; the caller's
-    // stream resumes after both are done
-    if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
+    // stream resumes after both are done.  The persistent grids' work counters
+    // are zeroed first, in stream order (a call that did not complete cannot
+    // leave a later one starting from a stale count).
+    if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess ||
+        zero_ints(sd->sched, SCHED_INTS, sd->x) != hipSuccess)
         return CHOL_ERR_HIP;
     const chol_status s = blocked_potrf_on<T>(n, A, lda, L, ldl, info, nb, sd->chain, sd->x, sd->ev[0], sd->ev[1],
                                               sd->sched, 2 * sd->wide_cus, (T *)sd->fwd_inv);
@@ -737,7 +740,8 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
     if (!sd)
         return CHOL_ERR_HIP;
     std::lock_guard<std::mutex> lk(sd->mu);
-    if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess)
+    if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess ||
+        zero_ints(sd->sched, SCHED_INTS, sd->x) != hipSuccess)
         return CHOL_ERR_HIP;
     const chol_status s = blocked_adjoint_on<T>(n, L, ldl, adjL, ldal, adjA, ldaa, accumulate, nb, ws, sd->chain,
                                                 sd->x, sd->ev[0], sd->ev[1], sd->sched, 2 * sd->wide_cus);
@@ -746,6 +750,16 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
     if (s != CHOL_OK)
         return s;
     return joined ? CHOL_OK : CHOL_ERR_HIP;
+}
+
+// Loads this file's kernels on the current device (their code object is
+// otherwise loaded on first launch).
+chol_status blocked_load()
+{
+    hipFuncAttributes a;
+    if (hip_failed(hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&k_tri<double, TRI_COPY_LOWER>))))
+        return CHOL_ERR_HIP;
+    return CHOL_OK;
 }
 
 #define CHOL_INST(T)                                                                                     \

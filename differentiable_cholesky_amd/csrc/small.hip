@@ -818,6 +818,16 @@ chol_status wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar
     return CHOL_OK;
 }
 
+// Loads this file's kernels on the current device (their code object is
+// otherwise loaded on first launch).
+chol_status small_load()
+{
+    hipFuncAttributes a;
+    if (hip_failed(hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&k_potrf_tile<float, 4, 8, true>))))
+        return CHOL_ERR_HIP;
+    return CHOL_OK;
+}
+
 #define CHOL_INST(T)                                                                                      \
     template chol_status small_potrf<T>(int, int64_t, const T *, int64_t, int64_t, T *, int64_t, int64_t, \
                                         int32_t *, int, int64_t, hipStream_t);                            \

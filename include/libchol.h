@@ -29,9 +29,17 @@
  *   - dtype selects fp32 or fp64 for every floating-point array of the call.
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
  *     keeps no reference after a call returns and allocates no device memory
- *     in these calls (the blocked adjoint takes a caller workspace).
+ *     in these calls (the blocked adjoint takes a caller workspace).  What it
+ *     keeps per device: two streams and six events, created on the first
+ *     blocked call (n > CHOL_SMALL_MAX_N) on that device, and, in the device
+ *     memory of its own code object (loaded with the library's kernels), a
+ *     256-byte array of work counters and two CHOL_MAX_NB x CHOL_MAX_NB fp64
+ *     slots for the forward's diagonal-tile inverses.  If the one-time set-up
+ *     fails, the call returns CHOL_ERR_HIP and the next blocked call retries.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
- *     is the null stream).  Nothing is synchronised with the host.
+ *     is the null stream).  Nothing is synchronised with the host.  A
+ *     blocked call runs on the library's two streams, joined to `stream` by
+ *     events at entry and exit, so it is ordered on `stream` like one kernel.
  *   - Numerical failure is not an error code: info[b] is set on the device to
  *     0 on success, else to 1 + the first column j whose pivot
  *     d = A_jj - sum_k L_jk^2 fails d > 0 (NaN fails); the factor's columns
@@ -45,6 +53,8 @@
  *     failure returns CHOL_ERR_HIP.  n == 0 or batch == 0 is a no-op.
  *   - Thread safety: calls from several host threads are safe; calls that share
  *     output buffers or a workspace on concurrent streams race on that memory.
+ *     Blocked calls on one device share the library's streams and device
+ *     buffers, so they run one after another (never overlapping each other).
  */
 #ifndef LIBCHOL_H
 #define LIBCHOL_H
@@ -60,7 +70,12 @@ extern "C" {
 
 /* Largest matrix edge handled by the batched small-tile kernels. */
 #define CHOL_SMALL_MAX_N 64
-/* Largest diagonal tile of the blocked factorisation (one workgroup keeps it in LDS). */
+/* Largest tile of the blocked factorisation (the page's T_A).  A diagonal tile
+ * is factored and inverted by one 256-thread workgroup in registers, and every
+ * product runs on 128 x 128 output tiles.  Larger tiles are not offered: the
+ * trailing update already contracts four tile columns (512) at a time, which
+ * gives the data reuse a larger tile would, while a larger diagonal tile would
+ * lengthen the serial chain of diagonal factors that the updates hide. */
 #define CHOL_MAX_NB 128
 
 typedef enum { CHOL_F32 = 0, CHOL_F64 = 1 } chol_dtype;
@@ -142,7 +157,11 @@ chol_status chol_potrf_adjoint_workspace_size(chol_dtype dtype, int64_t n, int64
 /*
  * chol_potrf_adjoint_batched -- adjoint for `batch` independent matrices,
  * n <= CHOL_SMALL_MAX_N, no workspace.  Strides and in-place rules as in
- * chol_potrf_batched / chol_potrf_adjoint.
+ * chol_potrf_batched / chol_potrf_adjoint; lower(adjA[b]) receives G_b (added
+ * with accumulate != 0).  (Warp issue #1316, resolution comment: the tile
+ * Cholesky's adjoint forms Phi(L^T adj_L), applies two triangular solves
+ * against L and accumulates into the lower triangle of A's gradient; here one
+ * matrix per group of lanes, every matrix of the batch in one launch.)
  */
 chol_status chol_potrf_adjoint_batched(chol_dtype dtype, int64_t n, int64_t batch,
                                        const void *L, int64_t ldl, int64_t strideL,
@@ -201,6 +220,17 @@ typedef enum {
 #define CHOL_PROFILE_ALL 0xffffffffu
 chol_status chol_profile_start(uint32_t mask);
 chol_status chol_profile_stop(int32_t max_ids, int64_t *count, double *ms, double *work);
+
+/*
+ * chol_init -- one-time set-up of the library on the current device: loads its
+ * kernels (and with them the device buffers of its code object, listed under
+ * "What it keeps per device" above) and creates its two streams and events.
+ * Optional: the first call on a device does the same on its own; calling
+ * chol_init first keeps that one-time device-memory use and latency out of
+ * the first factorisation.  Idempotent and thread-safe.  Returns CHOL_ERR_HIP
+ * if a HIP call fails (the set-up is retried by the next call).
+ */
+chol_status chol_init(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *chol_status_string(chol_status status);

@@ -49,6 +49,7 @@ def test_status_strings():
     ((F64, 10, P1, 10, P2, 9, NUL, 0, NUL), INVALID),         # ldl < n
     ((F64, 100, P1, 100, P2, 100, NUL, -1, NUL), INVALID),    # nb < 0
     ((F64, 100, P1, 100, P2, 100, NUL, 129, NUL), INVALID),   # nb > max
+    ((F64, 1000, P1, 1000, P2, 1000, NUL, 256, NUL), INVALID),  # nb = 256: tiles stop at 128
     ((F64, 10, P1, 10, ctypes.c_void_p(0x10000000 + 8), 10, NUL, 0, NUL), INVALID),  # partial overlap
     ((F64, 10, P1, 10, P1, 12, NUL, 0, NUL), INVALID),        # same buffer, different ld
     ((F64, 10, P1, 10, P2, 10, ctypes.c_void_p(0x20000000 + 16), 0, NUL), INVALID),  # info inside L
@@ -142,3 +143,13 @@ def test_library_binds_to_torch_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_init_reports_hip_failure_without_a_device():
+    # chol_init is the one-time set-up; with no device visible it must fail
+    # with CHOL_ERR_HIP (and a recorded HIP error), never crash
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert lib.chol_init() == _lib.CHOL_ERR_HIP
+    assert lib.chol_last_hip_error() != 0

@@ -223,10 +223,12 @@ k_splitk_reduce(int M, int N, int splits, const T *part, T *c, int64_t ldc)
     c[(int64_t)r * ldc + col] -= s;
 }
 
+// contraction length per split: a whole number of fp32 chunks (32), which is
+// also a whole number of fp64 chunks (16)
 static inline int split_chunk(int64_t K, int splits)
 {
     int c = (int)((K + splits - 1) / splits);
-    return (c + 15) / 16 * 16;
+    return (c + 31) / 32 * 32;
 }
 
 // ------------------------------------------------------------- forward ----
@@ -485,7 +487,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     // its CU with blocks of the trailing product: its waves win instruction
     // arbitration on their SIMDs
     __builtin_amdgcn_s_setprio(3);
-    __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
+    __shared__ T lds[LDS_ELEMS<T>];
     acc_t acc[4][4];
     auto zero = [&]() {
 #pragma unroll
@@ -516,9 +518,9 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     // stage 1: M = L^T tril(Wb); A(r, t) = L[t][r] (t >= r), B(t, c) = Wb[t][c] (t >= c)
     zero();
     {
-        Operand<T, OP_KM_LOWER> A{L, ldl, 0, kb, 0};
-        Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, 0};
-        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, PATH_GENERAL>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_KM_LOWER> A{L, ldl, 0, kb, vec_ok(L, ldl)};
+        Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, vec_ok(Wb, ldw)};
+        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false>(acc, A, B, 0, kb, lds);
     }
     mirror_to(s1, lds_scr);
     __threadfence_block();
@@ -528,7 +530,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     {
         Operand<T, OP_MK> A{s1, lds_scr, 0, kb, vs};
         Operand<T, OP_KM> B{inv, ldi, 0, kb, vs && vi};
-        tile_mma<T, OP_MK, OP_KM, false, PATH_MIXED>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_MK, OP_KM, false>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -548,7 +550,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     {
         Operand<T, OP_KM> A{inv, ldi, 0, kb, vs && vi};
         Operand<T, OP_KM> B{s2, lds_scr, 0, kb, vs && vi};
-        tile_mma<T, OP_KM, OP_KM, false, PATH_MIXED>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_KM, OP_KM, false>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -571,7 +573,7 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
     {
         Operand<T, OP_MK> A{sg, ldsg, 0, kb, vec_ok(sg, ldsg)};
         Operand<T, OP_KM> B{Lnext, ldl, 0, nj, vs && vec_ok(Lnext, ldl)};
-        tile_mma<T, OP_MK, OP_KM, false, PATH_MIXED>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_MK, OP_KM, false>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)

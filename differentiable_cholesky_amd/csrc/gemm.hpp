@@ -11,15 +11,31 @@
 //            (the adjoint of a lower-triangle-only trailing update reads the
 //            gradient this way)
 //   OP_KM_LOWER  OP_KM with entries k < m replaced by 0
+//   OP_SYM_DG    OP_SYM whose 128 x 128 diagonal blocks are all read from a
+//            dense copy (GemmArgs::dg); chosen by the host when every block
+//            the product meets has one
 //
 // Design for gfx950: a 256-thread block computes a 128 x 128 tile as 2 x 2
-// wavefronts of 64 x 64, each a 4 x 4 grid of 16x16x4 MFMA steps.  K advances
-// in chunks of 16 staged in LDS k-major (S[k][m]) and double-buffered; the next
-// chunk is fetched into registers with 16-byte global loads while the current
-// one feeds the matrix cores (the thread-to-element maps are given at Map
-// below).  Blocks are mapped to tiles so that each of the 8 XCDs receives a
-// contiguous row-major range of tiles (rows of A and columns of B stay in one
-// XCD's L2).
+// wavefronts of 64 x 64, each a 4 x 4 grid of 16x16x4 MFMA steps.  The
+// contraction advances in chunks of BK (one 128-byte row segment per m: 16
+// for fp64, 32 for fp32) staged in LDS, double-buffered.  A chunk is brought
+// in by 16-byte global loads that write LDS directly (global_load_lds_dwordx4:
+// lane i of a wave instruction fills bytes [16 i, 16 i + 16) of a 1 KB run),
+// so staging costs no registers and no LDS write instructions; the loads of
+// chunk c+1 are issued before the matrix-core steps of chunk c and waited for
+// once, at the barrier that ends the chunk.  Two LDS layouts:
+//   LAY_MK  [m][k] with the 16-byte slots of each row XOR-swizzled by m & 7,
+//           so that the 16 lanes reading one k for 16 rows hit distinct banks
+//           (a run of 8 rows is one wave instruction: the swizzle is applied
+//           by choosing which global slot each lane fetches);
+//   LAY_KM  [k][m] (128 contiguous m per k row, as k-major memory holds them).
+// Chunks that are not whole 16-byte runs inside the operand (edges, the
+// diagonal of a symmetric operand, an excluded block, unaligned operands) are
+// fetched element by element with bounds and written to LDS in the same
+// layout.  The lower mask of OP_KM_LOWER is applied when a fragment is read
+// from LDS, so masked operands also take the direct loads.  Blocks are mapped
+// to tiles so that each of the 8 XCDs receives a contiguous row-major range of
+// tiles (rows of A and columns of B stay in one XCD's L2).
 #pragma once
 
 #include <algorithm>
@@ -29,7 +45,7 @@
 
 namespace chol {
 
-enum { OP_MK = 0, OP_KM = 1, OP_SYM = 2, OP_KM_LOWER = 3 };
+enum { OP_MK = 0, OP_KM = 1, OP_SYM = 2, OP_KM_LOWER = 3, OP_SYM_DG = 4 };
 enum { C_SUB = 0,        // C -= AB
        C_SUB_LOWER = 1,  // C -= AB where row >= col
        C_STORE = 2,      // C  = AB
@@ -40,7 +56,7 @@ template <typename T> struct GemmArgs {
     const T *a; int64_t lda;
     const T *b; int64_t ldb;
     T *c; int64_t ldc;
-    int kchunk;          // split-K: contraction length per split (multiple of 16)
+    int kchunk;          // split-K: contraction length per split (multiple of 32)
     T *part;             // C_PARTIAL destination, splits * M * N
     int tri;             // 1: lower-triangular tile grid (M == N)
     int vec;             // 1: 16-byte global loads are legal for both operands
@@ -55,19 +71,41 @@ template <typename T> struct GemmArgs {
                          // must be zero at launch and is zero again afterwards
     const T *dg;         // OP_SYM A operand, optional: the symmetric 128 x 128
                          // diagonal blocks written whole (block I at dg + I*128*128,
-                         // row-major), read on the 16-byte path instead of
+                         // row-major), read by direct loads instead of
                          // assembling them from the lower triangle element by element
 };
 
 namespace gemm_detail {
 
-constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int BM = 128, BN = 128;
 constexpr int NT = 256;
-// LDS pitch of a k row (elements): even, so 16-byte writes stay aligned, and
-// chosen so the row-panel scatter is at most 2-way bank conflicted.
-template <typename T> struct Pitch;
-template <> struct Pitch<double> { static constexpr int v = 130; };
-template <> struct Pitch<float> { static constexpr int v = 132; };
+
+template <typename T> struct Stage {
+    static constexpr int PER = 16 / (int)sizeof(T);   // elements per 16-byte slot
+    static constexpr int BK = 8 * PER;                 // chunk depth: 128 bytes of k per m
+    static constexpr int TILE = 128 * BK;              // elements of one staged operand chunk (16 KB)
+    static constexpr int GEN = TILE / NT;              // elements per thread on the per-element path
+};
+// LDS a product needs: two buffers of the two operands' chunks (64 KB)
+template <typename T> constexpr int LDS_ELEMS = 4 * Stage<T>::TILE;
+
+enum { LAY_MK = 0, LAY_KM = 1 };
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// position of chunk element (m, k) in LDS
+template <typename T>
+__device__ __forceinline__ int lds_index(int lay, int m, int k)
+{
+    constexpr int PER = Stage<T>::PER, BK = Stage<T>::BK;
+    return lay == LAY_MK ? m * BK + (((k / PER) ^ (m & 7)) * PER) + (k % PER) : k * BM + m;
+}
+
+// s_waitcnt vmcnt(0): this wave's global loads (and their LDS writes) are done
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(1): all but the wave's last load are done
+__device__ __forceinline__ void wait_loads_but_1() { __builtin_amdgcn_s_waitcnt(0x0F71); }
 
 // element (m, k) of an operand, with bounds (m < mlim, k < klim) -> 0 outside
 template <typename T, int OP>
@@ -83,7 +121,7 @@ __device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim
         return p[(int64_t)k * ld + m];
     if (OP == OP_KM_LOWER)
         return k >= m ? p[(int64_t)k * ld + m] : T(0);
-    // OP_SYM
+    // OP_SYM, OP_SYM_DG
     if (m > k)
         return p[(int64_t)m * ld + k];
     if (m < k)
@@ -91,184 +129,113 @@ __device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim
     return T(2) * p[(int64_t)m * ld + m];
 }
 
-// Eight elements per thread per chunk, fetched as 16-byte loads of PER
-// consecutive elements.  Element j of thread t (wave w = t / 64, lane l):
-//   q = j / PER (load number), e = j % PER
-//   row-panel layout (LAY_MK): LPR = 16 / PER lanes cover the 16 k of one row
-//       m = w * 32 + q * (64 / LPR) + l / LPR,   k = (l % LPR) * PER + e
-//   k-major layout (LAY_KM): LPK = 128 / PER lanes cover the 128 m of one k row
-//       k = w * 4 + q * (64 / LPK) + l / LPK,    m = (l % LPK) * PER + e
-// so every load instruction reads whole 64- or 128-byte segments.
-template <typename T> struct Vec8 { T v[8]; };
-enum { LAY_MK = 0, LAY_KM = 1 };
-
-// LDS pitch of a chunk staged on the 16-byte path with layout LAY.  fp64
-// row-panel chunks (LAY_MK) take an odd pitch: a wave's 8-byte writes then
-// fall on distinct banks in every group of 16 lanes (with the even pitch,
-// lanes whose k differs by 8 collided); k-major chunks keep the even pitch
-// their 16-byte writes need.
-template <typename T, int LAY> struct LayPitch { static constexpr int v = Pitch<T>::v; };
-template <> struct LayPitch<double, LAY_MK> { static constexpr int v = 129; };
-
-// staging layouts an operand kind can use on the 16-byte path
-constexpr bool can_lay(int op, int lay)
-{
-    return op == OP_SYM || (op == OP_MK ? lay == LAY_MK : lay == LAY_KM);
-}
-
-template <typename T> struct Map {
-    static constexpr int PER = 16 / sizeof(T);
-    static constexpr int LPR = BK / PER;        // lanes per row (row-panel)
-    static constexpr int LPK = BM / PER;        // lanes per k row (k-major)
-    static __device__ __forceinline__ void mk(int t, int j, int &m, int &k)
-    {
-        const int w = t / 64, l = t % 64, q = j / PER, e = j % PER;
-        m = w * 32 + q * (64 / LPR) + l / LPR;
-        k = (l % LPR) * PER + e;
-    }
-    static __device__ __forceinline__ void km(int t, int j, int &m, int &k)
-    {
-        const int w = t / 64, l = t % 64, q = j / PER, e = j % PER;
-        k = w * 4 + q * (64 / LPK) + l / LPK;
-        m = (l % LPK) * PER + e;
-    }
-};
-
 template <typename T, int OP>
 struct Operand {
     const T *p;
     int64_t ld;
     int m0;      // tile origin along m
     int mlim;    // M (or N) bound
-    int vec;
+    int vec;     // 16-byte loads legal (base aligned, ld a multiple of 16 bytes)
     int excl;    // OP_SYM: leading excl x excl block left out
 
-    // layout used for a chunk starting at k0 (uniform over the block)
-    __device__ __forceinline__ int layout(int k0) const
+    // LDS layout of the operand's chunks: row panels keep rows, k-major
+    // operands keep k rows (the symmetric operand is only ever staged by the
+    // per-element path: its plain parts are handed over as row panels or
+    // k-major panels by the tile body)
+    static constexpr int LAY = (OP == OP_MK || OP == OP_SYM || OP == OP_SYM_DG) ? LAY_MK : LAY_KM;
+
+    // can the chunk at k0 be staged by direct 16-byte loads?
+    __device__ __forceinline__ bool direct(int k0, int klim) const
     {
-        if (OP == OP_MK)
-            return LAY_MK;
-        if (OP == OP_SYM)
-            return (m0 >= k0 + BK) ? LAY_MK : LAY_KM;
-        return LAY_KM;
-    }
-    // does the chunk need the per-element path (edges, diagonal crossing, masks)?
-    __device__ __forceinline__ bool generic(int k0, int klim) const
-    {
-        if (!vec || m0 + BM > mlim || k0 + BK > klim)
-            return true;
-        if (OP == OP_SYM)
-            return !(m0 >= k0 + BK || m0 + BM <= k0) || (m0 < excl && k0 < excl);
-        if (OP == OP_KM_LOWER)
-            return !(k0 >= m0 + BM - 1);         // plain only if every k >= every m
-        return false;
+        constexpr int BK = Stage<T>::BK, PER = Stage<T>::PER;
+        if (OP == OP_SYM || OP == OP_SYM_DG)
+            return false;
+        return vec && m0 + BM <= mlim && k0 + BK <= klim && k0 % PER == 0 && m0 % PER == 0;
     }
 
-    // layout of the chunk at k0 if it can take the 16-byte path, else -1
-    __device__ __forceinline__ int fast_lay(int k0, int klim) const
+    // direct loads of the chunk at k0 into S
+    __device__ __forceinline__ void stage_direct(int k0, T *S) const
     {
-        return generic(k0, klim) ? -1 : layout(k0);
-    }
-
-    // 16-byte loads of a chunk known to be on the fast path with layout LAY
-    template <int LAY>
-    __device__ __forceinline__ void fetch_fast(Vec8<T> &r, int tid, int k0) const
-    {
-        typedef Map<T> MP;
-        typedef T vt __attribute__((ext_vector_type(MP::PER)));
+        constexpr int PER = Stage<T>::PER, BK = Stage<T>::BK;
+        const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+        // the chunk's origin is uniform; a lane's element offset from it fits
+        // 32 bits (at most 127 rows of ld elements, ld < 2^24)
+        const int ld32 = (int)ld;
+        if (LAY == LAY_MK) {
+            // instruction q: rows 8q .. 8q+7; lane -> row r = lane / 8, LDS slot
+            // lane % 8 of that row, which holds global slot (lane % 8) ^ r
+            const T *base = p + (int64_t)m0 * ld + k0;
+            const int r = lane / 8, sl = (lane % 8) ^ r;
+            const int off = r * ld32 + sl * PER;
 #pragma unroll
-        for (int q = 0; q < 8 / MP::PER; ++q) {
-            int m, k;
-            if (LAY == LAY_MK)
-                MP::mk(tid, q * MP::PER, m, k);
-            else
-                MP::km(tid, q * MP::PER, m, k);
-            const T *src = (LAY == LAY_MK) ? p + (int64_t)(m0 + m) * ld + k0 + k
-                                           : p + (int64_t)(k0 + k) * ld + m0 + m;
-            const vt x = *reinterpret_cast<const vt *>(src);
-#pragma unroll
-            for (int e = 0; e < MP::PER; ++e)
-                r.v[q * MP::PER + e] = x[e];
-        }
-    }
-
-    template <int LAY>
-    static __device__ __forceinline__ void stash_lay(const Vec8<T> &r, T *S, int tid)
-    {
-        typedef Map<T> MP;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            int m, k;
-            if (LAY == LAY_MK)
-                MP::mk(tid, j, m, k);
-            else
-                MP::km(tid, j, m, k);
-            S[k * LayPitch<T, LAY>::v + m] = r.v[j];
-        }
-    }
-
-    __device__ __forceinline__ void fetch(Vec8<T> &r, int tid, int k0, int klim) const
-    {
-        typedef Map<T> MP;
-        const int lay = layout(k0);
-        if (!generic(k0, klim)) {
-            typedef T vt __attribute__((ext_vector_type(MP::PER)));
-#pragma unroll
-            for (int q = 0; q < 8 / MP::PER; ++q) {
-                int m, k;
-                if (lay == LAY_MK)
-                    MP::mk(tid, q * MP::PER, m, k);
-                else
-                    MP::km(tid, q * MP::PER, m, k);
-                const T *src = (lay == LAY_MK) ? p + (int64_t)(m0 + m) * ld + k0 + k
-                                               : p + (int64_t)(k0 + k) * ld + m0 + m;
-                const vt x = *reinterpret_cast<const vt *>(src);
-#pragma unroll
-                for (int e = 0; e < MP::PER; ++e)
-                    r.v[q * MP::PER + e] = x[e];
+            for (int j = 0; j < 4; ++j) {
+                const int q = w + 4 * j;
+                __builtin_amdgcn_global_load_lds((gvoid *)(base + (off + 8 * q * ld32)), (lvoid *)(S + 8 * q * BK),
+                                                 16, 0, 0);
             }
-            return;
-        }
+        } else {
+            // instruction q: elements [q * 64 PER, (q + 1) * 64 PER) of the [k][m] chunk
+            const T *base = p + (int64_t)k0 * ld + m0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            int m, k;
-            if (lay == LAY_MK)
-                MP::mk(tid, j, m, k);
-            else
-                MP::km(tid, j, m, k);
-            r.v[j] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim, excl);
+            for (int j = 0; j < 4; ++j) {
+                const int q = w + 4 * j;
+                const int e = q * 64 * PER + lane * PER;
+                __builtin_amdgcn_global_load_lds((gvoid *)(base + ((e / BM) * ld32 + e % BM)), (lvoid *)(S + q * 64 * PER),
+                                                 16, 0, 0);
+            }
         }
     }
 
-    // per-element path straight into the LDS chunk
-    __device__ __forceinline__ void put(T *S, int tid, int k0, int klim) const
+    // one element of one of the 128-byte lines of the chunk at k0 (a chunk
+    // is 128 such lines; lane l of waves 0 and 1 takes line l), read only to
+    // bring the line into L2 ahead of its direct load
+    __device__ __forceinline__ T touch(int k0) const
     {
-        typedef Map<T> MP;
-        const int lay = layout(k0);
+        constexpr int LPK = (int)sizeof(T);          // lines per k row of a k-major chunk (128 m)
+        const int l = threadIdx.x % 128;
+        if (LAY == LAY_MK)
+            return p[(int64_t)(m0 + l) * ld + k0];
+        return p[(int64_t)(k0 + l / LPK) * ld + m0 + (l % LPK) * (128 / LPK)];
+    }
+
+    // per-element path: bounds, masks, the symmetric diagonal; four
+    // elements in flight per step, which keeps the path's registers few
+    __device__ __forceinline__ void stage_elems(int k0, int klim, T *S) const
+    {
+        constexpr int BK = Stage<T>::BK, GEN = Stage<T>::GEN;
 #pragma unroll 1
-        for (int j = 0; j < 8; ++j) {
-            int m, k;
-            if (lay == LAY_MK)
-                MP::mk(tid, j, m, k);
-            else
-                MP::km(tid, j, m, k);
-            S[k * Pitch<T>::v + m] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim, excl);
+        for (int j0 = 0; j0 < GEN; j0 += 4) {
+            T v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = threadIdx.x + NT * (j0 + j);
+                const int m = LAY == LAY_MK ? e / BK : e % BM, k = LAY == LAY_MK ? e % BK : e / BM;
+                v[j] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim, excl);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = threadIdx.x + NT * (j0 + j);
+                const int m = LAY == LAY_MK ? e / BK : e % BM, k = LAY == LAY_MK ? e % BK : e / BM;
+                S[lds_index<T>(LAY, m, k)] = v[j];
+            }
         }
     }
 
-    __device__ __forceinline__ void stash(const Vec8<T> &r, T *S, int tid, int k0) const
+    __device__ __forceinline__ void stage(int k0, int klim, T *S) const
     {
-        typedef Map<T> MP;
-        const int lay = layout(k0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            int m, k;
-            if (lay == LAY_MK)
-                MP::mk(tid, j, m, k);
-            else
-                MP::km(tid, j, m, k);
-            S[k * Pitch<T>::v + m] = r.v[j];
-        }
+        if (direct(k0, klim))
+            stage_direct(k0, S);
+        else
+            stage_elems(k0, klim, S);
+    }
+
+    // fragment element (m, k) of the chunk at k0 staged in S
+    __device__ __forceinline__ T frag(const T *S, int m, int k, int k0) const
+    {
+        const T x = S[lds_index<T>(LAY, m, k)];
+        if (OP == OP_KM_LOWER)
+            return (k0 + k >= m0 + m) ? x : T(0);
+        return x;
     }
 };
 
@@ -281,26 +248,24 @@ __device__ __forceinline__ int xcd_tile(int b, int nt)
     return x * per + (x < rem ? x : rem) + i;
 }
 
-} // namespace gemm_detail
-
-namespace gemm_detail {
-
-// acc += (NEG ? -A : B) over one chunk staged at SA (A, pitch PA) and SB (B,
-// pitch PB) in LDS
-template <typename T, bool NEG, int PA = Pitch<T>::v, int PB = Pitch<T>::v>
-__device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], const T *SA, const T *SB, int lane,
-                                          int wm, int wn)
+// acc += (NEG ? -A : A) B over one chunk at k0 staged at SA (A) and SB (B)
+template <typename T, int AOP, int BOP, bool NEG>
+__device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
+                                          const Operand<T, BOP> &B, int k0, const T *SA, const T *SB)
 {
+    constexpr int BK = Stage<T>::BK;
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    const int wm = wave / 2, wn = wave % 2;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 4) {
         const int kr = kk + lane / 16;
         T af[4], bf[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            af[i] = SA[kr * PA + wm * 64 + i * 16 + lane % 16];
+            af[i] = A.frag(SA, wm * 64 + i * 16 + lane % 16, kr, k0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            bf[j] = SB[kr * PB + wn * 64 + j * 16 + lane % 16];
+            bf[j] = B.frag(SB, wn * 64 + j * 16 + lane % 16, kr, k0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -309,226 +274,96 @@ __device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], co
     }
 }
 
-// A run of nc >= 1 chunks starting at k0, all on the 16-byte path with fixed
-// layouts.  Software pipeline: while the matrix cores work on one LDS buffer,
-// the other is filled from registers loaded one chunk earlier, and the next
-// chunk's loads are issued.  Every load is unconditional (indices past the run
-// repeat its last chunk), so no loaded register ever merges with an older
-// value and the loads stay in flight across the matrix-core work.
-template <typename T, int AOP, int BOP, int LA, int LB, bool NEG>
-__device__ __forceinline__ void mma_run(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
-                                        const Operand<T, BOP> &B, int k0, int nc, T *lds)
-{
-    constexpr int SZ = BK * Pitch<T>::v;
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int wm = wave / 2, wn = wave % 2;
-    auto kc = [&](int c) { return k0 + (c < nc ? c : nc - 1) * BK; };
-    Vec8<T> a, b;
-    A.template fetch_fast<LA>(a, tid, k0);
-    B.template fetch_fast<LB>(b, tid, k0);
-    __syncthreads();                      // earlier users of the LDS buffers are done
-    Operand<T, AOP>::template stash_lay<LA>(a, lds, tid);
-    Operand<T, BOP>::template stash_lay<LB>(b, lds + SZ, tid);
-    A.template fetch_fast<LA>(a, tid, kc(1));
-    B.template fetch_fast<LB>(b, tid, kc(1));
-    __syncthreads();
-    for (int c = 0; c < nc; ++c) {
-        const T *S = lds + (c & 1) * 2 * SZ;
-        T *D = lds + ((c + 1) & 1) * 2 * SZ;
-        chunk_mma<T, NEG, LayPitch<T, LA>::v, LayPitch<T, LB>::v>(acc, S, S + SZ, lane, wm, wn);                   // chunk c
-        Operand<T, AOP>::template stash_lay<LA>(a, D, tid);                // chunk c+1
-        Operand<T, BOP>::template stash_lay<LB>(b, D + SZ, tid);
-        A.template fetch_fast<LA>(a, tid, kc(c + 2));
-        B.template fetch_fast<LB>(b, tid, kc(c + 2));
-        __syncthreads();
-    }
-}
-
-// mma_run with A's loads two chunks ahead (A is the operand streamed from
-// HBM; B stays one chunk ahead).  The loop takes chunks in pairs so the two A
-// register sets alternate without copies; with an odd count the last pair
-// skips only its second chunk's matrix-core work, and every load stays
-// unconditional (indices past the run repeat its last chunk).
-template <typename T, int AOP, int BOP, int LA, int LB, bool NEG>
-__device__ __forceinline__ void mma_run2(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
-                                         const Operand<T, BOP> &B, int k0, int nc, T *lds)
-{
-    constexpr int SZ = BK * Pitch<T>::v;
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int wm = wave / 2, wn = wave % 2;
-    auto kc = [&](int c) { return k0 + (c < nc ? c : nc - 1) * BK; };
-    Vec8<T> a0, a1, b;
-    A.template fetch_fast<LA>(a0, tid, k0);
-    B.template fetch_fast<LB>(b, tid, k0);
-    __syncthreads();                      // earlier users of the LDS buffers are done
-    Operand<T, AOP>::template stash_lay<LA>(a0, lds, tid);
-    Operand<T, BOP>::template stash_lay<LB>(b, lds + SZ, tid);
-    A.template fetch_fast<LA>(a1, tid, kc(1));
-    B.template fetch_fast<LB>(b, tid, kc(1));
-    A.template fetch_fast<LA>(a0, tid, kc(2));
-    __syncthreads();
-    T *const L0 = lds, *const L1 = lds + 2 * SZ;
-    for (int c = 0; c < nc; c += 2) {
-        // chunk c from L0; chunk c+1 (a1, b) into L1; a1 <- chunk c+3
-        chunk_mma<T, NEG, LayPitch<T, LA>::v, LayPitch<T, LB>::v>(acc, L0, L0 + SZ, lane, wm, wn);
-        Operand<T, AOP>::template stash_lay<LA>(a1, L1, tid);
-        Operand<T, BOP>::template stash_lay<LB>(b, L1 + SZ, tid);
-        A.template fetch_fast<LA>(a1, tid, kc(c + 3));
-        B.template fetch_fast<LB>(b, tid, kc(c + 2));
-        __syncthreads();
-        // chunk c+1 from L1; chunk c+2 (a0, b) into L0; a0 <- chunk c+4
-        if (c + 1 < nc)
-            chunk_mma<T, NEG, LayPitch<T, LA>::v, LayPitch<T, LB>::v>(acc, L1, L1 + SZ, lane, wm, wn);
-        Operand<T, AOP>::template stash_lay<LA>(a0, L0, tid);
-        Operand<T, BOP>::template stash_lay<LB>(b, L0 + SZ, tid);
-        A.template fetch_fast<LA>(a0, tid, kc(c + 4));
-        B.template fetch_fast<LB>(b, tid, kc(c + 3));
-        __syncthreads();
-    }
-}
-
-#ifndef CHOL_RUN_DEPTH
-#define CHOL_RUN_DEPTH 2
-#endif
-template <typename T, int AOP, int BOP, int LA, int LB, bool NEG>
-__device__ __forceinline__ void run_chunks(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
-                                           const Operand<T, BOP> &B, int k0, int nc, T *lds)
-{
-    if constexpr (CHOL_RUN_DEPTH == 2)
-        mma_run2<T, AOP, BOP, LA, LB, NEG>(acc, A, B, k0, nc, lds);
-    else
-        mma_run<T, AOP, BOP, LA, LB, NEG>(acc, A, B, k0, nc, lds);
-}
-
-// The K loop through the general path, chunk by chunk, for tiles with edges,
-// diagonal crossings or masks: every chunk is fetched by the path it needs
-// (16-byte or per element).  A's loads run two chunks ahead, B's one.
-template <typename T, int AOP, int BOP, bool NEG>
-__device__ __forceinline__ void mma_general(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
-                                            const Operand<T, BOP> &B, int kbeg, int kend, T *lds)
-{
-    constexpr int SZ = BK * Pitch<T>::v;
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int wm = wave / 2, wn = wave % 2;
-    Vec8<T> ra0, ra1, rb;
-    __syncthreads();
-    A.fetch(ra0, tid, kbeg, kend);
-    B.fetch(rb, tid, kbeg, kend);
-    A.stash(ra0, lds, tid, kbeg);
-    B.stash(rb, lds + SZ, tid, kbeg);
-    if (kbeg + BK < kend) {
-        A.fetch(ra1, tid, kbeg + BK, kend);
-        B.fetch(rb, tid, kbeg + BK, kend);
-    }
-    if (kbeg + 2 * BK < kend)
-        A.fetch(ra0, tid, kbeg + 2 * BK, kend);
-    __syncthreads();
-    int c = 0;
-    for (int k0 = kbeg; k0 < kend; k0 += BK, ++c) {
-        const int buf = c & 1;
-        const T *SA = lds + buf * 2 * SZ;
-        chunk_mma<T, NEG>(acc, SA, SA + SZ, lane, wm, wn);
-        if (k0 + BK < kend) {
-            T *D = lds + (buf ^ 1) * 2 * SZ;
-            B.stash(rb, D + SZ, tid, k0 + BK);
-            if (k0 + 2 * BK < kend)
-                B.fetch(rb, tid, k0 + 2 * BK, kend);
-            // chunk c+1 of A sits in set (c+1)&1; refill that set with chunk c+3
-            if ((c & 1) == 0) {
-                A.stash(ra1, D, tid, k0 + BK);
-                if (k0 + 3 * BK < kend)
-                    A.fetch(ra1, tid, k0 + 3 * BK, kend);
-            } else {
-                A.stash(ra0, D, tid, k0 + BK);
-                if (k0 + 3 * BK < kend)
-                    A.fetch(ra0, tid, k0 + 3 * BK, kend);
-            }
-        }
-        __syncthreads();
-    }
-}
-
 } // namespace gemm_detail
 
-// Pipelined runs over [kbeg, kend) where every chunk is on the 16-byte path
-// (klim is the contraction bound the chunks are classified against): the range
-// is cut where an operand's staging layout changes.
-template <typename T, int AOP, int BOP, bool NEG>
-__device__ __forceinline__ void tile_runs(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
-                                          const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, int klim, T *lds)
-{
-    using namespace gemm_detail;
-    int k = kbeg;
-    while (k < kend) {
-        const int la = A.fast_lay(k, klim), lb = B.fast_lay(k, klim);
-        int nc = 1;
-        while (k + nc * BK < kend && A.fast_lay(k + nc * BK, klim) == la && B.fast_lay(k + nc * BK, klim) == lb)
-            ++nc;
-        // only the layout pairs the operand kinds can produce are instantiated
-        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_MK)) {
-            if (la == LAY_MK && lb == LAY_MK)
-                run_chunks<T, AOP, BOP, LAY_MK, LAY_MK, NEG>(acc, A, B, k, nc, lds);
-        }
-        if constexpr (can_lay(AOP, LAY_MK) && can_lay(BOP, LAY_KM)) {
-            if (la == LAY_MK && lb == LAY_KM)
-                run_chunks<T, AOP, BOP, LAY_MK, LAY_KM, NEG>(acc, A, B, k, nc, lds);
-        }
-        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_MK)) {
-            if (la == LAY_KM && lb == LAY_MK)
-                run_chunks<T, AOP, BOP, LAY_KM, LAY_MK, NEG>(acc, A, B, k, nc, lds);
-        }
-        if constexpr (can_lay(AOP, LAY_KM) && can_lay(BOP, LAY_KM)) {
-            if (la == LAY_KM && lb == LAY_KM)
-                run_chunks<T, AOP, BOP, LAY_KM, LAY_KM, NEG>(acc, A, B, k, nc, lds);
-        }
-        k += nc * BK;
-    }
-}
-
 // The K loop of one 128 x 128 tile: acc += (NEG ? -A : A) B over k in
-// [kbeg, kend), operands staged through `lds` (2 buffers x 2 operands x
-// BK * Pitch<T>::v elements).  Called by all 256 threads of the block.  When
-// every chunk can take the 16-byte path, the range is cut into runs of chunks
-// on which both operands keep one layout each (pipelined); otherwise the tile
-// takes the general loop.  PATH fixes at compile time which of the two the
-// kernel carries (the host knows for plain operands and aligned sizes).
-enum { PATH_GENERAL = 0,   // every tile through the general loop
-       PATH_RUNS = 1,      // every chunk of every tile is on the 16-byte path
-       PATH_MIXED = 2 };   // decided per tile
-
-template <typename T, int AOP, int BOP, bool NEG, int PATH>
+// [kbeg, kend), operands staged through `lds` (LDS_ELEMS<T> elements).
+// Called by all 256 threads of the block.  Software pipeline over chunks: the
+// loads of chunk c+1 go out (directly into the free LDS buffers) before the
+// matrix-core steps of chunk c; one wait and one barrier end each chunk.
+// Each chunk of each operand is classified at run time (uniformly over the
+// block): direct loads wherever the chunk allows them, the per-element path
+// otherwise.  BOOST raises the waves' priority while they issue the next
+// chunk's loads and the current chunk's matrix-core steps, so that on a SIMD
+// shared by two blocks the block coming out of a barrier gets its memory
+// traffic going first.  TOUCH (for an A streamed from HBM without reuse):
+// one load per 128-byte line of A's chunk c+2 also goes out in iteration c,
+// which brings the chunk into L2 before its direct loads are issued; the
+// wait at the end of the chunk leaves that one load in flight.  (A second
+// LDS buffer set for a two-chunk lookahead would take the block to 80 KB of
+// LDS, and two blocks no longer fit a CU.)
+template <typename T, int AOP, int BOP, bool NEG, bool BOOST = false, bool TOUCH = false>
 __device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
                                          const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
-    if constexpr (PATH == PATH_GENERAL) {
-        mma_general<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, lds);
+    constexpr int BK = Stage<T>::BK, TILE = Stage<T>::TILE;
+    if (kend <= kbeg)
         return;
-    }
-    if constexpr (PATH == PATH_MIXED) {
-        // the chunks that need the per-element path (a diagonal crossing, an
-        // edge, a mask) span [g0, g1); they go through the general loop and
-        // the runs of 16-byte chunks before and after stay pipelined.  The
-        // three loops follow each other in straight-line code, which keeps
-        // the pipelined runs as lean in registers as in a kernel without the
-        // general loop.
-        int g0 = kend, g1 = kend;
-        for (int k = kbeg; k < kend; k += BK) {
-            if (A.fast_lay(k, kend) < 0 || B.fast_lay(k, kend) < 0) {
-                if (g0 == kend)
-                    g0 = k;
-                g1 = min(k + BK, kend);
-            }
+    const int nc = (kend - kbeg + BK - 1) / BK;
+    __syncthreads();                      // earlier users of the LDS buffers are done
+    A.stage(kbeg, kend, lds);
+    B.stage(kbeg, kend, lds + TILE);
+    wait_loads();
+    __syncthreads();
+    const bool toucher = TOUCH && threadIdx.x < 128;
+    T tsum = T(0), tprev = T(0);
+    for (int c = 0; c < nc; ++c) {
+        const int k0 = kbeg + c * BK;
+        const T *S = lds + (c & 1) * 2 * TILE;
+        if (BOOST)
+            __builtin_amdgcn_s_setprio(2);
+        if (c + 1 < nc) {
+            T *D = lds + ((c + 1) & 1) * 2 * TILE;
+            A.stage(k0 + BK, kend, D);
+            B.stage(k0 + BK, kend, D + TILE);
         }
-        if (g0 > kbeg)
-            tile_runs<T, AOP, BOP, NEG>(acc, A, B, kbeg, g0, kend, lds);
-        if (g1 > g0)
-            mma_general<T, AOP, BOP, NEG>(acc, A, B, g0, g1, lds);
-        if (kend > g1)
-            tile_runs<T, AOP, BOP, NEG>(acc, A, B, g1, kend, kend, lds);
-        return;
+        const bool touch = toucher && c + 2 < nc && A.direct(k0 + 2 * BK, kend);
+        T tnext = T(0);
+        if (touch)
+            tnext = A.touch(k0 + 2 * BK);
+        chunk_mma<T, AOP, BOP, NEG>(acc, A, B, k0, S, S + TILE);
+        if (BOOST)
+            __builtin_amdgcn_s_setprio(0);
+        if (touch)
+            wait_loads_but_1();
+        else
+            wait_loads();
+        __syncthreads();
+        if (TOUCH) {
+            tsum += tprev;                // loaded a chunk ago: complete by now
+            tprev = tnext;
+        }
     }
-    tile_runs<T, AOP, BOP, NEG>(acc, A, B, kbeg, kend, kend, lds);
+    if (TOUCH) {
+        // the touched values are consumed here, so the loads are kept; they
+        // carry nothing into the result
+        tsum += tprev;
+        __asm__ volatile("" : : "v"(tsum));
+    }
+}
+
+// The same product without the software pipeline, for the few chunks of a
+// symmetric operand that must be assembled element by element (the diagonal
+// block when no dense copy of it exists): stage, wait, compute, one chunk at
+// a time.  It keeps no state across chunks, which keeps the registers of the
+// kernels that carry it within budget.
+template <typename T, int AOP, int BOP, bool NEG>
+__device__ __forceinline__ void tile_mma_serial(typename Acc<T>::type (&acc)[4][4],
+                                                const gemm_detail::Operand<T, AOP> &A,
+                                                const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
+{
+    using namespace gemm_detail;
+    constexpr int BK = Stage<T>::BK, TILE = Stage<T>::TILE;
+#pragma unroll 1
+    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+        __syncthreads();
+        A.stage_elems(k0, kend, lds);
+        B.stage(k0, kend, lds + TILE);
+        wait_loads();
+        __syncthreads();
+        chunk_mma<T, AOP, BOP, NEG>(acc, A, B, k0, lds, lds + TILE);
+    }
 }
 
 // Position of accumulator element (i, j, v) of this thread inside the 128 x 128 tile.
@@ -541,7 +376,7 @@ __device__ __forceinline__ void acc_pos(int i, int j, int v, int &row, int &col)
 }
 
 // One 128 x 128 output tile (I, J) over the contraction range [kbeg, kend).
-template <typename T, int AOP, int BOP, int CM, int PATH>
+template <typename T, int AOP, int BOP, int CM, bool BOOST = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, int split, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
@@ -589,26 +424,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
 
     Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
     Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec, 0};
-    bool done = false;
-    if constexpr (AOP == OP_SYM && BOP == OP_KM && PATH == PATH_MIXED) {
-        // the tile's diagonal block [r0, r0 + 128) of the contraction, when it
-        // is whole, not left out and within [kbeg, kend): a plain row panel of
-        // its dense copy against B's rows shifted by r0; the parts left and
-        // right of it hold no diagonal crossing
-        const int d0 = max(kbeg, r0), d1 = min(kend, r0 + BM);
-        if (p.dg && p.vec && r0 + BM <= p.M && r0 >= p.excl && d0 < d1) {
-            if (d0 > kbeg)
-                tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, kbeg, d0, lds);
-            Operand<T, OP_MK> D{p.dg + (int64_t)I * BM * BM, BM, 0, BM, 1, 0};
-            Operand<T, OP_KM> B2{p.b + (int64_t)r0 * p.ldb, p.ldb, c0, p.N, p.vec, 0};
-            tile_runs<T, OP_MK, OP_KM, FROM_C>(acc, D, B2, d0 - r0, d1 - r0, d1 - r0, lds);
-            if (kend > d1)
-                tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, d1, kend, lds);
-            done = true;
+    if constexpr (AOP == OP_SYM || AOP == OP_SYM_DG) {
+        // Sym(S)(m, k) for the tile's rows m in [r0, r0 + 128): left of the
+        // diagonal block (k < r0) it is a row panel of S's lower triangle,
+        // right of it (k >= r0 + 128) a k-major panel of it (S[k][m]); both
+        // take the direct loads.  The diagonal block comes from its dense copy
+        // with OP_SYM_DG (a plain row panel against B's rows shifted by r0),
+        // else element by element.  The left-out leading block (at most 128
+        // wide) can only meet the diagonal block of tile row 0, whose left
+        // part is empty.
+        const int b1 = min(kend, r0), d0 = max(kbeg, r0), d1 = min(kend, r0 + BM), a0 = max(kbeg, r0 + BM);
+        if (b1 > kbeg) {
+            Operand<T, OP_MK> Ab{p.a, p.lda, r0, p.M, p.vec, 0};
+            tile_mma<T, OP_MK, BOP, FROM_C, BOOST, true>(acc, Ab, B, kbeg, b1, lds);
         }
+        if (d1 > d0 && !(r0 + BM <= p.excl)) {
+            if constexpr (AOP == OP_SYM_DG) {
+                Operand<T, OP_MK> D{p.dg + (int64_t)I * BM * BM, BM, 0, BM, 1, 0};
+                Operand<T, BOP> B2{p.b + (int64_t)r0 * p.ldb, p.ldb, c0, p.N, p.vec, 0};
+                tile_mma<T, OP_MK, BOP, FROM_C, BOOST>(acc, D, B2, d0 - r0, d1 - r0, lds);
+            } else {
+                tile_mma_serial<T, AOP, BOP, FROM_C>(acc, A, B, d0, d1, lds);
+            }
+        }
+        if (kend > a0) {
+            Operand<T, OP_KM> Aa{p.a, p.lda, r0, p.M, p.vec, 0};
+            tile_mma<T, OP_KM, BOP, FROM_C, BOOST, true>(acc, Aa, B, a0, kend, lds);
+        }
+    } else {
+        tile_mma<T, AOP, BOP, FROM_C, BOOST>(acc, A, B, kbeg, kend, lds);
     }
-    if (!done)
-        tile_mma<T, AOP, BOP, FROM_C, PATH>(acc, A, B, kbeg, kend, lds);
 
     if (interior && (CM != C_SUB_LOWER || I > J)) {
 #pragma unroll
@@ -672,12 +517,12 @@ __device__ __forceinline__ void tile_of(int t, int tri, int TJ, int &I, int &J)
 // compiled in (the choice is then made at run time from p.sched).
 enum { SCHED_BOTH = 0, SCHED_DYN = 1, SCHED_STATIC = 2 };
 
-template <typename T, int AOP, int BOP, int CM, int PATH, int SCHED>
+template <typename T, int AOP, int BOP, int CM, int SCHED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm(GemmArgs<T> p)
 {
     using namespace gemm_detail;
-    __shared__ T lds[2 * 2 * BK * Pitch<T>::v];
+    __shared__ T lds[LDS_ELEMS<T>];
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
     const int nt = p.tn ? p.tn : (p.tri ? TI * (TI + 1) / 2 : TI * TJ);
 
@@ -690,7 +535,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = blockIdx.y * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM, PATH>(p, I, J, blockIdx.y, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, true>(p, I, J, blockIdx.y, kbeg, kend, lds);
         return;
     }
 
@@ -714,7 +559,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = split * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM, PATH>(p, I, J, split, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, true>(p, I, J, split, kbeg, kend, lds);
     }
     // the last block to finish returns the counters to zero for the next launch
     if (threadIdx.x == 0) {
@@ -728,11 +573,13 @@ k_gemm(GemmArgs<T> p)
 
 // host side -------------------------------------------------------------------
 
+// direct 16-byte loads: aligned base and rows, and lane offsets within a tile
+// (127 rows of ld elements) that fit 32 bits
 template <typename T>
 static inline bool aligned16(const T *p, int64_t ld)
 {
     constexpr int PER = 16 / sizeof(T);
-    return ((uintptr_t)p % 16 == 0) && (ld % PER == 0);
+    return ((uintptr_t)p % 16 == 0) && (ld % PER == 0) && ld < ((int64_t)1 << 24);
 }
 
 template <typename T, int AOP, int BOP, int CM>
@@ -743,6 +590,14 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         return CHOL_OK;
     p.vec = aligned16(p.a, p.lda) && aligned16(p.b, p.ldb);
     p.splits = splits;
+    if constexpr (AOP == OP_SYM) {
+        // the excluded block is at most one tile; with a dense copy of every
+        // diagonal block the product meets, the kernel reads them from it
+        if (p.excl < 0 || p.excl > BM)
+            return CHOL_ERR_INVALID_VALUE;
+        if (p.dg && p.vec && p.M % BM == 0 && (p.excl == 0 || p.excl == BM) && ((uintptr_t)p.dg % 16) == 0)
+            return gemm<T, OP_SYM_DG, BOP, CM>(p, splits, st);
+    }
     const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
     const int nt_all = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
     if (p.t0 < 0 || p.tn < 0 || p.t0 + (p.tn ? p.tn : nt_all) > nt_all)
@@ -750,38 +605,17 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     const int nt = p.tn ? p.tn : nt_all;
     if (nt == 0)
         return CHOL_OK;
-    // which K-loop path the kernel carries: products of plain operands and
-    // of the symmetric operand decide per tile which chunks take the
-    // pipelined runs (all of them unless the tile has edges, diagonal
-    // crossings or masks); the masked triangular operands take only the
-    // general loop
-    constexpr bool PLAIN_A = AOP == OP_MK || AOP == OP_KM;
-    constexpr bool PLAIN_B = BOP == OP_MK || BOP == OP_KM;
-    const bool all_fast = p.vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0 &&
-                          (CM != C_PARTIAL || p.kchunk % BK == 0);
     const dim3 sgrid((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1));
-    unsigned dgrid = 0;
     if (p.sched) {
         // persistent blocks, all resident at once (two per CU the stream may use)
         const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1);
-        dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
-    }
-    auto launch = [&](auto path_c) {
-        constexpr int PATH = decltype(path_c)::value;
-        if (p.sched && CM == C_SUB_LOWER)
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, PATH, SCHED_DYN>), dim3(dgrid), dim3(NT), 0, st, p);
-        else if (p.sched)
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, PATH, SCHED_BOTH>), dim3(dgrid), dim3(NT), 0, st, p);
+        const unsigned dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
+        if (CM == C_SUB_LOWER)
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN>), dim3(dgrid), dim3(NT), 0, st, p);
         else
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, PATH, SCHED_BOTH>), sgrid, dim3(NT), 0, st, p);
-    };
-    if constexpr (PLAIN_A && PLAIN_B) {
-        (void)all_fast;
-        launch(std::integral_constant<int, PATH_MIXED>());
-    } else if constexpr (AOP == OP_SYM && PLAIN_B) {
-        launch(std::integral_constant<int, PATH_MIXED>());
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH>), dim3(dgrid), dim3(NT), 0, st, p);
     } else {
-        launch(std::integral_constant<int, PATH_GENERAL>());
+        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH>), sgrid, dim3(NT), 0, st, p);
     }
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     chol_potrf,
     chol_potrf_adjoint,
     chol_potrf_adjoint_batched,
+    chol_potrf_adjoint_noalloc,
     chol_potrf_adjoint_workspace_size,
     chol_potrf_batched,
     chol_potrf_plan,

@@ -20,6 +20,7 @@ CHOL_F32, CHOL_F64 = 0, 1
 CHOL_OK, CHOL_ERR_INVALID_VALUE, CHOL_ERR_NOT_SUPPORTED, CHOL_ERR_WORKSPACE, CHOL_ERR_HIP = range(5)
 SMALL_MAX_N = 64
 MAX_NB = 128
+NOALLOC_MAX_N = 1024
 
 
 class CholError(RuntimeError):
@@ -59,6 +60,8 @@ def _load() -> ctypes.CDLL:
     lib.chol_potrf_adjoint.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, i32, i64, vp, sz, vp]
     lib.chol_potrf_adjoint_workspace_size.restype = st
     lib.chol_potrf_adjoint_workspace_size.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(sz)]
+    lib.chol_potrf_adjoint_noalloc.restype = st
+    lib.chol_potrf_adjoint_noalloc.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, i32, i64, vp]
     lib.chol_potrf_adjoint_batched.restype = st
     lib.chol_potrf_adjoint_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, vp]
     lib.chol_wave_dot_fwd_adj.restype = st
@@ -206,6 +209,17 @@ def chol_potrf_adjoint(L, adjL, adjA=None, accumulate: bool = True, nb: int = 0,
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.chol_potrf_adjoint(code, n, pl, ldl, pb, ldb, pa, lda, 1 if accumulate else 0, nb, wptr,
                                   wbytes, _stream(stream)))
+    return adjA
+
+
+def chol_potrf_adjoint_noalloc(L, adjL, adjA, accumulate: bool = True, nb: int = 0, stream=None):
+    """chol_potrf_adjoint without a workspace (n <= CHOL_NOALLOC_MAX_N): the
+    library's static device array serves as workspace.  adjA must be given."""
+    pl, ldl = _mat(L, "L")
+    pb, ldb = _mat(adjL, "adjL")
+    pa, lda = _mat(adjA, "adjA")
+    _check(lib.chol_potrf_adjoint_noalloc(_dtype_code(L), L.shape[0], pl, ldl, pb, ldb, pa, lda,
+                                          1 if accumulate else 0, nb, _stream(stream)))
     return adjA
 
 

@@ -27,6 +27,11 @@ template <typename T>
 chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
                             int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t st);
 size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb);
+size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb, int max_splits);
+template <typename T>
+chol_status blocked_adjoint_single_stream(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
+                                          int64_t ldaa, int accumulate, int nb, void *ws, int *sched, int cus,
+                                          hipStream_t st);
 chol_status small_load();
 chol_status blocked_load();
 template <typename T>
@@ -91,6 +96,9 @@ chol_status chol_init(void)
 {
     clear_stale_status();
     if (chol::small_load() != CHOL_OK || chol::blocked_load() != CHOL_OK)
+        return CHOL_ERR_HIP;
+    chol::NoAlloc na;
+    if (!chol::noalloc_resources(na))
         return CHOL_ERR_HIP;
     return chol::side_resources() ? CHOL_OK : CHOL_ERR_HIP;
 }
@@ -245,6 +253,51 @@ chol_status chol_potrf_adjoint(chol_dtype dt, int64_t n, const void *L, int64_t 
                                              (double *)adjA, ldaa, accumulate, b, workspace, st);
     return chol::blocked_adjoint<float>(n, (const float *)L, ldl, (const float *)adjL, ldal, (float *)adjA,
                                         ldaa, accumulate, b, workspace, st);
+}
+
+chol_status chol_potrf_adjoint_noalloc(chol_dtype dt, int64_t n, const void *L, int64_t ldl, const void *adjL,
+                                       int64_t ldal, void *adjA, int64_t ldaa, int accumulate, int64_t nb,
+                                       void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n == 0)
+        return CHOL_OK;
+    if (!L || !adjL || !adjA || !ld_ok(ldl, n) || !ld_ok(ldal, n) || !ld_ok(ldaa, n))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > CHOL_NOALLOC_MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    const bool in_place = adjA == adjL;
+    if (in_place && accumulate)
+        return CHOL_ERR_INVALID_VALUE;
+    if (!alias_ok(adjL, ldal, 0, adjA, ldaa, 0, n, 1, es))
+        return CHOL_ERR_INVALID_VALUE;
+    if (overlap(extent(L, n, ldl, 1, 0, es), extent(adjA, n, ldaa, 1, 0, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    if (n <= CHOL_SMALL_MAX_N) {
+        if (dt == CHOL_F64)
+            return chol::small_potrf_adjoint<double>((int)n, 1, (const double *)L, ldl, 0, (const double *)adjL,
+                                                     ldal, 0, (double *)adjA, ldaa, 0, accumulate, st);
+        return chol::small_potrf_adjoint<float>((int)n, 1, (const float *)L, ldl, 0, (const float *)adjL, ldal,
+                                                0, (float *)adjA, ldaa, 0, accumulate, st);
+    }
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    if (chol::blocked_adjoint_workspace(n, b, es, accumulate != 0, chol::NOALLOC_SPLIT_MAX) >
+        (size_t)CHOL_NOALLOC_SCRATCH_BYTES)
+        return CHOL_ERR_NOT_SUPPORTED;
+    chol::NoAlloc na;
+    if (!chol::noalloc_resources(na))
+        return CHOL_ERR_HIP;
+    if (dt == CHOL_F64)
+        return chol::blocked_adjoint_single_stream<double>(n, (const double *)L, ldl, (const double *)adjL, ldal,
+                                                           (double *)adjA, ldaa, accumulate, b, na.scratch,
+                                                           na.sched, na.cus, st);
+    return chol::blocked_adjoint_single_stream<float>(n, (const float *)L, ldl, (const float *)adjL, ldal,
+                                                      (float *)adjA, ldaa, accumulate, b, na.scratch, na.sched,
+                                                      na.cus, st);
 }
 
 chol_status chol_potrf_adjoint_batched(chol_dtype dt, int64_t n, int64_t batch, const void *L, int64_t ldl,

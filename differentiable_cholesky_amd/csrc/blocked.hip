@@ -365,7 +365,7 @@ chol_status blocked_potrf(int64_t n, const T *A, int64_t lda, T *L, int64_t ldl,
 // Workspace layout (each part 256-byte aligned):
 //   [Wb    : n * n]                         running gradient (absent when formed in adj_A)
 //   [inv   : K * nb * nb]                   inverses of the diagonal tiles of L
-//   [part_x: SIDE_SPLIT_MAX * n * nb]       split partials of the large symmetric product
+//   [part_x: max_splits * n * nb]           split partials of the large symmetric product
 //   [part_b: (ceil(n / 128) + 1) * nb * nb] one partial of the tile column's diagonal
 //                                           update per 128-row tile of its panel, plus the
 //                                           slot the tile adjoint adds
@@ -376,14 +376,14 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static inline int64_t panel_tiles(int64_t n) { return (n + 127) / 128; }
 static const int SIDE_SPLIT_MAX = 32;    // splits of the large symmetric product
 
-size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
+size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb, int max_splits)
 {
     const int64_t K = (n + nb - 1) / nb;
     size_t s = 0;
     if (need_wb)
         s += align256((size_t)n * n * esize);
     s += align256((size_t)K * nb * nb * esize);
-    s += align256((size_t)SIDE_SPLIT_MAX * n * nb * esize);
+    s += align256((size_t)max_splits * n * nb * esize);
     s += align256((size_t)(panel_tiles(n) + 1) * nb * nb * esize);
     s += align256((size_t)2 * nb * nb * esize);
     s += align256((size_t)K * nb * nb * esize);
@@ -603,9 +603,9 @@ k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv
 // ending with the second term of tile column k-1.
 template <typename T>
 static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
-                                      int64_t ldaa, int accumulate, int nb, void *ws, hipStream_t sc,
-                                      hipStream_t sx, hipEvent_t e_tile, hipEvent_t e_wide, int *sched_x,
-                                      int cap_x)
+                                      int64_t ldaa, int accumulate, int nb, void *ws, int max_splits,
+                                      hipStream_t sc, hipStream_t sx, hipEvent_t e_tile, hipEvent_t e_wide,
+                                      int *sched_x, int cap_x)
 {
     chol_status s;
     const int64_t K = (n + nb - 1) / nb;
@@ -624,7 +624,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
     T *inv = (T *)w;
     w += align256((size_t)K * nb * nb * sizeof(T));
     T *part_x = (T *)w;
-    w += align256((size_t)SIDE_SPLIT_MAX * n * nb * sizeof(T));
+    w += align256((size_t)max_splits * n * nb * sizeof(T));
     T *part_b = (T *)w;
     w += align256((size_t)(panel_tiles(n) + 1) * nb * nb * sizeof(T));
     T *part_c = (T *)w;
@@ -722,7 +722,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
             const double flops = 2.0 * nb * ((double)(m + kb) * (m + kb) - (double)kb * kb);
             const T *dg = dense ? dense + k * nb * nb : nullptr;   // diagonal tiles from tile k on
             if ((s = sym_product<T>((int)(m + kb), nb, (int)(m + kb), Wkk, ldw, L + k0 * ldl + j0, ldl,
-                                    Wb + k0 * ldw + j0, ldw, kb, dg, part_x, SIDE_SPLIT_MAX, 128, sched_x,
+                                    Wb + k0 * ldw + j0, ldw, kb, dg, part_x, max_splits, 128, sched_x,
                                     cap_x, flops, sx)) != CHOL_OK)
                 return s;
         }
@@ -745,13 +745,34 @@ chol_status blocked_adjoint(int64_t n, const T *L, int64_t ldl, const T *adjL, i
     if (stream_join(sd->chain, st, sd->ev[2]) != hipSuccess || stream_join(sd->x, st, sd->ev[2]) != hipSuccess ||
         zero_ints(sd->sched, SCHED_INTS, sd->x) != hipSuccess)
         return CHOL_ERR_HIP;
-    const chol_status s = blocked_adjoint_on<T>(n, L, ldl, adjL, ldal, adjA, ldaa, accumulate, nb, ws, sd->chain,
-                                                sd->x, sd->ev[0], sd->ev[1], sd->sched, 2 * sd->wide_cus);
+    const chol_status s = blocked_adjoint_on<T>(n, L, ldl, adjL, ldal, adjA, ldaa, accumulate, nb, ws,
+                                                SIDE_SPLIT_MAX, sd->chain, sd->x, sd->ev[0], sd->ev[1], sd->sched,
+                                                2 * sd->wide_cus);
     const bool joined = stream_join(sd->chain, sd->x, sd->ev[3]) == hipSuccess &&
                         stream_join(st, sd->chain, sd->ev[4]) == hipSuccess;
     if (s != CHOL_OK)
         return s;
     return joined ? CHOL_OK : CHOL_ERR_HIP;
+}
+
+size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb)
+{
+    return blocked_adjoint_workspace(n, nb, esize, need_wb, SIDE_SPLIT_MAX);
+}
+
+// The adjoint on the caller's stream alone, with a caller-given workspace of
+// blocked_adjoint_workspace(n, nb, es, accumulate, NOALLOC_SPLIT_MAX) bytes
+// and its own work-counter slot: no library stream, event or allocation is
+// involved (the entry point for callers that cannot allocate).
+template <typename T>
+chol_status blocked_adjoint_single_stream(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
+                                          int64_t ldaa, int accumulate, int nb, void *ws, int *sched, int cus,
+                                          hipStream_t st)
+{
+    if (zero_ints(sched, 2, st) != hipSuccess)
+        return CHOL_ERR_HIP;
+    return blocked_adjoint_on<T>(n, L, ldl, adjL, ldal, adjA, ldaa, accumulate, nb, ws, NOALLOC_SPLIT_MAX, st, st,
+                                 nullptr, nullptr, sched, 2 * cus);
 }
 
 // Loads this file's kernels on the current device (their code object is
@@ -768,7 +789,9 @@ chol_status blocked_load()
     template chol_status blocked_potrf<T>(int64_t, const T *, int64_t, T *, int64_t, int32_t *, int,     \
                                           hipStream_t);                                                  \
     template chol_status blocked_adjoint<T>(int64_t, const T *, int64_t, const T *, int64_t, T *, int64_t, \
-                                            int, int, void *, hipStream_t);
+                                            int, int, void *, hipStream_t);                              \
+    template chol_status blocked_adjoint_single_stream<T>(int64_t, const T *, int64_t, const T *, int64_t, T *, \
+                                                          int64_t, int, int, void *, int *, int, hipStream_t);
 CHOL_INST(float)
 CHOL_INST(double)
 #undef CHOL_INST

@@ -9,10 +9,22 @@ namespace chol {
 __device__ __align__(256) int g_sched_counters[SCHED_INTS];
 __device__ __align__(256) double g_fwd_inverse_slots[2 * CHOL_MAX_NB * CHOL_MAX_NB];
 
+// Workspace of the allocation-free adjoint (chol_potrf_adjoint_noalloc), one
+// copy per device.  In host code its name is only a handle for the symbol
+// lookup below; every use goes through the device address resolved there.
+static __device__ __align__(256) unsigned char scratch[CHOL_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 constexpr int MAX_DEVICES = 64;
 Side g_side[MAX_DEVICES];
 std::mutex g_init_mu[MAX_DEVICES];
+
+struct NoAllocSlot {
+    NoAlloc r{};
+    bool ok = false;
+};
+NoAllocSlot g_noalloc[MAX_DEVICES];
+std::mutex g_noalloc_mu[MAX_DEVICES];
 
 __global__ void k_zero_ints(int *p, int count)
 {
@@ -86,8 +98,40 @@ Side *side_resources()
     return &s;
 }
 
+bool noalloc_resources(NoAlloc &out)
+{
+    int dev = 0;
+    if (hip_failed(hipGetDevice(&dev)))
+        return false;
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        hip_failed(hipErrorInvalidDevice);
+        return false;
+    }
+    NoAllocSlot &s = g_noalloc[dev];
+    std::lock_guard<std::mutex> lk(g_noalloc_mu[dev]);
+    if (!s.ok) {
+        NoAlloc r{};
+        int *counters = nullptr;
+        if (hip_failed(hipGetSymbolAddress(&r.scratch, HIP_SYMBOL(scratch))) ||
+            hip_failed(hipGetSymbolAddress((void **)&counters, HIP_SYMBOL(g_sched_counters))) ||
+            hip_failed(hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev)))
+            return false;
+        if (r.cus <= 0) {
+            hip_failed(hipErrorInvalidDevice);
+            return false;
+        }
+        r.sched = counters + SCHED_STRIDE;   // slot 1; slot 0 belongs to the calls on the library streams
+        s.r = r;
+        s.ok = true;
+    }
+    out = s.r;
+    return true;
+}
+
 hipError_t stream_join(hipStream_t waiter, hipStream_t src, hipEvent_t ev)
 {
+    if (waiter == src)
+        return hipSuccess;              // one stream: already in order
     hipError_t e = hipEventRecord(ev, src);
     if (hip_failed(e))
         return e;

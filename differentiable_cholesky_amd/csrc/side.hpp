@@ -49,6 +49,22 @@ struct Side {
 // HIP error recorded) if they could not be created -- a later call retries.
 Side *side_resources();
 
+// Split cap of the symmetric product in the allocation-free adjoint, whose
+// workspace lives in the library's static `scratch` array.
+constexpr int NOALLOC_SPLIT_MAX = 4;
+
+// The allocation-free adjoint's device storage on the current device: the
+// address of the static `scratch` array (CHOL_NOALLOC_SCRATCH_BYTES) and of
+// its own work-counter slot, and the device's CU count.  Resolved once per
+// device (symbol lookups only: nothing is allocated or created); false (and
+// the HIP error recorded) on failure.
+struct NoAlloc {
+    void *scratch;
+    int *sched;
+    int cus;
+};
+bool noalloc_resources(NoAlloc &out);
+
 // Enqueue-side helpers: make `waiter` wait for everything enqueued so far on `src`.
 hipError_t stream_join(hipStream_t waiter, hipStream_t src, hipEvent_t ev);
 

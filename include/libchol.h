@@ -155,6 +155,36 @@ chol_status chol_potrf_adjoint_workspace_size(chol_dtype dtype, int64_t n, int64
                                               size_t *bytes);
 
 /*
+ * chol_potrf_adjoint_noalloc -- chol_potrf_adjoint for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace, and the same result (G in the lower triangle of adjA, added with
+ * accumulate != 0; adjA == adjL allowed with accumulate == 0).
+ *   n      <= CHOL_NOALLOC_MAX_N; larger n returns CHOL_ERR_NOT_SUPPORTED
+ *          before anything is launched.
+ * The workspace is a device array of CHOL_NOALLOC_SCRATCH_BYTES inside the
+ * library's code object (one per device, held until the process ends); the
+ * call allocates nothing and creates nothing: its kernels run on `stream`
+ * alone (no library stream or event), in the order of the blocked adjoint,
+ * with the split count of the large products capped so that the workspace
+ * fits.  The array keeps the last call's contents; every value a call reads
+ * from it is written by that call first.  Calls on one device share the
+ * array and a work counter, so calls that overlap on one GPU (concurrent
+ * streams, or concurrent with another chol_potrf_adjoint_noalloc call) race;
+ * calls ordered on one stream, or synchronised, do not.  The device address
+ * of the array is looked up once per device (by chol_init, or the first
+ * call); argument errors as for chol_potrf_adjoint.
+ */
+#define CHOL_NOALLOC_MAX_N 1024
+#define CHOL_NOALLOC_SCRATCH_BYTES (16u << 20)
+chol_status chol_potrf_adjoint_noalloc(chol_dtype dtype, int64_t n,
+                                       const void *L, int64_t ldl,
+                                       const void *adjL, int64_t ldal,
+                                       void *adjA, int64_t ldaa,
+                                       int accumulate, int64_t nb,
+                                       void *stream);
+
+/*
  * chol_potrf_adjoint_batched -- adjoint for `batch` independent matrices,
  * n <= CHOL_SMALL_MAX_N, no workspace.  Strides and in-place rules as in
  * chol_potrf_batched / chol_potrf_adjoint; lower(adjA[b]) receives G_b (added

@@ -153,3 +153,15 @@ def test_init_reports_hip_failure_without_a_device():
         pytest.skip("a GPU is visible")
     assert lib.chol_init() == _lib.CHOL_ERR_HIP
     assert lib.chol_last_hip_error() != 0
+
+
+def test_noalloc_adjoint_argument_errors():
+    # the allocation-free adjoint validates like chol_potrf_adjoint and
+    # rejects sizes beyond its static workspace before launching anything
+    n = _lib.NOALLOC_MAX_N
+    f = lib.chol_potrf_adjoint_noalloc
+    assert f(F64, n + 1, P1, n + 1, P2, n + 1, P3, n + 1, 1, 0, NUL) == NOTSUP
+    assert f(F64, n, P1, n, P2, n, P2, n, 1, 0, NUL) == INVALID          # in place with accumulate
+    assert f(F64, n, NUL, n, P2, n, P3, n, 1, 0, NUL) == INVALID
+    assert f(F64, n, P1, n, P2, n, P3, n, 1, 129, NUL) == INVALID      # nb too large
+    assert f(F64, 0, NUL, 0, NUL, 0, NUL, 0, 1, 0, NUL) == OK

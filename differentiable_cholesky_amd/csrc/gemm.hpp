@@ -286,12 +286,13 @@ __device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], co
 // otherwise.  BOOST raises the waves' priority while they issue the next
 // chunk's loads and the current chunk's matrix-core steps, so that on a SIMD
 // shared by two blocks the block coming out of a barrier gets its memory
-// traffic going first.  TOUCH (for an A streamed from HBM without reuse):
-// one load per 128-byte line of A's chunk c+2 also goes out in iteration c,
-// which brings the chunk into L2 before its direct loads are issued; the
-// wait at the end of the chunk leaves that one load in flight.  (A second
-// LDS buffer set for a two-chunk lookahead would take the block to 80 KB of
-// LDS, and two blocks no longer fit a CU.)
+// traffic going first.  TOUCH (for an A streamed from HBM without reuse, as
+// in the symmetric product): one load per 128-byte line of A's chunk c+2
+// also goes out in iteration c (from waves 0 and 1), which brings the chunk
+// into L2 before its direct loads are issued; the wait at the end of the
+// chunk leaves that one load in flight.  (A second LDS buffer set for a
+// two-chunk lookahead would take the block to 80 KB of LDS, and two blocks no
+// longer fit a CU.)
 template <typename T, int AOP, int BOP, bool NEG, bool BOOST = false, bool TOUCH = false>
 __device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
                                          const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)

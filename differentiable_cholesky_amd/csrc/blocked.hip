@@ -278,6 +278,13 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             flops = (double)w * (w + 1) * Kd + 2.0 * (M - w) * w * Kd;
         }
         prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, flops);
+        // the narrow updates of single panels (128 deep) and those with few
+        // 128 x 128 tiles take 64 x 64 tiles: a 128-deep 128 x 128 tile is
+        // ~20 us of one CU's matrix cores, and a short launch is as long as
+        // its slowest tile
+        const int64_t tiles128 = ((M + 127) / 128) * ((w + 127) / 128);
+        if (!tri && (Kd <= 128 || tiles128 < 256))
+            return gemm<T, OP_MK, OP_MK, C_SUB_LOWER, 64>(p, 1, sx);
         return gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx);
     };
     const std::vector<FwdOp> plan = forward_plan(n, nb, A != L, cap_x);
@@ -309,7 +316,7 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             p.b = slot_ptr(o.slot); p.ldb = MAX_TILE;
             p.c = L + r0 * ldl + k0; p.ldc = ldl;
             prof::Scope ps(CHOL_K_PANEL_SOLVE, sx, (double)m * kb * kb);
-            s = gemm<T, OP_MK, OP_MK, C_STORE>(p, 1, sx);
+            s = gemm<T, OP_MK, OP_MK, C_STORE, 64>(p, 1, sx);
             break;
         }
         case FWD_UPDATE:
@@ -676,7 +683,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 p.b = invk; p.ldb = nb;
                 p.c = Wp; p.ldc = ldw;
                 prof::Scope ps(CHOL_K_ADJ_PANEL, sx, (double)m * kb * kb);
-                if ((s = gemm<T, OP_MK, OP_KM, C_STORE>(p, 1, sx)) != CHOL_OK)
+                if ((s = gemm<T, OP_MK, OP_KM, C_STORE, 64>(p, 1, sx)) != CHOL_OK)
                     return s;
             }
         }

@@ -77,17 +77,33 @@ template <typename T> struct GemmArgs {
 
 namespace gemm_detail {
 
-constexpr int BM = 128, BN = 128;
+constexpr int BM = 128;   // the large tile edge (the symmetric operand's diagonal blocks)
 constexpr int NT = 256;
 
-template <typename T> struct Stage {
+// Chunk geometry of one operand's TE x BK chunk (TE = 128 or 64 rows along
+// m).  An output tile is TM x 128 (TM = 128 or 64): A's chunks have TM rows,
+// B's 128, and the 2 x 2 waves each own TM/2 x 64 of it, an FRM x 4 grid of
+// 16 x 16 MFMA tiles.  (A block always owns whole 128-column spans of its
+// rows, so products computed in place over a 128-wide panel stay race-free.)
+template <typename T, int TE = 128> struct Stage {
+    static_assert(TE == 128 || TE == 64, "tile edge 128 or 64");
     static constexpr int PER = 16 / (int)sizeof(T);   // elements per 16-byte slot
     static constexpr int BK = 8 * PER;                 // chunk depth: 128 bytes of k per m
-    static constexpr int TILE = 128 * BK;              // elements of one staged operand chunk (16 KB)
+    static constexpr int TILE = TE * BK;               // elements of one staged operand chunk
     static constexpr int GEN = TILE / NT;              // elements per thread on the per-element path
+    static constexpr int DPW = TE / 32;                // direct-load instructions per wave per chunk
 };
-// LDS a product needs: two buffers of the two operands' chunks (64 KB)
-template <typename T> constexpr int LDS_ELEMS = 4 * Stage<T>::TILE;
+template <int TM> struct WaveTile {
+    static constexpr int WM = TM / 2;                  // wave tile rows
+    static constexpr int FRM = TM / 32;                // MFMA tiles along the wave tile's rows
+    static constexpr int WN = 64, FRN = 4;
+};
+// a wave's accumulators: FRM x FRN MFMA result tiles
+template <typename T, int TM> using AccTile = typename Acc<T>::type[WaveTile<TM>::FRM][WaveTile<TM>::FRN];
+
+// LDS a product needs: two buffers of A's (TM x BK) and B's (128 x BK) chunks
+// (64 KB for 128-row tiles, 48 KB for 64-row tiles)
+template <typename T, int TM = 128> constexpr int LDS_ELEMS = 2 * (Stage<T, TM>::TILE + Stage<T, 128>::TILE);
 
 enum { LAY_MK = 0, LAY_KM = 1 };
 
@@ -95,11 +111,11 @@ typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
 // position of chunk element (m, k) in LDS
-template <typename T>
+template <typename T, int TE>
 __device__ __forceinline__ int lds_index(int lay, int m, int k)
 {
-    constexpr int PER = Stage<T>::PER, BK = Stage<T>::BK;
-    return lay == LAY_MK ? m * BK + (((k / PER) ^ (m & 7)) * PER) + (k % PER) : k * BM + m;
+    constexpr int PER = Stage<T, TE>::PER, BK = Stage<T, TE>::BK;
+    return lay == LAY_MK ? m * BK + (((k / PER) ^ (m & 7)) * PER) + (k % PER) : k * TE + m;
 }
 
 // s_waitcnt vmcnt(0): this wave's global loads (and their LDS writes) are done
@@ -129,7 +145,7 @@ __device__ __forceinline__ T elem(const T *p, int64_t ld, int m, int k, int mlim
     return T(2) * p[(int64_t)m * ld + m];
 }
 
-template <typename T, int OP>
+template <typename T, int OP, int TS = 128>   // TS: the operand's chunk rows (along m)
 struct Operand {
     const T *p;
     int64_t ld;
@@ -147,16 +163,16 @@ struct Operand {
     // can the chunk at k0 be staged by direct 16-byte loads?
     __device__ __forceinline__ bool direct(int k0, int klim) const
     {
-        constexpr int BK = Stage<T>::BK, PER = Stage<T>::PER;
+        constexpr int BK = Stage<T, TS>::BK, PER = Stage<T, TS>::PER;
         if (OP == OP_SYM || OP == OP_SYM_DG)
             return false;
-        return vec && m0 + BM <= mlim && k0 + BK <= klim && k0 % PER == 0 && m0 % PER == 0;
+        return vec && m0 + TS <= mlim && k0 + BK <= klim && k0 % PER == 0 && m0 % PER == 0;
     }
 
     // direct loads of the chunk at k0 into S
     __device__ __forceinline__ void stage_direct(int k0, T *S) const
     {
-        constexpr int PER = Stage<T>::PER, BK = Stage<T>::BK;
+        constexpr int PER = Stage<T, TS>::PER, BK = Stage<T, TS>::BK, DPW = Stage<T, TS>::DPW;
         const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
         // the chunk's origin is uniform; a lane's element offset from it fits
         // 32 bits (at most 127 rows of ld elements, ld < 2^24)
@@ -168,7 +184,7 @@ struct Operand {
             const int r = lane / 8, sl = (lane % 8) ^ r;
             const int off = r * ld32 + sl * PER;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < DPW; ++j) {
                 const int q = w + 4 * j;
                 __builtin_amdgcn_global_load_lds((gvoid *)(base + (off + 8 * q * ld32)), (lvoid *)(S + 8 * q * BK),
                                                  16, 0, 0);
@@ -177,46 +193,46 @@ struct Operand {
             // instruction q: elements [q * 64 PER, (q + 1) * 64 PER) of the [k][m] chunk
             const T *base = p + (int64_t)k0 * ld + m0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < DPW; ++j) {
                 const int q = w + 4 * j;
                 const int e = q * 64 * PER + lane * PER;
-                __builtin_amdgcn_global_load_lds((gvoid *)(base + ((e / BM) * ld32 + e % BM)), (lvoid *)(S + q * 64 * PER),
+                __builtin_amdgcn_global_load_lds((gvoid *)(base + ((e / TS) * ld32 + e % TS)), (lvoid *)(S + q * 64 * PER),
                                                  16, 0, 0);
             }
         }
     }
 
     // one element of one of the 128-byte lines of the chunk at k0 (a chunk
-    // is 128 such lines; lane l of waves 0 and 1 takes line l), read only to
-    // bring the line into L2 ahead of its direct load
+    // is TS such lines; thread l < TS takes line l), read only to bring the
+    // line into L2 ahead of its direct load
     __device__ __forceinline__ T touch(int k0) const
     {
-        constexpr int LPK = (int)sizeof(T);          // lines per k row of a k-major chunk (128 m)
-        const int l = threadIdx.x % 128;
+        constexpr int LPK = TS * (int)sizeof(T) / 128;   // lines per k row of a k-major chunk
+        const int l = threadIdx.x % TS;
         if (LAY == LAY_MK)
             return p[(int64_t)(m0 + l) * ld + k0];
-        return p[(int64_t)(k0 + l / LPK) * ld + m0 + (l % LPK) * (128 / LPK)];
+        return p[(int64_t)(k0 + l / LPK) * ld + m0 + (l % LPK) * (128 / (int)sizeof(T))];
     }
 
     // per-element path: bounds, masks, the symmetric diagonal; four
     // elements in flight per step, which keeps the path's registers few
     __device__ __forceinline__ void stage_elems(int k0, int klim, T *S) const
     {
-        constexpr int BK = Stage<T>::BK, GEN = Stage<T>::GEN;
+        constexpr int BK = Stage<T, TS>::BK, GEN = Stage<T, TS>::GEN;
 #pragma unroll 1
         for (int j0 = 0; j0 < GEN; j0 += 4) {
             T v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int e = threadIdx.x + NT * (j0 + j);
-                const int m = LAY == LAY_MK ? e / BK : e % BM, k = LAY == LAY_MK ? e % BK : e / BM;
+                const int m = LAY == LAY_MK ? e / BK : e % TS, k = LAY == LAY_MK ? e % BK : e / TS;
                 v[j] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim, excl);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int e = threadIdx.x + NT * (j0 + j);
-                const int m = LAY == LAY_MK ? e / BK : e % BM, k = LAY == LAY_MK ? e % BK : e / BM;
-                S[lds_index<T>(LAY, m, k)] = v[j];
+                const int m = LAY == LAY_MK ? e / BK : e % TS, k = LAY == LAY_MK ? e % BK : e / TS;
+                S[lds_index<T, TS>(LAY, m, k)] = v[j];
             }
         }
     }
@@ -232,7 +248,7 @@ struct Operand {
     // fragment element (m, k) of the chunk at k0 staged in S
     __device__ __forceinline__ T frag(const T *S, int m, int k, int k0) const
     {
-        const T x = S[lds_index<T>(LAY, m, k)];
+        const T x = S[lds_index<T, TS>(LAY, m, k)];
         if (OP == OP_KM_LOWER)
             return (k0 + k >= m0 + m) ? x : T(0);
         return x;
@@ -249,27 +265,28 @@ __device__ __forceinline__ int xcd_tile(int b, int nt)
 }
 
 // acc += (NEG ? -A : A) B over one chunk at k0 staged at SA (A) and SB (B)
-template <typename T, int AOP, int BOP, bool NEG>
-__device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], const Operand<T, AOP> &A,
-                                          const Operand<T, BOP> &B, int k0, const T *SA, const T *SB)
+template <typename T, int AOP, int BOP, bool NEG, int TM>
+__device__ __forceinline__ void chunk_mma(AccTile<T, TM> &acc, const Operand<T, AOP, TM> &A,
+                                          const Operand<T, BOP, 128> &B, int k0, const T *SA, const T *SB)
 {
-    constexpr int BK = Stage<T>::BK;
+    constexpr int BK = Stage<T, TM>::BK;
+    constexpr int FRM = WaveTile<TM>::FRM, FRN = WaveTile<TM>::FRN, WM = WaveTile<TM>::WM, WN = WaveTile<TM>::WN;
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
     const int wm = wave / 2, wn = wave % 2;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 4) {
         const int kr = kk + lane / 16;
-        T af[4], bf[4];
+        T af[FRM], bf[FRN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[i] = A.frag(SA, wm * 64 + i * 16 + lane % 16, kr, k0);
+        for (int i = 0; i < FRM; ++i)
+            af[i] = A.frag(SA, wm * WM + i * 16 + lane % 16, kr, k0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bf[j] = B.frag(SB, wn * 64 + j * 16 + lane % 16, kr, k0);
+        for (int j = 0; j < FRN; ++j)
+            bf[j] = B.frag(SB, wn * WN + j * 16 + lane % 16, kr, k0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FRM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FRN; ++j)
                 acc[i][j] = mfma16x16x4_s<NEG>(af[i], bf[j], acc[i][j]);
     }
 }
@@ -293,37 +310,37 @@ __device__ __forceinline__ void chunk_mma(typename Acc<T>::type (&acc)[4][4], co
 // chunk leaves that one load in flight.  (A second LDS buffer set for a
 // two-chunk lookahead would take the block to 80 KB of LDS, and two blocks no
 // longer fit a CU.)
-template <typename T, int AOP, int BOP, bool NEG, bool BOOST = false, bool TOUCH = false>
-__device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], const gemm_detail::Operand<T, AOP> &A,
-                                         const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
+template <typename T, int AOP, int BOP, bool NEG, bool BOOST = false, bool TOUCH = false, int TM = 128>
+__device__ __forceinline__ void tile_mma(gemm_detail::AccTile<T, TM> &acc, const gemm_detail::Operand<T, AOP, TM> &A,
+                                         const gemm_detail::Operand<T, BOP, 128> &B, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
-    constexpr int BK = Stage<T>::BK, TILE = Stage<T>::TILE;
+    constexpr int BK = Stage<T, TM>::BK, TA = Stage<T, TM>::TILE, SZ = TA + Stage<T, 128>::TILE;
     if (kend <= kbeg)
         return;
     const int nc = (kend - kbeg + BK - 1) / BK;
     __syncthreads();                      // earlier users of the LDS buffers are done
     A.stage(kbeg, kend, lds);
-    B.stage(kbeg, kend, lds + TILE);
+    B.stage(kbeg, kend, lds + TA);
     wait_loads();
     __syncthreads();
-    const bool toucher = TOUCH && threadIdx.x < 128;
+    const bool toucher = TOUCH && threadIdx.x < TM;
     T tsum = T(0), tprev = T(0);
     for (int c = 0; c < nc; ++c) {
         const int k0 = kbeg + c * BK;
-        const T *S = lds + (c & 1) * 2 * TILE;
+        const T *S = lds + (c & 1) * SZ;
         if (BOOST)
             __builtin_amdgcn_s_setprio(2);
         if (c + 1 < nc) {
-            T *D = lds + ((c + 1) & 1) * 2 * TILE;
+            T *D = lds + ((c + 1) & 1) * SZ;
             A.stage(k0 + BK, kend, D);
-            B.stage(k0 + BK, kend, D + TILE);
+            B.stage(k0 + BK, kend, D + TA);
         }
         const bool touch = toucher && c + 2 < nc && A.direct(k0 + 2 * BK, kend);
         T tnext = T(0);
         if (touch)
             tnext = A.touch(k0 + 2 * BK);
-        chunk_mma<T, AOP, BOP, NEG>(acc, A, B, k0, S, S + TILE);
+        chunk_mma<T, AOP, BOP, NEG, TM>(acc, A, B, k0, S, S + TA);
         if (BOOST)
             __builtin_amdgcn_s_setprio(0);
         if (touch)
@@ -349,71 +366,77 @@ __device__ __forceinline__ void tile_mma(typename Acc<T>::type (&acc)[4][4], con
 // block when no dense copy of it exists): stage, wait, compute, one chunk at
 // a time.  It keeps no state across chunks, which keeps the registers of the
 // kernels that carry it within budget.
-template <typename T, int AOP, int BOP, bool NEG>
-__device__ __forceinline__ void tile_mma_serial(typename Acc<T>::type (&acc)[4][4],
-                                                const gemm_detail::Operand<T, AOP> &A,
-                                                const gemm_detail::Operand<T, BOP> &B, int kbeg, int kend, T *lds)
+template <typename T, int AOP, int BOP, bool NEG, int TM = 128>
+__device__ __forceinline__ void tile_mma_serial(gemm_detail::AccTile<T, TM> &acc,
+                                                const gemm_detail::Operand<T, AOP, TM> &A,
+                                                const gemm_detail::Operand<T, BOP, 128> &B, int kbeg, int kend,
+                                                T *lds)
 {
     using namespace gemm_detail;
-    constexpr int BK = Stage<T>::BK, TILE = Stage<T>::TILE;
+    constexpr int BK = Stage<T, TM>::BK, TA = Stage<T, TM>::TILE;
 #pragma unroll 1
     for (int k0 = kbeg; k0 < kend; k0 += BK) {
         __syncthreads();
         A.stage_elems(k0, kend, lds);
-        B.stage(k0, kend, lds + TILE);
+        B.stage(k0, kend, lds + TA);
         wait_loads();
         __syncthreads();
-        chunk_mma<T, AOP, BOP, NEG>(acc, A, B, k0, lds, lds + TILE);
+        chunk_mma<T, AOP, BOP, NEG, TM>(acc, A, B, k0, lds, lds + TA);
     }
 }
 
-// Position of accumulator element (i, j, v) of this thread inside the 128 x 128 tile.
-template <typename T>
+// Position of accumulator element (i, j, v) of this thread inside the TM x 128 tile.
+template <typename T, int TM = 128>
 __device__ __forceinline__ void acc_pos(int i, int j, int v, int &row, int &col)
 {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    row = (wave / 2) * 64 + i * 16 + Acc<T>::row(lane, v);
-    col = (wave % 2) * 64 + j * 16 + lane % 16;
+    row = (wave / 2) * gemm_detail::WaveTile<TM>::WM + i * 16 + Acc<T>::row(lane, v);
+    col = (wave % 2) * gemm_detail::WaveTile<TM>::WN + j * 16 + lane % 16;
 }
 
-// One 128 x 128 output tile (I, J) over the contraction range [kbeg, kend).
-template <typename T, int AOP, int BOP, int CM, bool BOOST = false>
+// One TM x 128 output tile (I, J) over the contraction range [kbeg, kend).
+template <typename T, int AOP, int BOP, int CM, bool BOOST = false, int TM = 128>
 __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, int split, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
-    const int r0 = I * BM, c0 = J * BN;
+    constexpr int FRM = WaveTile<TM>::FRM, FRN = WaveTile<TM>::FRN, TN = 128;
+    static_assert(TM == BM || (AOP != OP_SYM && AOP != OP_SYM_DG), "the symmetric operand takes 128 tiles");
+    const int r0 = I * TM, c0 = J * TN;
 
     // C -= AB runs as acc = C, acc += (-A) B: the accumulators start from C,
     // so the epilogue is a plain store and no accumulator has to leave the
     // matrix-core registers for a read-modify-write.
     constexpr bool FROM_C = (CM == C_SUB || CM == C_SUB_LOWER);
+    // a lower-only update has nothing to do on a tile above the diagonal
+    if (CM == C_SUB_LOWER && r0 + TM - 1 < c0)
+        return;
     // a tile inside M x N needs no per-entry bounds test: its loads of C and
     // its stores are issued back to back, without a branch around each one
-    const bool interior = r0 + BM <= p.M && c0 + BN <= p.N;
-    acc_t acc[4][4];
+    const bool interior = r0 + TM <= p.M && c0 + TN <= p.N;
+    acc_t acc[FRM][FRN];
     if (FROM_C && interior) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FRM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FRN; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     int row, col;
-                    acc_pos<T>(i, j, v, row, col);
+                    acc_pos<T, TM>(i, j, v, row, col);
                     acc[i][j][v] = p.c[(int64_t)(row + r0) * p.ldc + col + c0];
                 }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FRM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FRN; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     T x = T(0);
                     if (FROM_C) {
                         int row, col;
-                        acc_pos<T>(i, j, v, row, col);
+                        acc_pos<T, TM>(i, j, v, row, col);
                         row += r0;
                         col += c0;
                         if (row < p.M && col < p.N)
@@ -423,8 +446,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
                 }
     }
 
-    Operand<T, AOP> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
-    Operand<T, BOP> B{p.b, p.ldb, c0, p.N, p.vec, 0};
+    Operand<T, AOP, TM> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
+    Operand<T, BOP, TN> B{p.b, p.ldb, c0, p.N, p.vec, 0};
     if constexpr (AOP == OP_SYM || AOP == OP_SYM_DG) {
         // Sym(S)(m, k) for the tile's rows m in [r0, r0 + 128): left of the
         // diagonal block (k < r0) it is a row panel of S's lower triangle,
@@ -453,18 +476,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
             tile_mma<T, OP_KM, BOP, FROM_C, BOOST, true>(acc, Aa, B, a0, kend, lds);
         }
     } else {
-        tile_mma<T, AOP, BOP, FROM_C, BOOST>(acc, A, B, kbeg, kend, lds);
+        tile_mma<T, AOP, BOP, FROM_C, BOOST, false, TM>(acc, A, B, kbeg, kend, lds);
     }
 
-    if (interior && (CM != C_SUB_LOWER || I > J)) {
+    if (interior && (CM != C_SUB_LOWER || r0 >= c0 + TN - 1)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FRM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FRN; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     int row, col;
-                    acc_pos<T>(i, j, v, row, col);
+                    acc_pos<T, TM>(i, j, v, row, col);
                     row += r0;
                     col += c0;
                     if (CM == C_PARTIAL)
@@ -475,13 +498,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FRM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FRN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int row, col;
-                acc_pos<T>(i, j, v, row, col);
+                acc_pos<T, TM>(i, j, v, row, col);
                 row += r0;
                 col += c0;
                 if (row >= p.M || col >= p.N)
@@ -518,13 +541,20 @@ __device__ __forceinline__ void tile_of(int t, int tri, int TJ, int &I, int &J)
 // compiled in (the choice is then made at run time from p.sched).
 enum { SCHED_BOTH = 0, SCHED_DYN = 1, SCHED_STATIC = 2 };
 
-template <typename T, int AOP, int BOP, int CM, int SCHED>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Waves per SIMD the register allocation aims for: two blocks of 128-row
+// tiles per CU (256 registers each, 64 KB of LDS), or three of 64-row tiles
+// (half the accumulators, 48 KB of LDS).
+template <int TM> constexpr int gemm_waves() { return TM == 128 ? 2 : 3; }
+
+template <typename T, int AOP, int BOP, int CM, int SCHED, int TM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gemm_waves<TM>(), gemm_waves<TM>())))
 k_gemm(GemmArgs<T> p)
 {
     using namespace gemm_detail;
-    __shared__ T lds[LDS_ELEMS<T>];
-    const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
+    __shared__ T lds[LDS_ELEMS<T, TM>];
+    // tile grid: TM-row by 128-column tiles (the lower-triangular grid only
+    // with square tiles, TM = 128)
+    const int TI = (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
     const int nt = p.tn ? p.tn : (p.tri ? TI * (TI + 1) / 2 : TI * TJ);
 
     if (SCHED == SCHED_STATIC || (SCHED == SCHED_BOTH && !p.sched)) {
@@ -536,7 +566,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = blockIdx.y * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM, true>(p, I, J, blockIdx.y, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, true, TM>(p, I, J, blockIdx.y, kbeg, kend, lds);
         return;
     }
 
@@ -560,7 +590,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = split * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM, true>(p, I, J, split, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, true, TM>(p, I, J, split, kbeg, kend, lds);
     }
     // the last block to finish returns the counters to zero for the next launch
     if (threadIdx.x == 0) {
@@ -583,23 +613,29 @@ static inline bool aligned16(const T *p, int64_t ld)
     return ((uintptr_t)p % 16 == 0) && (ld % PER == 0) && ld < ((int64_t)1 << 24);
 }
 
-template <typename T, int AOP, int BOP, int CM>
+// C op= A B on the stream; TM: output tile rows (128, or 64 for short
+// products whose 128 x 128 tiles would be too few, or too long each, to
+// spread over the device; tiles are always 128 columns wide)
+template <typename T, int AOP, int BOP, int CM, int TM = 128>
 static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
 {
     using namespace gemm_detail;
     if (p.M <= 0 || p.N <= 0)
         return CHOL_OK;
+    if (TM != BM && p.tri)
+        return CHOL_ERR_INVALID_VALUE;           // the triangular tile grid needs square tiles
     p.vec = aligned16(p.a, p.lda) && aligned16(p.b, p.ldb);
     p.splits = splits;
     if constexpr (AOP == OP_SYM) {
+        static_assert(TM == BM, "the symmetric operand takes 128 tiles");
         // the excluded block is at most one tile; with a dense copy of every
         // diagonal block the product meets, the kernel reads them from it
         if (p.excl < 0 || p.excl > BM)
             return CHOL_ERR_INVALID_VALUE;
         if (p.dg && p.vec && p.M % BM == 0 && (p.excl == 0 || p.excl == BM) && ((uintptr_t)p.dg % 16) == 0)
-            return gemm<T, OP_SYM_DG, BOP, CM>(p, splits, st);
+            return gemm<T, OP_SYM_DG, BOP, CM, TM>(p, splits, st);
     }
-    const int TI = (p.M + BM - 1) / BM, TJ = (p.N + BN - 1) / BN;
+    const int TI = (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
     const int nt_all = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
     if (p.t0 < 0 || p.tn < 0 || p.t0 + (p.tn ? p.tn : nt_all) > nt_all)
         return CHOL_ERR_INVALID_VALUE;
@@ -612,11 +648,11 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1);
         const unsigned dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
         if (CM == C_SUB_LOWER)
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN>), dim3(dgrid), dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN, TM>), dim3(dgrid), dim3(NT), 0, st, p);
         else
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH>), dim3(dgrid), dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM>), dim3(dgrid), dim3(NT), 0, st, p);
     } else {
-        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH>), sgrid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM>), sgrid, dim3(NT), 0, st, p);
     }
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;

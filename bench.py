@@ -207,7 +207,8 @@ def main():
     ap.add_argument("--cpu-sample-n", type=int, default=5632)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters) and exit")
+                    help="only run the library's streaming kernels on 1 GiB (read, write, copy: the HBM "
+                         "ceiling, and the reference for the HBM byte counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -219,14 +220,31 @@ def main():
     import torch
 
     if args.calibrate_copy:
-        # a plain copy of a known size: rocprofv3's FETCH_SIZE / WRITE_SIZE of
-        # this kernel give the scale factor from counter KiB to HBM bytes
-        src = torch.ones(1 << 27, dtype=torch.float64, device="cuda")     # 1 GiB
+        # the library's own streaming kernels on 1 GiB buffers: the device-
+        # memory ceiling (read-only, write-only, copy), and a copy of known size
+        # whose rocprofv3 FETCH_SIZE / WRITE_SIZE give the scale factor from
+        # counter KiB to bytes
+        import differentiable_cholesky_amd as dc
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 8, dtype=torch.float64, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": src.numel() * 8, "launches": 3}), flush=True)
+        sink = torch.empty(dc._lib.HBM_READ_SINK_FLOATS, dtype=torch.float32, device="cuda")
+        out = {"calibrate_copy_bytes": nbytes}
+        for name, mode, a, b, moved in (("read", 0, src, sink, nbytes), ("write", 1, None, dst, nbytes),
+                                        ("copy", 2, src, dst, 2 * nbytes)):
+            reps = 10
+            dc.chol_hbm_stream(mode, a, b, nbytes)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(reps):
+                dc.chol_hbm_stream(mode, a, b, nbytes)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / reps
+            out[f"{name}_GBs"] = round(moved / (ms * 1e-3) / 1e9, 1)
+            out[f"{name}_us"] = round(ms * 1e3, 1)
+        out["launches_per_mode"] = 11
+        print(json.dumps(out), flush=True)
         return
 
     import differentiable_cholesky_amd as dc

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     MAX_NB,
     SMALL_MAX_N,
     chol_abi_version,
+    chol_hbm_stream,
     chol_init,
     chol_potrf,
     chol_potrf_adjoint,

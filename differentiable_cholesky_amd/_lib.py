@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.chol_potrf_adjoint_noalloc.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, i32, i64, vp]
     lib.chol_potrf_adjoint_batched.restype = st
     lib.chol_potrf_adjoint_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, vp]
+    lib.chol_hbm_stream.restype = st
+    lib.chol_hbm_stream.argtypes = [ctypes.c_int, vp, vp, sz, vp]
     lib.chol_wave_dot_fwd_adj.restype = st
     lib.chol_wave_dot_fwd_adj.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, i32, vp]
     lib.chol_status_string.restype = ctypes.c_char_p
@@ -247,6 +249,15 @@ def chol_wave_dot_fwd_adj(a, b, ybar, abar=None, bbar=None, staging: int = 0, st
     _check(lib.chol_wave_dot_fwd_adj(_dtype_code(a), a.numel(), p(a), p(b), p(y), p(ybar), p(abar), p(bbar),
                                      staging, _stream(stream)))
     return y, abar, bbar
+
+
+HBM_READ_SINK_FLOATS = 2048 * 256
+
+
+def chol_hbm_stream(mode: int, src, dst, nbytes: int, stream=None) -> None:
+    """Diagnostic streaming kernel: 0 read src, 1 write dst, 2 copy src to dst."""
+    p = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    _check(lib.chol_hbm_stream(mode, p(src), p(dst), nbytes, _stream(stream)))
 
 
 def chol_status_string(status: int) -> str:

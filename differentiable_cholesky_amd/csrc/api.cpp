@@ -32,6 +32,7 @@ template <typename T>
 chol_status blocked_adjoint_single_stream(int64_t n, const T *L, int64_t ldl, const T *adjL, int64_t ldal, T *adjA,
                                           int64_t ldaa, int accumulate, int nb, void *ws, int *sched, int cus,
                                           hipStream_t st);
+chol_status hbm_stream(int mode, const void *src, void *dst, size_t bytes, hipStream_t st);
 chol_status small_load();
 chol_status blocked_load();
 template <typename T>
@@ -334,6 +335,24 @@ chol_status chol_potrf_adjoint_batched(chol_dtype dt, int64_t n, int64_t batch, 
                                                  strideAA, accumulate, st);
     return chol::small_potrf_adjoint<float>((int)n, batch, (const float *)L, ldl, strideL, (const float *)adjL,
                                             ldal, strideAL, (float *)adjA, ldaa, strideAA, accumulate, st);
+}
+
+chol_status chol_hbm_stream(int mode, const void *src, void *dst, size_t bytes, void *stream)
+{
+    if (mode < 0 || mode > 2 || bytes % 16 != 0)
+        return CHOL_ERR_INVALID_VALUE;
+    if (bytes == 0)
+        return CHOL_OK;
+    if ((mode != 1 && (!src || (uintptr_t)src % 16)) || !dst || (uintptr_t)dst % 16)
+        return CHOL_ERR_INVALID_VALUE;
+    const size_t dst_bytes = mode == 0 ? (size_t)CHOL_HBM_READ_SINK_FLOATS * 4 : bytes;
+    if (mode != 1) {
+        const Extent a{(uintptr_t)src, (uintptr_t)src + bytes}, b{(uintptr_t)dst, (uintptr_t)dst + dst_bytes};
+        if (overlap(a, b))
+            return CHOL_ERR_INVALID_VALUE;
+    }
+    clear_stale_status();
+    return chol::hbm_stream(mode, src, dst, bytes, (hipStream_t)stream);
 }
 
 chol_status chol_wave_dot_fwd_adj(chol_dtype dt, int64_t n, const void *a, const void *b, void *y,

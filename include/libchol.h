@@ -217,6 +217,19 @@ chol_status chol_wave_dot_fwd_adj(chol_dtype dtype, int64_t n,
                                   int staging, void *stream);
 
 /*
+ * chol_hbm_stream -- diagnostic: plain streaming kernels that measure the
+ * device-memory ceiling the bandwidth-bound kernels are compared with.
+ *   mode 0  read `bytes` from src (dst receives CHOL_HBM_READ_SINK_FLOATS
+ *           floats of per-thread sums, so that no load is dropped);
+ *   mode 1  write `bytes` to dst;
+ *   mode 2  copy `bytes` from src to dst (disjoint).
+ * bytes must be a multiple of 16 and the pointers 16-byte aligned device
+ * pointers; otherwise CHOL_ERR_INVALID_VALUE.  Asynchronous on `stream`.
+ */
+#define CHOL_HBM_READ_SINK_FLOATS (2048 * 256)
+chol_status chol_hbm_stream(int mode, const void *src, void *dst, size_t bytes, void *stream);
+
+/*
  * Timing hook (diagnostics; used by the benchmark for per-kernel rooflines).
  * chol_profile_start(mask) clears previous records and turns timing on for
  * later calls in this process: each launch of a kernel family i below with

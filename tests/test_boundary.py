@@ -165,3 +165,12 @@ def test_noalloc_adjoint_argument_errors():
     assert f(F64, n, NUL, n, P2, n, P3, n, 1, 0, NUL) == INVALID
     assert f(F64, n, P1, n, P2, n, P3, n, 1, 129, NUL) == INVALID      # nb too large
     assert f(F64, 0, NUL, 0, NUL, 0, NUL, 0, 1, 0, NUL) == OK
+
+
+def test_hbm_stream_argument_errors():
+    f = lib.chol_hbm_stream
+    assert f(3, P1, P2, 1 << 20, NUL) == INVALID                       # unknown mode
+    assert f(2, P1, P2, (1 << 20) + 8, NUL) == INVALID                 # not a multiple of 16
+    assert f(2, P1, ctypes.c_void_p(0x10000000 + 64), 1 << 20, NUL) == INVALID   # overlapping copy
+    assert f(0, NUL, P2, 1 << 20, NUL) == INVALID                      # read without a source
+    assert f(2, P1, P2, 0, NUL) == OK

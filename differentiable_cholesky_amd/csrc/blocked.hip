@@ -45,7 +45,7 @@ enum { TRI_COPY_LOWER = 0, TRI_ZERO_UPPER = 1, TRI_ADD_LOWER = 2 };
 // 32 x 32 element tiles; a block covers one tile with 256 threads.
 template <typename T, int MODE>
 __global__ void __launch_bounds__(256)
-k_tri(int64_t n, const T *src, int64_t lds, T *dst, int64_t ldd)
+k_tri(int64_t n, int64_t w, const T *src, int64_t lds, T *dst, int64_t ldd)
 {
     const int64_t i0 = (int64_t)blockIdx.y * 32, j0 = (int64_t)blockIdx.x * 32;
     if (MODE == TRI_ZERO_UPPER ? (j0 + 31 <= i0) : (j0 > i0 + 31))
@@ -53,7 +53,7 @@ k_tri(int64_t n, const T *src, int64_t lds, T *dst, int64_t ldd)
     const int tj = threadIdx.x % 32, ti = threadIdx.x / 32;
     for (int r = ti; r < 32; r += 8) {
         const int64_t i = i0 + r, j = j0 + tj;
-        if (i >= n || j >= n)
+        if (i >= n || j >= w)
             continue;
         if (MODE == TRI_COPY_LOWER) {
             if (j <= i)
@@ -68,15 +68,23 @@ k_tri(int64_t n, const T *src, int64_t lds, T *dst, int64_t ldd)
     }
 }
 
+// the entries of the n x n operand in columns 0 .. w-1 (w <= n; the lower ones
+// for COPY_LOWER and ADD_LOWER, the strict upper ones for ZERO_UPPER)
 template <typename T, int MODE>
-static chol_status tri_op(int64_t n, const T *src, int64_t lds, T *dst, int64_t ldd, hipStream_t st)
+static chol_status tri_op(int64_t n, const T *src, int64_t lds, T *dst, int64_t ldd, hipStream_t st,
+                          int64_t w = -1)
 {
-    const double tri = (double)n * (n + 1) / 2, es = (double)sizeof(T);
+    if (w < 0 || w > n)
+        w = n;
+    // lower entries of the first w columns: w (n - w) + w (w + 1) / 2
+    const double tri = (double)w * (n - w) + (double)w * (w + 1) / 2, es = (double)sizeof(T);
     const double bytes = MODE == TRI_COPY_LOWER ? 2 * tri * es
-                       : MODE == TRI_ZERO_UPPER ? ((double)n * n - tri) * es : 3 * tri * es;
+                       : MODE == TRI_ZERO_UPPER ? ((double)n * w - tri) * es : 3 * tri * es;
     prof::Scope ps(CHOL_K_ELEMENTWISE, st, bytes);
-    const unsigned t = (unsigned)((n + 31) / 32);
-    hipLaunchKernelGGL((k_tri<T, MODE>), dim3(t, t), dim3(256), 0, st, n, src, lds, dst, ldd);
+    const unsigned tr = (unsigned)((n + 31) / 32), tc = (unsigned)((w + 31) / 32);
+    if (tr == 0 || tc == 0)
+        return CHOL_OK;
+    hipLaunchKernelGGL((k_tri<T, MODE>), dim3(tc, tr), dim3(256), 0, st, n, w, src, lds, dst, ldd);
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;
 }
@@ -248,8 +256,10 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
     // lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T with Q = panels f .. f+np-1
     // (tile columns f .. f+np-1 of L); tri: the whole trailing triangle W[c:, c:]
     // instead, restricted to the 128 x 128 tiles t0 .. t0+tn-1 (row-major over
-    // the lower tiles), taken by persistent blocks
-    auto lower_update = [&](int64_t c, int64_t w, int64_t f, int np, bool tri, int t0, int tn) -> chol_status {
+    // the lower tiles), taken by persistent blocks; from_a: W's current values
+    // are those of A (the tiles' first update), the results go to L
+    auto lower_update = [&](int64_t c, int64_t w, int64_t f, int np, bool tri, int t0, int tn,
+                            bool from_a) -> chol_status {
         const int64_t M = n - c;
         const int Kd = np * nb;
         GemmArgs<T> p{};
@@ -257,6 +267,10 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         p.a = L + c * ldl + f * nb; p.lda = ldl;
         p.b = L + c * ldl + f * nb; p.ldb = ldl;
         p.c = L + c * ldl + c; p.ldc = ldl;
+        if (from_a) {
+            p.cin = A + c * lda + c;
+            p.ldcin = lda;
+        }
         double flops;
         if (tri) {
             p.tri = 1;
@@ -292,7 +306,7 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         chol_status s = CHOL_OK;
         switch (o.kind) {
         case FWD_COPY:
-            s = tri_op<T, TRI_COPY_LOWER>(n, A, lda, L, ldl, sc);
+            s = tri_op<T, TRI_COPY_LOWER>(n, A, lda, L, ldl, sc, o.w);
             break;
         case FWD_DIAG: {
             const int64_t k0 = o.k * nb;
@@ -320,10 +334,10 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             break;
         }
         case FWD_UPDATE:
-            s = lower_update(o.c, o.w, o.f, o.np, false, 0, 0);
+            s = lower_update(o.c, o.w, o.f, o.np, false, 0, 0, false);
             break;
         case FWD_TRI:
-            s = lower_update(o.c, 0, o.f, o.np, true, o.t0, o.tn);
+            s = lower_update(o.c, 0, o.f, o.np, true, o.t0, o.tn, o.slot == 1);
             break;
         case FWD_JOIN: {
             hipEvent_t ev = o.slot == 0 ? e_diag : e_next;

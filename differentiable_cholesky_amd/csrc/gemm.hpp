@@ -56,6 +56,8 @@ template <typename T> struct GemmArgs {
     const T *a; int64_t lda;
     const T *b; int64_t ldb;
     T *c; int64_t ldc;
+    const T *cin; int64_t ldcin;  // C_SUB, C_SUB_LOWER, optional: C's values read
+                         // from here (same shape) and the results written to c
     int kchunk;          // split-K: contraction length per split (multiple of 32)
     T *part;             // C_PARTIAL destination, splits * M * N
     int tri;             // 1: lower-triangular tile grid (M == N)
@@ -414,6 +416,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
     // a tile inside M x N needs no per-entry bounds test: its loads of C and
     // its stores are issued back to back, without a branch around each one
     const bool interior = r0 + TM <= p.M && c0 + TN <= p.N;
+    const T *cin = p.cin ? p.cin : p.c;
+    const int64_t ldcin = p.cin ? p.ldcin : p.ldc;
     acc_t acc[FRM][FRN];
     if (FROM_C && interior) {
 #pragma unroll
@@ -424,7 +428,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
                 for (int v = 0; v < 4; ++v) {
                     int row, col;
                     acc_pos<T, TM>(i, j, v, row, col);
-                    acc[i][j][v] = p.c[(int64_t)(row + r0) * p.ldc + col + c0];
+                    acc[i][j][v] = cin[(int64_t)(row + r0) * ldcin + col + c0];
                 }
     } else {
 #pragma unroll
@@ -440,7 +444,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
                         row += r0;
                         col += c0;
                         if (row < p.M && col < p.N)
-                            x = p.c[(int64_t)row * p.ldc + col];
+                            x = cin[(int64_t)row * ldcin + col];
                     }
                     acc[i][j][v] = x;
                 }

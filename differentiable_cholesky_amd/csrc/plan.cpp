@@ -29,6 +29,10 @@ namespace chol {
 // The diagonal tiles' inverses alternate between two slots: the panel solve
 // of tile column k reads slot k % 2 while tile column k+1 is factored into
 // the other one.
+// With A apart from L, only the tile columns left of the first group's far
+// triangle are copied from A into L: that triangle's tiles receive their
+// first update from the first group's far-triangle parts, which read them
+// from A and write them to L (copy and update in one pass).
 std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
 {
     std::vector<FwdOp> ops;
@@ -48,12 +52,18 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
         const int64_t TI = (n - c + 127) / 128;
         return (int)(TI * (TI + 1) / 2);
     };
-    if (copy)
-        op(FWD_COPY, FWD_CHAIN);
+    if (copy) {
+        // columns left of the first group's far triangle (all of them when
+        // the matrix has no such triangle)
+        const int64_t first_far = std::min<int64_t>(nb, n) + (int64_t)FWD_DEFER * nb;
+        op(FWD_COPY, FWD_CHAIN).w = first_far < n ? first_far : n;
+    }
     diag(0, FWD_CHAIN);
-    // the far triangle of the current group: first column, panels, tile count
+    // the far triangle of the current group: first column, panels, tile count,
+    // whether its tiles are read from A (the first group's, when copying)
     int64_t fcol = -1, ff = 0;
     int fnp = 0, ftiles = 0;
+    bool ffrom_a = false;
     bool diag_wide = false;   // the last diagonal tile was factored on the wide stream
     for (int64_t k = 0; k < K; ++k) {
         const int64_t k0 = k * nb;
@@ -83,6 +93,7 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
                 ff = f;
                 fnp = np;
                 ftiles = tri_tiles(fcol);
+                ffrom_a = copy && k == 0;
             } else {
                 fcol = -1;
             }
@@ -107,6 +118,7 @@ std::vector<FwdOp> forward_plan(int64_t n, int nb, bool copy, int slots)
             o.np = fnp;
             o.t0 = t0;
             o.tn = t1 - t0;
+            o.slot = ffrom_a ? 1 : -1;
             diag_wide = false;
         } else {
             // nothing to run beside the diagonal factor: it follows the

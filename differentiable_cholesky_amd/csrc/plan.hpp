@@ -13,12 +13,13 @@
 namespace chol {
 
 enum FwdKind {
-    FWD_COPY = 0,        // chain: lower triangle of A into L
+    FWD_COPY = 0,        // chain: lower part of columns 0 .. w-1 of A into L
     FWD_DIAG = 1,        // chain (or wide, with nothing beside it): factor tile column k's diagonal
                          // tile; slot >= 0: its inverse into slot
     FWD_PANEL = 2,       // wide: panel solve of tile column k (rows below its tile), reading slot
     FWD_UPDATE = 3,      // wide: lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T, Q = panels f .. f+np-1
     FWD_TRI = 4,         // wide: lower tiles t0 .. t0+tn-1 (128 x 128, row-major) of W[c:, c:] -= Q Q^T
+                         // (slot 1: W read from A, the tiles' first update)
     FWD_JOIN = 5,        // `stream` waits for everything enqueued so far on the other stream (event ev)
     FWD_ZERO_UPPER = 6   // chain: strict upper triangle of L set to zero
 };
@@ -30,7 +31,7 @@ struct FwdOp {
     int64_t c, w, f;     // FWD_UPDATE, FWD_TRI (w unused for FWD_TRI)
     int32_t np, t0, tn;  // panels; FWD_TRI tile window
     int32_t slot;        // FWD_DIAG: inverse slot written (-1: none); FWD_PANEL: slot read;
-                         // FWD_JOIN: event index
+                         // FWD_JOIN: event index; FWD_TRI: 1 if the tiles are read from A
 };
 
 // depth of the deferred trailing update: the far triangle is updated with

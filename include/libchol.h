@@ -289,7 +289,9 @@ int chol_abi_version(void);
  * panels.  Host only: calls no GPU function.
  *   ops  [out] host, cap rows of CHOL_PLAN_FIELDS int64 each (may be NULL if
  *              cap == 0), one row per operation in enqueue order:
- *     kind    0 copy lower(A) into L (chain stream)
+ *     kind    0 copy the lower part of columns 0 .. w-1 of A into L (chain
+ *               stream); the columns right of them are brought over by the
+ *               first kind-4 operations, which read A (slot 1)
  *             1 factor diagonal tile k (chain stream, or wide where no
  *               far-triangle part runs beside it); slot >= 0: its inverse
  *               is written whole into inverse slot `slot`
@@ -298,7 +300,9 @@ int chol_abi_version(void);
  *             3 lower part of W[c:, c:c+w] -= Q[c:] Q[c:c+w]^T with Q the
  *               tile columns f .. f+np-1 of L (wide)
  *             4 the lower 128 x 128 tiles t0 .. t0+tn-1 (row-major) of the
- *               trailing triangle W[c:, c:] -= Q Q^T, same Q (wide)
+ *               trailing triangle W[c:, c:] -= Q Q^T, same Q (wide); slot 1:
+ *               W's values are read from A (the tiles' first update, in
+ *               place of their copy), -1: from L
  *             5 `stream` waits for every operation enqueued so far on the
  *               other stream
  *             6 clear the strict upper triangle of L (chain)

@@ -3,11 +3,14 @@ chol_potrf_plan (the list of operations chol_potrf enqueues, with the joins
 between its two streams).  Two properties, on cells of g x g elements
 (g = gcd(nb, 128), so every operation covers whole cells):
 
-* panel bookkeeping: every trailing-update operation subtracts each panel's
-  product from a cell at most once, each tile column holds exactly the
-  products of the panels left of it when its diagonal tile is factored and
-  when its panel is solved, and at the end every lower cell holds exactly
-  the panels left of its tile column;
+* panel bookkeeping: every lower cell is brought over from A exactly once,
+  before anything else touches it (by the copy, or by the far-triangle
+  update that reads A, which must then be the cell's first update); every
+  trailing-update operation subtracts each panel's product from a cell at
+  most once, each tile column holds exactly the products of the panels left
+  of it when its diagonal tile is factored and when its panel is solved, and
+  at the end every lower cell holds exactly the panels left of its tile
+  column;
 * ordering: any two operations that touch the same data (a cell of the
   matrix or an inverse slot), at least one of them writing it, are ordered
   by stream order or by a join.
@@ -50,6 +53,9 @@ def _check(n, nb, plan=None, slots=480):
     lower_all = _mask(C, (0, C), (0, C), True)
 
     applied = {}                               # lower cell -> bitmask of panels applied
+    loaded = set()                             # lower cells that hold A's values (or later ones)
+    if not any(int(row[0]) == COPY for row in plan):
+        loaded = {(a, b) for a in range(C) for b in range(a + 1)}   # in place: L is A
     clock = [[0, 0], [0, 0]]                   # per stream: known positions of (chain, wide)
     pos = [0, 0]
     done = []                                  # (stream, position, clock, reads, writes)
@@ -58,14 +64,19 @@ def _check(n, nb, plan=None, slots=480):
         k0 = k * nbe
         for b in range(cell(k0), cell(min(k0 + nbe, n))):
             for a in range(b, C):
+                assert (a, b) in loaded, (n, nb, "tile column", k, "cell never loaded from A", (a, b))
                 got = applied.get((a, b), 0)
                 assert got == (1 << k) - 1, (n, nb, "tile column", k, "cell", (a, b), bin(got))
 
-    def apply(rows_c, cols_c, f, np_, lower_rule):
+    def apply(rows_c, cols_c, f, np_, lower_rule, from_a=False):
         pm = ((1 << np_) - 1) << f
         for a in range(*rows_c):
             for b in range(*cols_c):
                 if a >= b and lower_rule(a, b):
+                    if from_a:
+                        assert (a, b) not in loaded, (n, nb, "cell loaded from A twice", (a, b))
+                        loaded.add((a, b))
+                    assert (a, b) in loaded, (n, nb, "cell updated before it holds A", (a, b))
                     got = applied.get((a, b), 0)
                     assert not got & pm, (n, nb, "panel applied twice", (a, b), f, np_)
                     applied[(a, b)] = got | pm
@@ -80,7 +91,12 @@ def _check(n, nb, plan=None, slots=480):
             clock[stream][other] = max(clock[stream][other], pos[other])
             continue
         if kind == COPY:
-            writes = lower_all
+            assert 0 < w <= n, (n, nb, "copy width", w)
+            for a in range(C):
+                for b in range(min(a + 1, cell(w))):
+                    assert (a, b) not in loaded, (n, nb, "cell loaded from A twice", (a, b))
+                    loaded.add((a, b))
+            writes = _mask(C, (0, C), (0, cell(w)), True)
         elif kind == ZERO:
             writes = _mask(C, (0, C), (0, C), False) & ~_mask(C, (0, C), (0, C), True) | \
                 sum(1 << (a * C + a) for a in range(C))
@@ -112,10 +128,11 @@ def _check(n, nb, plan=None, slots=480):
             TI = (M + 127) // 128
             tiles = [(I, J) for I in range(TI) for J in range(I + 1)]
             assert 0 <= t0 and t0 + tn <= len(tiles) and tn > 0
+            assert slot in (-1, 1), (n, nb, "far-triangle source", slot)
             for I, J in tiles[t0:t0 + tn]:
                 rows_c = (cell(c + 128 * I), cell(min(c + 128 * I + 128, n)))
                 cols_c = (cell(c + 128 * J), cell(min(c + 128 * J + 128, n)))
-                apply(rows_c, cols_c, f, np_, lambda a, b: True)
+                apply(rows_c, cols_c, f, np_, lambda a, b: True, from_a=slot == 1)
                 writes |= _mask(C, rows_c, cols_c, True)
             reads = _mask(C, (cell(c), C), (cell(f * nbe), cell((f + np_) * nbe)), False)
         else:
@@ -131,6 +148,7 @@ def _check(n, nb, plan=None, slots=480):
 
     for a in range(C):
         for b in range(a + 1):
+            assert (a, b) in loaded, (n, nb, "final: cell never loaded from A", (a, b))
             want = (1 << ((b * g) // nbe)) - 1
             assert applied.get((a, b), 0) == want, (n, nb, "final", (a, b))
 
@@ -191,7 +209,22 @@ def _mutants(plan):
     bad[i, 5] += 1
     bad[i, 6] -= 1
     out.append(("panel missing", bad))
+    # the copy one tile column short: the first far triangle's tiles are
+    # read from A, but that column's cells are never brought over
+    bad = plan.copy()
+    assert bad[0, 0] == COPY
+    bad[0, 4] -= nb_of(plan)
+    out.append(("copy short", bad))
+    # a later far-triangle part that reads A: it would discard earlier updates
+    bad = plan.copy()
+    late = [i for i in tri if plan[i, 9] != 1]
+    bad[late[0], 9] = 1
+    out.append(("late part reads A", bad))
     return out
+
+
+def nb_of(plan):
+    return int(next(row[4] for row in plan if row[0] == UPDATE and row[6] == 1))
 
 
 @pytest.mark.parametrize("n,nb", [(1300, 128), (2100, 96)])
@@ -201,6 +234,23 @@ def test_schedule_check_catches_planted_mistakes(n, nb):
         with pytest.raises(AssertionError):
             _check(n, nb, bad)
         assert name
+
+
+def test_first_far_triangle_read_from_a():
+    # with A apart from L only the columns left of the first far triangle are
+    # copied; the first group's parts read A.  In place (copy=False), nothing
+    # reads A.
+    for n, nb in [(16384, 128), (2100, 96)]:
+        plan = dc.chol_potrf_plan(n, nb, copy=True)
+        assert plan[0, 0] == COPY and plan[0, 4] == 5 * nb
+        tri = plan[plan[:, 0] == TRI]
+        first = tri[:, 5] == 0                    # the first group's parts: panel 0 alone
+        assert first.any() and (tri[first, 9] == 1).all() and (tri[~first, 9] == -1).all()
+        inplace = dc.chol_potrf_plan(n, nb, copy=False)
+        assert (inplace[:, 0] != COPY).all() and (inplace[inplace[:, 0] == TRI][:, 9] == -1).all()
+        _check(n, nb, inplace)
+    plan = dc.chol_potrf_plan(600, 128, copy=True)     # no far triangle: everything copied
+    assert plan[0, 4] == 600 and not (plan[:, 0] == TRI).any()
 
 
 def test_plan_argument_errors():

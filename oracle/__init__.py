@@ -19,6 +19,12 @@ What each function computes, and the pages it follows, is stated in
                           factorisation, used only to cross-check the formula.
 * ``dot`` / ``dot_adjoint`` -- y = a.b and a_bar += y_bar b, b_bar += y_bar a
                           (Warp issue #1374, description and repro).
+* ``potrs``            -- X = (L L^T)^{-1} B by forward and back substitution
+                          against L (the solve the factor is returned for,
+                          jaxmg docs, "Cholesky factorization"; the two
+                          triangular solves of Warp issue #1316).
+* ``potrs_adjoint``    -- adj_B = (L L^T)^{-1} adj_X and
+                          adj_L = -tril((adj_B X^T + X adj_B^T) L).
 
 Every array argument is a NumPy array; inputs of any float dtype are promoted
 to fp64 exactly (float32 -> float64 is exact).
@@ -72,6 +78,10 @@ def _load_path(path: str):
     lib.oracle_potrf_adjoint_batched.restype = i32
     lib.oracle_potrf_adjoint_batched.argtypes = [i64, i64, dp, i64, i64, dp, i64, i64,
                                                  dp, i64, i64, i32]
+    lib.oracle_potrs.restype = None
+    lib.oracle_potrs.argtypes = [i64, i64, dp, i64, dp, i64, dp, i64]
+    lib.oracle_potrs_adjoint.restype = i32
+    lib.oracle_potrs_adjoint.argtypes = [i64, i64, dp, i64, dp, i64, dp, i64, dp, i64, dp, i64, i32]
     lib.oracle_dot.restype = ctypes.c_double
     lib.oracle_dot.argtypes = [i64, dp, dp]
     lib.oracle_dot_adjoint.restype = None
@@ -173,3 +183,55 @@ def dot_adjoint(a, b, ybar: float):
     bbar = np.zeros_like(b)
     _load().oracle_dot_adjoint(a.size, _ptr(a), _ptr(b), float(ybar), _ptr(abar), _ptr(bbar))
     return abar, bbar
+
+
+def _rhs(B, n):
+    B = _f64(B)
+    vec = B.ndim == 1
+    B2 = B.reshape(n, 1) if vec else B
+    assert B2.shape[0] == n
+    return np.ascontiguousarray(B2), vec
+
+
+def potrs(L, B):
+    """X = (L L^T)^{-1} B for one lower factor L (n x n) and B (n or n x nrhs),
+    or for stacked ``[batch, n, n]`` / ``[batch, n, nrhs]`` arrays.  Only the
+    lower triangle of L is read."""
+    L = _f64(L)
+    lib = _load()
+    if L.ndim == 3:
+        B = _f64(B)
+        return np.stack([potrs(L[b], B[b]) for b in range(L.shape[0])])
+    n = L.shape[0]
+    B2, vec = _rhs(B, n)
+    X = np.zeros_like(B2)
+    nrhs = B2.shape[1]
+    lib.oracle_potrs(n, nrhs, _ptr(L), n, _ptr(B2), nrhs, _ptr(X), nrhs)
+    return X.reshape(-1) if vec else X
+
+
+def potrs_adjoint(L, X, adjX, adjL=None, accumulate: bool = True):
+    """Adjoint of X = potrs(L, B): returns ``(adj_B, adj_L)`` with adj_B =
+    (L L^T)^{-1} adj_X and the lower triangle of adj_L incremented by
+    (``accumulate``) or set to (otherwise) -tril((adj_B X^T + X adj_B^T) L);
+    adj_L's strict upper triangle is returned unchanged (zero if not given).
+    Stacked ``[batch, ...]`` arrays are handled element by element."""
+    L = _f64(L)
+    lib = _load()
+    if L.ndim == 3:
+        X, adjX = _f64(X), _f64(adjX)
+        outs = [potrs_adjoint(L[b], X[b], adjX[b], None if adjL is None else _f64(adjL)[b], accumulate)
+                for b in range(L.shape[0])]
+        return np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs])
+    n = L.shape[0]
+    X2, vec = _rhs(X, n)
+    aX2, _ = _rhs(adjX, n)
+    nrhs = X2.shape[1]
+    assert aX2.shape == X2.shape
+    adjB = np.zeros_like(X2)
+    out = np.zeros_like(L) if adjL is None else _f64(adjL).copy()
+    rc = lib.oracle_potrs_adjoint(n, nrhs, _ptr(L), n, _ptr(X2), nrhs, _ptr(aX2), nrhs, _ptr(adjB), nrhs,
+                                  _ptr(out), n, 1 if accumulate else 0)
+    if rc != 0:
+        raise MemoryError("oracle potrs adjoint could not allocate its scratch matrix")
+    return (adjB.reshape(-1) if vec else adjB), out

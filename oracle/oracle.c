@@ -251,6 +251,86 @@ int32_t oracle_potrf_adjoint_batched(int64_t n, int64_t batch,
     return bad ? -1 : 0;
 }
 
+/* Solve with the factor: X = A^{-1} B for A = L L^T, B and X n x nrhs
+ * (row-major, leading dimensions ldb, ldx).  The factor is returned without a
+ * solve [jaxmg-potrf]; this is the solve it is computed for, written as the
+ * two triangular solves against L that [warp-1316] names for the adjoint:
+ *   L Y = B     forward substitution:  Y_i = (B_i - sum_{k<i} L_ik Y_k) / L_ii
+ *   L^T X = Y   back substitution:     X_i = (Y_i - sum_{k>i} L_ki X_k) / L_ii
+ * (rows i; each right-hand-side column on its own).  Only the lower triangle of
+ * L is read.  X may be B itself (then B is overwritten); otherwise they must
+ * not overlap. */
+void oracle_potrs(int64_t n, int64_t nrhs, const double *L, int64_t ldl,
+                  const double *B, int64_t ldb, double *X, int64_t ldx)
+{
+    if (n <= 0 || nrhs <= 0)
+        return;
+    if (X != B)
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t c = 0; c < nrhs; ++c)
+                AT(X, ldx, i, c) = AT(B, ldb, i, c);
+#pragma omp parallel for schedule(static) if (nrhs > 1 && n * nrhs > 4096)
+    for (int64_t c = 0; c < nrhs; ++c) {
+        for (int64_t i = 0; i < n; ++i) {
+            double s = AT(X, ldx, i, c);
+            for (int64_t k = 0; k < i; ++k)
+                s -= AT(L, ldl, i, k) * AT(X, ldx, k, c);
+            AT(X, ldx, i, c) = s / AT(L, ldl, i, i);
+        }
+        for (int64_t i = n - 1; i >= 0; --i) {
+            double s = AT(X, ldx, i, c);
+            for (int64_t k = i + 1; k < n; ++k)
+                s -= AT(L, ldl, k, i) * AT(X, ldx, k, c);
+            AT(X, ldx, i, c) = s / AT(L, ldl, i, i);
+        }
+    }
+}
+
+/* Adjoint of X = (L L^T)^{-1} B, given adj_X (reverse mode).  With A = L L^T,
+ * dX = -A^{-1} dA X and dA = dL L^T + L dL^T, so for any adj_X
+ *   <adj_X, dX> = <adj_B, dB> - <(adj_B X^T + X adj_B^T) L, dL>,
+ *   adj_B = A^{-1} adj_X                     (the same two triangular solves)
+ * and the gradient with respect to the lower entries of L is
+ *   adj_L = -tril((adj_B X^T + X adj_B^T) L).
+ * adj_B is written (it may be adj_X itself); lower(adj_L) += adj_L
+ * (accumulate != 0) or = adj_L (accumulate == 0); the strict upper triangle of
+ * adj_L is not touched.  Returns 0, or -1 if the scratch allocation fails. */
+int32_t oracle_potrs_adjoint(int64_t n, int64_t nrhs, const double *L, int64_t ldl,
+                             const double *X, int64_t ldx, const double *adjX, int64_t ldax,
+                             double *adjB, int64_t ldab, double *adjL, int64_t ldal,
+                             int32_t accumulate)
+{
+    if (n <= 0)
+        return 0;
+    oracle_potrs(n, nrhs, L, ldl, adjX, ldax, adjB, ldab);
+    double *W = (double *)calloc((size_t)n * (size_t)n, sizeof(double));
+    if (!W)
+        return -1;
+    /* W = adj_B X^T + X adj_B^T */
+#pragma omp parallel for schedule(static) if (n > 64)
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = 0; k < n; ++k) {
+            double w = 0.0;
+            for (int64_t c = 0; c < nrhs; ++c)
+                w += AT(adjB, ldab, i, c) * AT(X, ldx, k, c) + AT(X, ldx, i, c) * AT(adjB, ldab, k, c);
+            W[(size_t)i * n + k] = w;
+        }
+    /* adj_L_ij = -sum_{k >= j} W_ik L_kj  for i >= j */
+#pragma omp parallel for schedule(static) if (n > 64)
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j <= i; ++j) {
+            double g = 0.0;
+            for (int64_t k = j; k < n; ++k)
+                g += W[(size_t)i * n + k] * AT(L, ldl, k, j);
+            if (accumulate)
+                AT(adjL, ldal, i, j) -= g;
+            else
+                AT(adjL, ldal, i, j) = -g;
+        }
+    free(W);
+    return 0;
+}
+
 /* Dot product and its adjoint [warp-1374]:
  *   y = sum_k a_k b_k ;   a_bar_k += y_bar b_k ;   b_bar_k += y_bar a_k. */
 double oracle_dot(int64_t n, const double *a, const double *b)

@@ -228,3 +228,112 @@ def test_tile_dot_values_from_warp_1374():
     assert np.array_equal(abar, g["grad_a"])
     assert np.array_equal(bbar, g["grad_b"])
     assert not np.array_equal(abar, g["grad_a_missing_broadcast"])
+
+
+# ------------------------------------------------------------------ solve ----
+# The solve with the factor (X = A^{-1} B for A = L L^T) and its adjoint, pinned
+# against a library solve, closed forms, finite differences and, for the
+# adjoint, the matrix-calculus gradient of <C, A^{-1} B> with respect to A.
+
+def _spd_and_factor(n, seed):
+    rng = np.random.default_rng(seed)
+    G = rng.standard_normal((n, n))
+    A = G @ G.T / n + np.eye(n)
+    L, info = oracle.potrf(A)
+    assert info == 0
+    return rng, A, L
+
+
+@pytest.mark.parametrize("n,nrhs", [(1, 1), (5, 1), (17, 3), (64, 64), (130, 7)])
+def test_potrs_matches_library_solve(n, nrhs):
+    rng, A, L = _spd_and_factor(n, 10 + n)
+    B = rng.standard_normal((n, nrhs))
+    X = oracle.potrs(L, B)
+    Xref = np.linalg.solve(L @ L.T, B)
+    assert np.max(np.abs(X - Xref)) <= 1e-12 * max(1.0, np.max(np.abs(Xref)))
+    # and the residual against A itself
+    assert np.max(np.abs(A @ X - B)) <= 1e-11 * max(1.0, np.max(np.abs(B)))
+
+
+def test_potrs_closed_forms():
+    rng = np.random.default_rng(4)
+    B = rng.standard_normal((6, 2))
+    # identity factor: X = B exactly
+    assert np.array_equal(oracle.potrs(np.eye(6), B), B)
+    # diagonal factor: X_ic = B_ic / d_i^2
+    d = np.array([1.0, 2.0, 0.5, 4.0, 3.0, 0.25])
+    X = oracle.potrs(np.diag(d), B)
+    assert np.max(np.abs(X - B / (d * d)[:, None])) <= 1e-15 * np.max(np.abs(B / (d * d)[:, None]))
+    # 1 x 1: x = b / l^2
+    assert oracle.potrs(np.array([[3.0]]), np.array([18.0]))[0] == 2.0
+    # 2 x 2 by hand: L = [[2, 0], [1, 3]], A = [[4, 2], [2, 10]], b = (6, 14):
+    # y = (3, 11/3), x2 = 11/9, x1 = (3 - 11/9) / 2 = 8/9; check A x = b
+    x = oracle.potrs(np.array([[2.0, 0.0], [1.0, 3.0]]), np.array([6.0, 14.0]))
+    assert np.max(np.abs(x - np.array([8.0 / 9.0, 11.0 / 9.0]))) <= 4e-16
+
+
+def test_potrs_reads_only_the_lower_triangle():
+    rng, A, L = _spd_and_factor(9, 5)
+    B = rng.standard_normal((9, 2))
+    Lu = L.copy()
+    Lu[np.triu_indices(9, 1)] = np.nan
+    assert np.array_equal(oracle.potrs(Lu, B), oracle.potrs(L, B))
+
+
+@pytest.mark.parametrize("n,nrhs", [(1, 1), (3, 2), (6, 3)])
+def test_potrs_adjoint_central_finite_differences(n, nrhs):
+    rng, A, L = _spd_and_factor(n, 20 + n)
+    B = rng.standard_normal((n, nrhs))
+    C = rng.standard_normal((n, nrhs))                 # adj_X
+    X = oracle.potrs(L, B)
+    adjB, adjL = oracle.potrs_adjoint(L, X, C)
+    f = lambda L_, B_: float(np.sum(C * oracle.potrs(L_, B_)))
+    eps = 1e-6
+    for i in range(n):
+        for c in range(nrhs):
+            Bp, Bm = B.copy(), B.copy()
+            Bp[i, c] += eps
+            Bm[i, c] -= eps
+            fd = (f(L, Bp) - f(L, Bm)) / (2 * eps)
+            assert abs(fd - adjB[i, c]) <= 1e-7 * max(1.0, abs(fd))
+        for j in range(i + 1):
+            Lp, Lm = L.copy(), L.copy()
+            Lp[i, j] += eps
+            Lm[i, j] -= eps
+            fd = (f(Lp, B) - f(Lm, B)) / (2 * eps)
+            assert abs(fd - adjL[i, j]) <= 1e-7 * max(1.0, abs(fd))
+    assert np.all(np.triu(adjL, 1) == 0.0)
+
+
+def test_potrs_adjoint_chained_with_factor_adjoint_matches_matrix_calculus():
+    # f(A) = <C, A^{-1} B> with A symmetric, parameterised by its lower entries:
+    # df/dA = -(A^{-1} C)(A^{-1} B)^T =: -W, so the lower-entry gradient is
+    # -(W + W^T) below the diagonal and -W_ii on it.  Chaining the solve's
+    # adjoint (adj_L) into the factor's adjoint must give exactly that.
+    n, nrhs = 12, 4
+    rng, A, L = _spd_and_factor(n, 31)
+    B = rng.standard_normal((n, nrhs))
+    C = rng.standard_normal((n, nrhs))
+    X = oracle.potrs(L, B)
+    _, adjL = oracle.potrs_adjoint(L, X, C)
+    adjA = oracle.potrf_adjoint(L, adjL)
+    W = np.linalg.solve(A, C) @ np.linalg.solve(A, B).T
+    want = -(W + W.T)
+    want[np.diag_indices(n)] = -np.diag(W)
+    want = np.tril(want)
+    assert np.max(np.abs(np.tril(adjA) - want)) <= 1e-11 * np.max(np.abs(want))
+
+
+def test_potrs_adjoint_accumulate_and_overwrite():
+    n, nrhs = 7, 2
+    rng, A, L = _spd_and_factor(n, 41)
+    X = oracle.potrs(L, rng.standard_normal((n, nrhs)))
+    C = rng.standard_normal((n, nrhs))
+    start = rng.standard_normal((n, n))
+    _, g0 = oracle.potrs_adjoint(L, X, C)
+    _, acc = oracle.potrs_adjoint(L, X, C, adjL=start, accumulate=True)
+    _, ovw = oracle.potrs_adjoint(L, X, C, adjL=start, accumulate=False)
+    low = np.tril(np.ones((n, n), bool))
+    assert np.allclose(acc[low], start[low] + g0[low], rtol=0, atol=1e-14)
+    assert np.array_equal(ovw[low], g0[low])
+    assert np.array_equal(acc[~low], start[~low]) and np.array_equal(ovw[~low], start[~low])

@@ -42,6 +42,18 @@ MUTATIONS = [
      "const double g = (i == j) ? 2.0 * S[(size_t)i * n + i]"),
     ("adj_overwrites_when_accumulating", "AT(adjA, ldaa, i, j) += g;", "AT(adjA, ldaa, i, j) = g;"),
     ("dot_reversed_index", "y += a[k] * b[k];", "y += a[k] * b[n - 1 - k];"),
+    ("potrs_forward_sign", "s -= AT(L, ldl, i, k) * AT(X, ldx, k, c);",
+     "s += AT(L, ldl, i, k) * AT(X, ldx, k, c);"),
+    ("potrs_back_not_transposed", "s -= AT(L, ldl, k, i) * AT(X, ldx, k, c);",
+     "s -= AT(L, ldl, i, k) * AT(X, ldx, k, c);"),
+    ("potrs_one_solve_only", "        for (int64_t i = n - 1; i >= 0; --i) {\n            double s = AT(X, ldx, i, c);",
+     "        for (int64_t i = n - 1; i >= n; --i) {\n            double s = AT(X, ldx, i, c);"),
+    ("potrs_adj_one_sided_W",
+     "w += AT(adjB, ldab, i, c) * AT(X, ldx, k, c) + AT(X, ldx, i, c) * AT(adjB, ldab, k, c);",
+     "w += AT(adjB, ldab, i, c) * AT(X, ldx, k, c);"),
+    ("potrs_adj_sign", "AT(adjL, ldal, i, j) -= g;", "AT(adjL, ldal, i, j) += g;"),
+    ("potrs_adj_L_transposed", "g += W[(size_t)i * n + k] * AT(L, ldl, k, j);",
+     "g += W[(size_t)i * n + k] * AT(L, ldl, j, k);"),
     ("dot_adjoint_swapped", "abar[k] += ybar * b[k];", "abar[k] += ybar * a[k];"),
 ]
 
@@ -59,6 +71,10 @@ PINS = [
     lambda: pins.test_symmetric_pair_invariant(12, 7, 3),
     pins.test_upper_of_adjL_ignored_and_upper_of_adjA_untouched,
     pins.test_tile_dot_values_from_warp_1374,
+    lambda: pins.test_potrs_matches_library_solve(17, 3),
+    pins.test_potrs_closed_forms,
+    lambda: pins.test_potrs_adjoint_central_finite_differences(6, 3),
+    pins.test_potrs_adjoint_chained_with_factor_adjoint_matches_matrix_calculus,
 ]
 
 

@@ -21,6 +21,12 @@ from ._lib import (  # noqa: F401
     chol_potrf_adjoint_workspace_size,
     chol_potrf_batched,
     chol_potrf_plan,
+    chol_potrs,
+    chol_potrs_adjoint,
+    chol_potrs_adjoint_batched,
+    chol_potrs_adjoint_workspace_size,
+    chol_potrs_batched,
+    chol_potrs_workspace_size,
     chol_status_string,
     chol_wave_dot_fwd_adj,
     header_entry_points,

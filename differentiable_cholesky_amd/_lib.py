@@ -84,6 +84,20 @@ def _load() -> ctypes.CDLL:
     lib.chol_profile_start.argtypes = [ctypes.c_uint32]
     lib.chol_profile_stop.restype = st
     lib.chol_profile_stop.argtypes = [ctypes.c_int32, vp, vp, vp]
+    lib.chol_potrs.restype = st
+    lib.chol_potrs.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, i64, vp, sz, vp]
+    lib.chol_potrs_workspace_size.restype = st
+    lib.chol_potrs_workspace_size.argtypes = [i32, i64, i64, i64, ctypes.POINTER(sz)]
+    lib.chol_potrs_batched.restype = st
+    lib.chol_potrs_batched.argtypes = [i32, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, vp]
+    lib.chol_potrs_adjoint.restype = st
+    lib.chol_potrs_adjoint.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32, i64,
+                                       vp, sz, vp]
+    lib.chol_potrs_adjoint_workspace_size.restype = st
+    lib.chol_potrs_adjoint_workspace_size.argtypes = [i32, i64, i64, i64, ctypes.POINTER(sz)]
+    lib.chol_potrs_adjoint_batched.restype = st
+    lib.chol_potrs_adjoint_batched.argtypes = [i32, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                               vp, i64, i64, vp, i64, i64, i32, vp]
     return lib
 
 
@@ -235,6 +249,131 @@ def chol_potrf_adjoint_batched(L, adjL, adjA=None, accumulate: bool = True, stre
     _check(lib.chol_potrf_adjoint_batched(_dtype_code(L), L.shape[1], L.shape[0], pl, ldl, sl, pb, ldb, sb,
                                           pa, lda, sa, 1 if accumulate else 0, _stream(stream)))
     return adjA
+
+
+def _rhs(t, name: str, n: int):
+    """(pointer, ld, nrhs) of an n x nrhs row-major device matrix (a 1-D tensor
+    of n entries is one column)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dim() == 1:
+        if t.shape[0] != n or (n > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must hold {n} contiguous entries")
+        return ctypes.c_void_p(t.data_ptr()), 1, 1
+    if t.dim() != 2 or t.shape[0] != n:
+        raise ValueError(f"{name} must be [n, nrhs] with n = {n}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return ctypes.c_void_p(t.data_ptr()), max(int(t.stride(0)), int(t.shape[1]), 1), int(t.shape[1])
+
+
+def _rhs_bat(t, name: str, n: int):
+    """(pointer, ld, stride, nrhs) of a [batch, n, nrhs] row-major device array."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dim() != 3 or t.shape[1] != n:
+        raise ValueError(f"{name} must be [batch, n, nrhs] with n = {n}")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    nrhs = int(t.shape[2])
+    ld = max(int(t.stride(1)), nrhs, 1)
+    stride = int(t.stride(0)) if t.shape[0] > 1 else ld * n
+    return ctypes.c_void_p(t.data_ptr()), ld, stride, nrhs
+
+
+def _workspace(need: int, device, workspace):
+    torch = _torch()
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    wptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return workspace, wptr, wbytes
+
+
+def chol_potrs_workspace_size(dtype_code: int, n: int, nrhs: int, nb: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.chol_potrs_workspace_size(dtype_code, n, nrhs, nb, ctypes.byref(out)))
+    return int(out.value)
+
+
+def chol_potrs(L, B, X=None, nb: int = 0, workspace=None, stream=None):
+    """X = (L L^T)^{-1} B (B: [n] or [n, nrhs]); ``X`` may be ``B`` (in place)."""
+    torch = _torch()
+    if X is None:
+        X = torch.empty_like(B)
+    pl, ldl = _mat(L, "L")
+    n = L.shape[0]
+    pb, ldb, nrhs = _rhs(B, "B", n)
+    px, ldx, nx = _rhs(X, "X", n)
+    if nx != nrhs:
+        raise ValueError("X and B must have the same shape")
+    code = _dtype_code(L)
+    _, wptr, wbytes = _workspace(chol_potrs_workspace_size(code, n, nrhs, nb), L.device, workspace)
+    _check(lib.chol_potrs(code, n, nrhs, pl, ldl, pb, ldb, px, ldx, nb, wptr, wbytes, _stream(stream)))
+    return X
+
+
+def chol_potrs_batched(L, B, X=None, stream=None):
+    """X[b] = (L[b] L[b]^T)^{-1} B[b] for [batch, n, n] L and [batch, n, nrhs] B (n <= 64)."""
+    torch = _torch()
+    if X is None:
+        X = torch.empty_like(B)
+    pl, ldl, sl = _bat(L, "L")
+    n = L.shape[1]
+    pb, ldb, sb, nrhs = _rhs_bat(B, "B", n)
+    px, ldx, sx, _ = _rhs_bat(X, "X", n)
+    _check(lib.chol_potrs_batched(_dtype_code(L), n, nrhs, L.shape[0], pl, ldl, sl, pb, ldb, sb, px, ldx, sx,
+                                  _stream(stream)))
+    return X
+
+
+def chol_potrs_adjoint_workspace_size(dtype_code: int, n: int, nrhs: int, nb: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.chol_potrs_adjoint_workspace_size(dtype_code, n, nrhs, nb, ctypes.byref(out)))
+    return int(out.value)
+
+
+def chol_potrs_adjoint(L, X, adjX, adjB=None, adjL=None, accumulate: bool = True, nb: int = 0, workspace=None,
+                       stream=None):
+    """Adjoint of X = chol_potrs(L, B): returns (adjB, adjL) with adjB =
+    (L L^T)^{-1} adjX (``adjB`` may be ``adjX``) and lower(adjL) += (or =)
+    -tril((adjB X^T + X adjB^T) L)."""
+    torch = _torch()
+    if adjB is None:
+        adjB = torch.empty_like(adjX)
+    if adjL is None:
+        adjL = torch.zeros_like(L)
+    pl, ldl = _mat(L, "L")
+    n = L.shape[0]
+    px, ldx, nrhs = _rhs(X, "X", n)
+    pa, lda, na = _rhs(adjX, "adjX", n)
+    pb, ldb, nb_ = _rhs(adjB, "adjB", n)
+    if na != nrhs or nb_ != nrhs:
+        raise ValueError("X, adjX and adjB must have the same shape")
+    pg, ldg = _mat(adjL, "adjL")
+    code = _dtype_code(L)
+    _, wptr, wbytes = _workspace(chol_potrs_adjoint_workspace_size(code, n, nrhs, nb), L.device, workspace)
+    _check(lib.chol_potrs_adjoint(code, n, nrhs, pl, ldl, px, ldx, pa, lda, pb, ldb, pg, ldg,
+                                  1 if accumulate else 0, nb, wptr, wbytes, _stream(stream)))
+    return adjB, adjL
+
+
+def chol_potrs_adjoint_batched(L, X, adjX, adjB=None, adjL=None, accumulate: bool = True, stream=None):
+    """Batched chol_potrs_adjoint (n <= 64): returns (adjB, adjL)."""
+    torch = _torch()
+    if adjB is None:
+        adjB = torch.empty_like(adjX)
+    if adjL is None:
+        adjL = torch.zeros_like(L)
+    pl, ldl, sl = _bat(L, "L")
+    n = L.shape[1]
+    px, ldx, sx, nrhs = _rhs_bat(X, "X", n)
+    pa, lda, sa, _ = _rhs_bat(adjX, "adjX", n)
+    pb, ldb, sb, _ = _rhs_bat(adjB, "adjB", n)
+    pg, ldg, sg = _bat(adjL, "adjL")
+    _check(lib.chol_potrs_adjoint_batched(_dtype_code(L), n, nrhs, L.shape[0], pl, ldl, sl, px, ldx, sx, pa, lda,
+                                          sa, pb, ldb, sb, pg, ldg, sg, 1 if accumulate else 0, _stream(stream)))
+    return adjB, adjL
 
 
 def chol_wave_dot_fwd_adj(a, b, ybar, abar=None, bbar=None, staging: int = 0, stream=None):

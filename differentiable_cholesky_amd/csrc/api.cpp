@@ -33,6 +33,24 @@ chol_status blocked_adjoint_single_stream(int64_t n, const T *L, int64_t ldl, co
                                           int64_t ldaa, int accumulate, int nb, void *ws, int *sched, int cus,
                                           hipStream_t st);
 chol_status hbm_stream(int mode, const void *src, void *dst, size_t bytes, hipStream_t st);
+template <typename T>
+chol_status small_potrs(int n, int nrhs, int64_t batch, const T *L, int64_t ldl, int64_t sL, const T *B, int64_t ldb,
+                        int64_t sB, T *X, int64_t ldx, int64_t sX, hipStream_t st);
+template <typename T>
+chol_status small_potrs_adjoint(int n, int nrhs, int64_t batch, const T *L, int64_t ldl, int64_t sL, const T *X,
+                                int64_t ldx, int64_t sX, const T *adjX, int64_t ldax, int64_t saX, T *adjB,
+                                int64_t ldab, int64_t saB, T *adjL, int64_t ldal, int64_t saL, int accumulate,
+                                hipStream_t st);
+template <typename T>
+chol_status blocked_potrs(int64_t n, int64_t nrhs, const T *L, int64_t ldl, const T *B, int64_t ldb, T *X,
+                          int64_t ldx, int nb, void *ws, hipStream_t st);
+template <typename T>
+chol_status blocked_potrs_adjoint(int64_t n, int64_t nrhs, const T *L, int64_t ldl, const T *X, int64_t ldx,
+                                  const T *adjX, int64_t ldax, T *adjB, int64_t ldab, T *adjL, int64_t ldal,
+                                  int accumulate, int nb, void *ws, hipStream_t st);
+size_t blocked_solve_workspace(int64_t n, int nb, size_t es);
+chol_status zero_lower_batched(size_t es, int64_t n, int64_t batch, void *p, int64_t ld, int64_t stride, hipStream_t st);
+size_t blocked_solve_adjoint_workspace(int64_t n, int64_t nrhs, int nb, size_t es);
 chol_status small_load();
 chol_status blocked_load();
 template <typename T>
@@ -71,6 +89,23 @@ bool alias_ok(const void *i, int64_t ldi, int64_t si, const void *o, int64_t ldo
     if (i == o)
         return ldi == ldo && (batch <= 1 || si == so);
     return !overlap(extent(i, n, ldi, batch, si, es), extent(o, n, ldo, batch, so, es));
+}
+
+// rows x cols blocks (right-hand sides of the solve)
+Extent rect_extent(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t batch, int64_t stride, size_t es)
+{
+    Extent e{(uintptr_t)p, (uintptr_t)p};
+    if (rows > 0 && cols > 0 && batch > 0)
+        e.hi = e.lo + (size_t)((batch - 1) * stride + (rows - 1) * ld + cols) * es;
+    return e;
+}
+
+bool rect_alias_ok(const void *i, int64_t ldi, int64_t si, const void *o, int64_t ldo, int64_t so, int64_t rows,
+                   int64_t cols, int64_t batch, size_t es)
+{
+    if (i == o)
+        return ldi == ldo && (batch <= 1 || si == so);
+    return !overlap(rect_extent(i, rows, cols, ldi, batch, si, es), rect_extent(o, rows, cols, ldo, batch, so, es));
 }
 
 bool ld_ok(int64_t ld, int64_t n) { return ld >= std::max<int64_t>(1, n); }
@@ -130,6 +165,232 @@ int64_t chol_potrf_plan(int64_t n, int64_t nb, int copy, int64_t slots, int64_t 
         r[5] = o.f; r[6] = o.np; r[7] = o.t0; r[8] = o.tn; r[9] = o.slot;
     }
     return count;
+}
+
+// ------------------------------------------------------------------ solve ----
+
+namespace {
+// shared checks of the solve entry points; returns CHOL_OK to go on, or the
+// status to return (CHOL_OK with *noop for empty problems)
+chol_status potrs_args(chol_dtype dt, int64_t n, int64_t nrhs, int64_t batch, const void *L, int64_t ldl,
+                       int64_t sL, const void *B, int64_t ldb, int64_t sB, const void *X, int64_t ldx, int64_t sX,
+                       bool *noop)
+{
+    *noop = false;
+    if (!valid_dtype(dt) || n < 0 || nrhs < 0 || batch < 0)
+        return CHOL_ERR_INVALID_VALUE;
+    if (n == 0 || nrhs == 0 || batch == 0) {
+        *noop = true;
+        return CHOL_OK;
+    }
+    if (!L || !B || !X || !ld_ok(ldl, n) || !ld_ok(ldb, nrhs) || !ld_ok(ldx, nrhs) ||
+        !stride_ok(sL, ldl, n, batch) || !stride_ok(sB, ldb, n, batch) || !stride_ok(sX, ldx, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > MAX_N || nrhs > INT32_MAX || batch > ((int64_t)1 << 31) - 1)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    if (!rect_alias_ok(B, ldb, sB, X, ldx, sX, n, nrhs, batch, es) ||
+        overlap(extent(L, n, ldl, batch, sL, es), rect_extent(X, n, nrhs, ldx, batch, sX, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    return CHOL_OK;
+}
+} // namespace
+
+chol_status chol_potrs_workspace_size(chol_dtype dt, int64_t n, int64_t nrhs, int64_t nb, size_t *bytes)
+{
+    if (!bytes || !valid_dtype(dt) || n < 0 || nrhs < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    *bytes = 0;
+    if (n <= CHOL_SMALL_MAX_N || nrhs == 0)
+        return CHOL_OK;
+    if (n > MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    *bytes = chol::blocked_solve_workspace(n, nb ? (int)nb : DEFAULT_NB, esize(dt));
+    return CHOL_OK;
+}
+
+chol_status chol_potrs(chol_dtype dt, int64_t n, int64_t nrhs, const void *L, int64_t ldl, const void *B,
+                       int64_t ldb, void *X, int64_t ldx, int64_t nb, void *workspace, size_t workspace_bytes,
+                       void *stream)
+{
+    if (!nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    bool noop;
+    chol_status s = potrs_args(dt, n, nrhs, 1, L, ldl, 0, B, ldb, 0, X, ldx, 0, &noop);
+    if (s != CHOL_OK || noop)
+        return s;
+    const size_t es = esize(dt);
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    if (n <= CHOL_SMALL_MAX_N) {
+        if (dt == CHOL_F64)
+            return chol::small_potrs<double>((int)n, (int)nrhs, 1, (const double *)L, ldl, 0, (const double *)B, ldb,
+                                             0, (double *)X, ldx, 0, st);
+        return chol::small_potrs<float>((int)n, (int)nrhs, 1, (const float *)L, ldl, 0, (const float *)B, ldb, 0,
+                                        (float *)X, ldx, 0, st);
+    }
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    const size_t need = chol::blocked_solve_workspace(n, b, es);
+    if (!workspace || workspace_bytes < need)
+        return CHOL_ERR_WORKSPACE;
+    const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlap(ws, extent(L, n, ldl, 1, 0, es)) || overlap(ws, rect_extent(B, n, nrhs, ldb, 1, 0, es)) ||
+        overlap(ws, rect_extent(X, n, nrhs, ldx, 1, 0, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    if (dt == CHOL_F64)
+        return chol::blocked_potrs<double>(n, nrhs, (const double *)L, ldl, (const double *)B, ldb, (double *)X, ldx,
+                                           b, workspace, st);
+    return chol::blocked_potrs<float>(n, nrhs, (const float *)L, ldl, (const float *)B, ldb, (float *)X, ldx, b,
+                                      workspace, st);
+}
+
+chol_status chol_potrs_batched(chol_dtype dt, int64_t n, int64_t nrhs, int64_t batch, const void *L, int64_t ldl,
+                               int64_t strideL, const void *B, int64_t ldb, int64_t strideB, void *X, int64_t ldx,
+                               int64_t strideX, void *stream)
+{
+    if (n > CHOL_SMALL_MAX_N && valid_dtype(dt) && nrhs >= 0 && batch >= 0)
+        return CHOL_ERR_NOT_SUPPORTED;
+    bool noop;
+    chol_status s = potrs_args(dt, n, nrhs, batch, L, ldl, strideL, B, ldb, strideB, X, ldx, strideX, &noop);
+    if (s != CHOL_OK || noop)
+        return s;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    if (dt == CHOL_F64)
+        return chol::small_potrs<double>((int)n, (int)nrhs, batch, (const double *)L, ldl, strideL,
+                                         (const double *)B, ldb, strideB, (double *)X, ldx, strideX, st);
+    return chol::small_potrs<float>((int)n, (int)nrhs, batch, (const float *)L, ldl, strideL, (const float *)B, ldb,
+                                    strideB, (float *)X, ldx, strideX, st);
+}
+
+namespace {
+chol_status potrs_adjoint_args(chol_dtype dt, int64_t n, int64_t nrhs, int64_t batch, const void *L, int64_t ldl,
+                               int64_t sL, const void *X, int64_t ldx, int64_t sX, const void *adjX, int64_t ldax,
+                               int64_t saX, const void *adjB, int64_t ldab, int64_t saB, const void *adjL,
+                               int64_t ldal, int64_t saL, bool *noop)
+{
+    // adj_B = solve(adj_X): the solve's own rules (adj_B may be adj_X)
+    chol_status s = potrs_args(dt, n, nrhs, batch, L, ldl, sL, adjX, ldax, saX, adjB, ldab, saB, noop);
+    if (s != CHOL_OK)
+        return s;
+    if (*noop) {
+        // no right-hand side: adj_L's term is zero, and only adj_L is touched
+        if (n == 0 || batch == 0)
+            return CHOL_OK;
+        if (!adjL || !ld_ok(ldal, n) || !stride_ok(saL, ldal, n, batch))
+            return CHOL_ERR_INVALID_VALUE;
+        return CHOL_OK;
+    }
+    if (!X || !adjL || !ld_ok(ldx, nrhs) || !ld_ok(ldal, n) || !stride_ok(sX, ldx, n, batch) ||
+        !stride_ok(saL, ldal, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    const size_t es = esize(dt);
+    const Extent eB = rect_extent(adjB, n, nrhs, ldab, batch, saB, es);
+    const Extent eL = extent(adjL, n, ldal, batch, saL, es);
+    // outputs (adj_B, adj_L) apart from each other and from the inputs they do not replace
+    if (overlap(eB, eL) || overlap(eB, rect_extent(X, n, nrhs, ldx, batch, sX, es)) ||
+        overlap(eL, extent(L, n, ldl, batch, sL, es)) || overlap(eL, rect_extent(X, n, nrhs, ldx, batch, sX, es)) ||
+        overlap(eL, rect_extent(adjX, n, nrhs, ldax, batch, saX, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    return CHOL_OK;
+}
+} // namespace
+
+chol_status chol_potrs_adjoint_workspace_size(chol_dtype dt, int64_t n, int64_t nrhs, int64_t nb, size_t *bytes)
+{
+    if (!bytes || !valid_dtype(dt) || n < 0 || nrhs < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    *bytes = 0;
+    if (n <= CHOL_SMALL_MAX_N || nrhs == 0)
+        return CHOL_OK;
+    if (n > MAX_N || nrhs > INT32_MAX / 2)
+        return CHOL_ERR_NOT_SUPPORTED;
+    *bytes = chol::blocked_solve_adjoint_workspace(n, nrhs, nb ? (int)nb : DEFAULT_NB, esize(dt));
+    return CHOL_OK;
+}
+
+chol_status chol_potrs_adjoint(chol_dtype dt, int64_t n, int64_t nrhs, const void *L, int64_t ldl, const void *X,
+                               int64_t ldx, const void *adjX, int64_t ldax, void *adjB, int64_t ldab, void *adjL,
+                               int64_t ldal, int accumulate, int64_t nb, void *workspace, size_t workspace_bytes,
+                               void *stream)
+{
+    if (!nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    bool noop;
+    chol_status s = potrs_adjoint_args(dt, n, nrhs, 1, L, ldl, 0, X, ldx, 0, adjX, ldax, 0, adjB, ldab, 0, adjL,
+                                       ldal, 0, &noop);
+    if (s != CHOL_OK)
+        return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (noop) {
+        // nrhs == 0: adj_L's term is zero (overwrite mode clears its lower triangle)
+        if (n == 0 || accumulate)
+            return CHOL_OK;
+        clear_stale_status();
+        return chol::zero_lower_batched(esize(dt), n, 1, adjL, ldal, 0, st);
+    }
+    const size_t es = esize(dt);
+    clear_stale_status();
+    if (n <= CHOL_SMALL_MAX_N) {
+        if (dt == CHOL_F64)
+            return chol::small_potrs_adjoint<double>((int)n, (int)nrhs, 1, (const double *)L, ldl, 0,
+                                                     (const double *)X, ldx, 0, (const double *)adjX, ldax, 0,
+                                                     (double *)adjB, ldab, 0, (double *)adjL, ldal, 0, accumulate,
+                                                     st);
+        return chol::small_potrs_adjoint<float>((int)n, (int)nrhs, 1, (const float *)L, ldl, 0, (const float *)X,
+                                                ldx, 0, (const float *)adjX, ldax, 0, (float *)adjB, ldab, 0,
+                                                (float *)adjL, ldal, 0, accumulate, st);
+    }
+    if (nrhs > INT32_MAX / 2)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    const size_t need = chol::blocked_solve_adjoint_workspace(n, nrhs, b, es);
+    if (!workspace || workspace_bytes < need)
+        return CHOL_ERR_WORKSPACE;
+    const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlap(ws, extent(L, n, ldl, 1, 0, es)) || overlap(ws, rect_extent(X, n, nrhs, ldx, 1, 0, es)) ||
+        overlap(ws, rect_extent(adjX, n, nrhs, ldax, 1, 0, es)) ||
+        overlap(ws, rect_extent(adjB, n, nrhs, ldab, 1, 0, es)) || overlap(ws, extent(adjL, n, ldal, 1, 0, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    if (dt == CHOL_F64)
+        return chol::blocked_potrs_adjoint<double>(n, nrhs, (const double *)L, ldl, (const double *)X, ldx,
+                                                   (const double *)adjX, ldax, (double *)adjB, ldab, (double *)adjL,
+                                                   ldal, accumulate, b, workspace, st);
+    return chol::blocked_potrs_adjoint<float>(n, nrhs, (const float *)L, ldl, (const float *)X, ldx,
+                                              (const float *)adjX, ldax, (float *)adjB, ldab, (float *)adjL, ldal,
+                                              accumulate, b, workspace, st);
+}
+
+chol_status chol_potrs_adjoint_batched(chol_dtype dt, int64_t n, int64_t nrhs, int64_t batch, const void *L,
+                                       int64_t ldl, int64_t strideL, const void *X, int64_t ldx, int64_t strideX,
+                                       const void *adjX, int64_t ldax, int64_t strideAX, void *adjB, int64_t ldab,
+                                       int64_t strideAB, void *adjL, int64_t ldal, int64_t strideAL, int accumulate,
+                                       void *stream)
+{
+    if (n > CHOL_SMALL_MAX_N && valid_dtype(dt) && nrhs >= 0 && batch >= 0)
+        return CHOL_ERR_NOT_SUPPORTED;
+    bool noop;
+    chol_status s = potrs_adjoint_args(dt, n, nrhs, batch, L, ldl, strideL, X, ldx, strideX, adjX, ldax, strideAX,
+                                       adjB, ldab, strideAB, adjL, ldal, strideAL, &noop);
+    if (s != CHOL_OK)
+        return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (noop) {
+        if (n == 0 || batch == 0 || accumulate)
+            return CHOL_OK;
+        clear_stale_status();
+        return chol::zero_lower_batched(esize(dt), n, batch, adjL, ldal, strideAL, st);
+    }
+    clear_stale_status();
+    if (dt == CHOL_F64)
+        return chol::small_potrs_adjoint<double>((int)n, (int)nrhs, batch, (const double *)L, ldl, strideL,
+                                                 (const double *)X, ldx, strideX, (const double *)adjX, ldax,
+                                                 strideAX, (double *)adjB, ldab, strideAB, (double *)adjL, ldal,
+                                                 strideAL, accumulate, st);
+    return chol::small_potrs_adjoint<float>((int)n, (int)nrhs, batch, (const float *)L, ldl, strideL,
+                                            (const float *)X, ldx, strideX, (const float *)adjX, ldax, strideAX,
+                                            (float *)adjB, ldab, strideAB, (float *)adjL, ldal, strideAL,
+                                            accumulate, st);
 }
 
 int chol_last_hip_error(void) { return chol::g_last_hip_error.load(std::memory_order_relaxed); }

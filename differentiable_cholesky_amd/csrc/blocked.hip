@@ -40,7 +40,7 @@ chol_status diag_potrf(int n, T *W, int64_t ld, int32_t *info, int info_mode, in
 static constexpr int MAX_TILE = CHOL_MAX_NB;
 
 // ------------------------------------------------------------ elementwise ----
-enum { TRI_COPY_LOWER = 0, TRI_ZERO_UPPER = 1, TRI_ADD_LOWER = 2 };
+enum { TRI_COPY_LOWER = 0, TRI_ZERO_UPPER = 1, TRI_ADD_LOWER = 2, TRI_ZERO_LOWER = 3 };
 
 // 32 x 32 element tiles; a block covers one tile with 256 threads.
 template <typename T, int MODE>
@@ -61,6 +61,9 @@ k_tri(int64_t n, int64_t w, const T *src, int64_t lds, T *dst, int64_t ldd)
         } else if (MODE == TRI_ZERO_UPPER) {
             if (j > i)
                 dst[i * ldd + j] = T(0);
+        } else if (MODE == TRI_ZERO_LOWER) {
+            if (j <= i)
+                dst[i * ldd + j] = T(0);
         } else {
             if (j <= i)
                 dst[i * ldd + j] += src[i * lds + j];
@@ -79,7 +82,8 @@ static chol_status tri_op(int64_t n, const T *src, int64_t lds, T *dst, int64_t 
     // lower entries of the first w columns: w (n - w) + w (w + 1) / 2
     const double tri = (double)w * (n - w) + (double)w * (w + 1) / 2, es = (double)sizeof(T);
     const double bytes = MODE == TRI_COPY_LOWER ? 2 * tri * es
-                       : MODE == TRI_ZERO_UPPER ? ((double)n * w - tri) * es : 3 * tri * es;
+                       : MODE == TRI_ZERO_UPPER ? ((double)n * w - tri) * es
+                       : MODE == TRI_ZERO_LOWER ? tri * es : 3 * tri * es;
     prof::Scope ps(CHOL_K_ELEMENTWISE, st, bytes);
     const unsigned tr = (unsigned)((n + 31) / 32), tc = (unsigned)((w + 31) / 32);
     if (tr == 0 || tc == 0)
@@ -798,6 +802,229 @@ chol_status blocked_adjoint_single_stream(int64_t n, const T *L, int64_t ldl, co
 
 // Loads this file's kernels on the current device (their code object is
 // otherwise loaded on first launch).
+
+// --------------------------------------------------------------- solve ----
+// X = (L L^T)^{-1} B for n > CHOL_SMALL_MAX_N: the two triangular solves
+// against L, tile by tile, each diagonal block applied as a product with its
+// stored inverse (all K inverses are formed first, one block per tile, into
+// the caller's workspace) and each off-diagonal block as an update:
+//   forward  (k = 0 .. K-1):   X_k = Linv_kk X_k ;   X[r0:] -= L[r0:, k] X_k
+//   backward (k = K-1 .. 0):   X_k = Linv_kk^T X_k ; X[:k0] -= L[k, :k0]^T X_k
+// X_k = Linv X_k runs in place: its product has one 128-row tile row, and a
+// block reads its 128-column span of X_k whole before it writes that span.
+
+// rows x cols copy of a row-major block (leading dimensions lds, ldd)
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_copy2d(int64_t rows, int64_t cols, const T *src, int64_t lds, T *dst, int64_t ldd)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * cols)
+        return;
+    const int64_t r = idx / cols, c = idx % cols;
+    dst[r * ldd + c] = src[r * lds + c];
+}
+
+template <typename T>
+static chol_status copy2d(int64_t rows, int64_t cols, const T *src, int64_t lds, T *dst, int64_t ldd, hipStream_t st)
+{
+    const int64_t tot = rows * cols;
+    if (tot <= 0)
+        return CHOL_OK;
+    hipLaunchKernelGGL((k_copy2d<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, rows, cols, src, lds,
+                       dst, ldd);
+    CHOL_LAUNCH_CHECK();
+    return CHOL_OK;
+}
+
+// C (M x N, leading dimension ldc) = sum of the split partials, in split order
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_splitk_sum(int M, int N, int splits, const T *part, T *c, int64_t ldc)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t tot = (int64_t)M * N;
+    if (idx >= tot)
+        return;
+    const int r = (int)(idx / N), col = (int)(idx % N);
+    T s = T(0);
+    for (int q = 0; q < splits; ++q)
+        s += part[(int64_t)q * tot + idx];
+    c[(int64_t)r * ldc + col] = s;
+}
+
+static int64_t solve_tiles(int64_t n, int nb) { return (n + nb - 1) / nb; }
+
+template <typename T>
+static chol_status blocked_solve_on(int64_t n, int64_t nrhs, const T *L, int64_t ldl, T *X, int64_t ldx, int nb,
+                                    const T *inv, hipStream_t st)
+{
+    const int64_t K = solve_tiles(n, nb);
+    chol_status s;
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool back = pass == 1;
+        for (int64_t q = 0; q < K; ++q) {
+            const int64_t k = back ? K - 1 - q : q;
+            const int64_t k0 = k * nb;
+            const int kb = (int)std::min<int64_t>(nb, n - k0);
+            const int64_t r0 = k0 + kb;
+            {
+                // X_k = Linv_kk X_k (forward) or Linv_kk^T X_k (backward), in place
+                GemmArgs<T> p{};
+                p.M = kb; p.N = (int)nrhs; p.K = kb;
+                p.a = inv + k * (int64_t)nb * nb; p.lda = nb;
+                p.b = X + k0 * ldx; p.ldb = ldx;
+                p.c = X + k0 * ldx; p.ldc = ldx;
+                s = back ? gemm<T, OP_KM, OP_KM, C_STORE>(p, 1, st) : gemm<T, OP_MK, OP_KM, C_STORE>(p, 1, st);
+                if (s != CHOL_OK)
+                    return s;
+            }
+            const int64_t m = back ? k0 : n - r0;
+            if (m == 0)
+                continue;
+            GemmArgs<T> p{};
+            p.M = (int)m; p.N = (int)nrhs; p.K = kb;
+            p.b = X + k0 * ldx; p.ldb = ldx;
+            p.lda = ldl;
+            if (back) {
+                // X[:k0] -= L[k, :k0]^T X_k : A(m, t) = L[k0 + t][m]
+                p.a = L + k0 * ldl;
+                p.c = X; p.ldc = ldx;
+                s = gemm<T, OP_KM, OP_KM, C_SUB, 64>(p, 1, st);
+            } else {
+                // X[r0:] -= L[r0:, k] X_k : A(m, t) = L[r0 + m][k0 + t]
+                p.a = L + r0 * ldl + k0;
+                p.c = X + r0 * ldx; p.ldc = ldx;
+                s = gemm<T, OP_MK, OP_KM, C_SUB, 64>(p, 1, st);
+            }
+            if (s != CHOL_OK)
+                return s;
+        }
+    }
+    return CHOL_OK;
+}
+
+template <typename T>
+static chol_status solve_inverses(int64_t n, const T *L, int64_t ldl, int nb, T *inv, hipStream_t st)
+{
+    const int64_t K = solve_tiles(n, nb);
+    hipLaunchKernelGGL((k_trinv<T>), dim3((unsigned)K), dim3(256), 0, st, n, nb, (int64_t)0, (int64_t)nb,
+                       const_cast<T *>(L), ldl, 1, inv, (int64_t)nb * nb, (int64_t)nb);
+    CHOL_LAUNCH_CHECK();
+    return CHOL_OK;
+}
+
+// split count of the adjoint's products P = [S|X]^T L (2 nrhs x n, n deep):
+// enough (row tile, column tile, split) items for the device's block slots
+static int solve_adj_splits(int64_t n, int64_t nrhs)
+{
+    const int64_t tiles = ((2 * nrhs + 127) / 128) * ((n + 127) / 128);
+    const int64_t want = (480 + tiles - 1) / tiles;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(32, std::min<int64_t>(want, n / 256 + 1)));
+}
+
+size_t blocked_solve_workspace(int64_t n, int nb, size_t es)
+{
+    return align256((size_t)solve_tiles(n, nb) * nb * nb * es);
+}
+
+size_t blocked_solve_adjoint_workspace(int64_t n, int64_t nrhs, int nb, size_t es)
+{
+    const int sp = solve_adj_splits(n, nrhs);
+    return blocked_solve_workspace(n, nb, es) + 2 * align256((size_t)n * 2 * nrhs * es) +
+           align256((size_t)2 * nrhs * n * es) + (sp > 1 ? align256((size_t)sp * 2 * nrhs * n * es) : 0);
+}
+
+template <typename T>
+chol_status blocked_potrs(int64_t n, int64_t nrhs, const T *L, int64_t ldl, const T *B, int64_t ldb, T *X,
+                          int64_t ldx, int nb, void *ws, hipStream_t st)
+{
+    T *inv = (T *)ws;
+    prof::Scope ps(CHOL_K_SOLVE, st, 2.0 * n * n * nrhs);
+    chol_status s = solve_inverses<T>(n, L, ldl, nb, inv, st);
+    if (s == CHOL_OK && X != B)
+        s = copy2d<T>(n, nrhs, B, ldb, X, ldx, st);
+    if (s != CHOL_OK)
+        return s;
+    return blocked_solve_on<T>(n, nrhs, L, ldl, X, ldx, nb, inv, st);
+}
+
+// adj_B = (L L^T)^{-1} adj_X; lower(adj_L) (+)= -tril((adj_B X^T + X adj_B^T) L).
+// With S = adj_B, [S|X]^T L = [Q; P] (Q = S^T L, P = X^T L, L read as its
+// lower triangle), and S P + X Q = [X|S] [Q; P], so the gradient is one
+// lower-only product of depth 2 nrhs.
+template <typename T>
+chol_status blocked_potrs_adjoint(int64_t n, int64_t nrhs, const T *L, int64_t ldl, const T *X, int64_t ldx,
+                                  const T *adjX, int64_t ldax, T *adjB, int64_t ldab, T *adjL, int64_t ldal,
+                                  int accumulate, int nb, void *ws, hipStream_t st)
+{
+    char *w = (char *)ws;
+    T *inv = (T *)w;
+    w += blocked_solve_workspace(n, nb, sizeof(T));
+    T *sx = (T *)w;                       // [S | X], n x 2 nrhs
+    w += align256((size_t)n * 2 * nrhs * sizeof(T));
+    T *xs = (T *)w;                       // [X | S]
+    w += align256((size_t)n * 2 * nrhs * sizeof(T));
+    T *qp = (T *)w;                       // [Q; P], 2 nrhs x n
+    w += align256((size_t)2 * nrhs * n * sizeof(T));
+    T *part = (T *)w;
+    const int sp = solve_adj_splits(n, nrhs);
+
+    chol_status s;
+    {
+        prof::Scope ps(CHOL_K_SOLVE, st, 2.0 * n * n * nrhs);
+        s = solve_inverses<T>(n, L, ldl, nb, inv, st);
+        if (s == CHOL_OK && adjB != adjX)
+            s = copy2d<T>(n, nrhs, adjX, ldax, adjB, ldab, st);
+        if (s == CHOL_OK)
+            s = blocked_solve_on<T>(n, nrhs, L, ldl, adjB, ldab, nb, inv, st);
+    }
+    prof::Scope ps(CHOL_K_SOLVE_ADJOINT, st, 4.0 * n * n * nrhs);
+    if (s == CHOL_OK)
+        s = copy2d<T>(n, nrhs, adjB, ldab, sx, 2 * nrhs, st);
+    if (s == CHOL_OK)
+        s = copy2d<T>(n, nrhs, X, ldx, sx + nrhs, 2 * nrhs, st);
+    if (s == CHOL_OK)
+        s = copy2d<T>(n, nrhs, X, ldx, xs, 2 * nrhs, st);
+    if (s == CHOL_OK)
+        s = copy2d<T>(n, nrhs, adjB, ldab, xs + nrhs, 2 * nrhs, st);
+    if (s != CHOL_OK)
+        return s;
+    {
+        // [Q; P] = [S|X]^T L: A(m, t) = sx[t][m], B(m = j, t) = L[t][j] for t >= j
+        GemmArgs<T> p{};
+        p.M = (int)(2 * nrhs); p.N = (int)n; p.K = (int)n;
+        p.a = sx; p.lda = 2 * nrhs;
+        p.b = L; p.ldb = ldl;
+        if (sp > 1) {
+            p.part = part;
+            p.kchunk = split_chunk(n, sp);
+            const int used = (int)((n + p.kchunk - 1) / p.kchunk);
+            s = gemm<T, OP_KM, OP_KM_LOWER, C_PARTIAL>(p, used, st);
+            if (s != CHOL_OK)
+                return s;
+            const int64_t tot = 2 * nrhs * n;
+            hipLaunchKernelGGL((k_splitk_sum<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
+                               (int)(2 * nrhs), (int)n, used, (const T *)part, qp, n);
+            CHOL_LAUNCH_CHECK();
+        } else {
+            p.c = qp; p.ldc = n;
+            s = gemm<T, OP_KM, OP_KM_LOWER, C_STORE>(p, 1, st);
+            if (s != CHOL_OK)
+                return s;
+        }
+    }
+    if (!accumulate && (s = tri_op<T, TRI_ZERO_LOWER>(n, nullptr, 0, adjL, ldal, st)) != CHOL_OK)
+        return s;
+    // lower(adj_L) -= [X|S] [Q; P]: A(i, t) = xs[i][t], B(m = j, t) = qp[t][j]
+    GemmArgs<T> p{};
+    p.M = (int)n; p.N = (int)n; p.K = (int)(2 * nrhs);
+    p.a = xs; p.lda = 2 * nrhs;
+    p.b = qp; p.ldb = n;
+    p.c = adjL; p.ldc = ldal;
+    return gemm<T, OP_MK, OP_KM, C_SUB_LOWER>(p, 1, st);
+}
+
 chol_status blocked_load()
 {
     hipFuncAttributes a;
@@ -812,7 +1039,12 @@ chol_status blocked_load()
     template chol_status blocked_adjoint<T>(int64_t, const T *, int64_t, const T *, int64_t, T *, int64_t, \
                                             int, int, void *, hipStream_t);                              \
     template chol_status blocked_adjoint_single_stream<T>(int64_t, const T *, int64_t, const T *, int64_t, T *, \
-                                                          int64_t, int, int, void *, int *, int, hipStream_t);
+                                                          int64_t, int, int, void *, int *, int, hipStream_t); \
+    template chol_status blocked_potrs<T>(int64_t, int64_t, const T *, int64_t, const T *, int64_t, T *, int64_t, \
+                                          int, void *, hipStream_t);                                     \
+    template chol_status blocked_potrs_adjoint<T>(int64_t, int64_t, const T *, int64_t, const T *, int64_t,     \
+                                                  const T *, int64_t, T *, int64_t, T *, int64_t, int, int,     \
+                                                  void *, hipStream_t);
 CHOL_INST(float)
 CHOL_INST(double)
 #undef CHOL_INST

@@ -61,7 +61,7 @@ template <typename T> struct GemmArgs {
     int kchunk;          // split-K: contraction length per split (multiple of 32)
     T *part;             // C_PARTIAL destination, splits * M * N
     int tri;             // 1: lower-triangular tile grid (M == N)
-    int vec;             // 1: 16-byte global loads are legal for both operands
+    int vec;             // bit 0 (A), bit 1 (B): 16-byte global loads are legal for that operand
     int splits;          // split count (C_PARTIAL)
     int excl;            // OP_SYM A operand: entries (m, k) with m < excl and
                          // k < excl read as zero (a block left out of the product)
@@ -450,8 +450,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
                 }
     }
 
-    Operand<T, AOP, TM> A{p.a, p.lda, r0, p.M, p.vec, p.excl};
-    Operand<T, BOP, TN> B{p.b, p.ldb, c0, p.N, p.vec, 0};
+    const int va = p.vec & 1, vb = (p.vec >> 1) & 1;
+    Operand<T, AOP, TM> A{p.a, p.lda, r0, p.M, va, p.excl};
+    Operand<T, BOP, TN> B{p.b, p.ldb, c0, p.N, vb, 0};
     if constexpr (AOP == OP_SYM || AOP == OP_SYM_DG) {
         // Sym(S)(m, k) for the tile's rows m in [r0, r0 + 128): left of the
         // diagonal block (k < r0) it is a row panel of S's lower triangle,
@@ -463,20 +464,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
         // part is empty.
         const int b1 = min(kend, r0), d0 = max(kbeg, r0), d1 = min(kend, r0 + BM), a0 = max(kbeg, r0 + BM);
         if (b1 > kbeg) {
-            Operand<T, OP_MK> Ab{p.a, p.lda, r0, p.M, p.vec, 0};
+            Operand<T, OP_MK> Ab{p.a, p.lda, r0, p.M, va, 0};
             tile_mma<T, OP_MK, BOP, FROM_C, BOOST, true>(acc, Ab, B, kbeg, b1, lds);
         }
         if (d1 > d0 && !(r0 + BM <= p.excl)) {
             if constexpr (AOP == OP_SYM_DG) {
                 Operand<T, OP_MK> D{p.dg + (int64_t)I * BM * BM, BM, 0, BM, 1, 0};
-                Operand<T, BOP> B2{p.b + (int64_t)r0 * p.ldb, p.ldb, c0, p.N, p.vec, 0};
+                Operand<T, BOP> B2{p.b + (int64_t)r0 * p.ldb, p.ldb, c0, p.N, vb, 0};
                 tile_mma<T, OP_MK, BOP, FROM_C, BOOST>(acc, D, B2, d0 - r0, d1 - r0, lds);
             } else {
                 tile_mma_serial<T, AOP, BOP, FROM_C>(acc, A, B, d0, d1, lds);
             }
         }
         if (kend > a0) {
-            Operand<T, OP_KM> Aa{p.a, p.lda, r0, p.M, p.vec, 0};
+            Operand<T, OP_KM> Aa{p.a, p.lda, r0, p.M, va, 0};
             tile_mma<T, OP_KM, BOP, FROM_C, BOOST, true>(acc, Aa, B, a0, kend, lds);
         }
     } else {
@@ -628,7 +629,7 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         return CHOL_OK;
     if (TM != BM && p.tri)
         return CHOL_ERR_INVALID_VALUE;           // the triangular tile grid needs square tiles
-    p.vec = aligned16(p.a, p.lda) && aligned16(p.b, p.ldb);
+    p.vec = (aligned16(p.a, p.lda) ? 1 : 0) | (aligned16(p.b, p.ldb) ? 2 : 0);
     p.splits = splits;
     if constexpr (AOP == OP_SYM) {
         static_assert(TM == BM, "the symmetric operand takes 128 tiles");
@@ -636,7 +637,7 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         // diagonal block the product meets, the kernel reads them from it
         if (p.excl < 0 || p.excl > BM)
             return CHOL_ERR_INVALID_VALUE;
-        if (p.dg && p.vec && p.M % BM == 0 && (p.excl == 0 || p.excl == BM) && ((uintptr_t)p.dg % 16) == 0)
+        if (p.dg && p.vec == 3 && p.M % BM == 0 && (p.excl == 0 || p.excl == BM) && ((uintptr_t)p.dg % 16) == 0)
             return gemm<T, OP_SYM_DG, BOP, CM, TM>(p, splits, st);
     }
     const int TI = (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;

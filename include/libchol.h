@@ -200,6 +200,98 @@ chol_status chol_potrf_adjoint_batched(chol_dtype dtype, int64_t n, int64_t batc
                                        int accumulate, void *stream);
 
 /*
+ * chol_potrs -- solve with the factor: X = A^{-1} B for A = L L^T, given the
+ * lower factor L (for example from chol_potrf).  The factor is returned
+ * without a solve (jaxmg documentation, "Cholesky factorization", opening
+ * paragraph); this is the solve it is computed for, made of the two
+ * triangular solves against L that Warp issue #1316's resolution comment
+ * names: L Y = B by forward substitution, then L^T X = Y.
+ *   L      [in]  device, n x n, leading dimension ldl; lower triangle read.
+ *   B      [in]  device, n x nrhs, leading dimension ldb >= max(1, nrhs).
+ *   X      [out] device, n x nrhs, leading dimension ldx >= max(1, nrhs).
+ *                X == B with ldx == ldb solves in place; otherwise X must
+ *                overlap neither B nor L.
+ *   nb     tile size of the blocked solve (0 = 128, else 1..CHOL_MAX_NB);
+ *          ignored for n <= CHOL_SMALL_MAX_N.
+ *   workspace, workspace_bytes: device scratch of at least the size
+ *          chol_potrs_workspace_size reports (0 for n <= CHOL_SMALL_MAX_N);
+ *          too small returns CHOL_ERR_WORKSPACE.  It must not overlap L, B or X.
+ * n <= CHOL_SMALL_MAX_N: one wavefront per matrix, substitution row by row.
+ * Larger n: the inverses of the diagonal tiles are formed in the workspace,
+ * then both solves run tile by tile as matrix-core products (each diagonal
+ * block as a product with its inverse, each off-diagonal block as an update).
+ * There is no failure status: a zero or non-finite diagonal entry of L gives
+ * non-finite entries in X.  nrhs == 0 is a no-op.
+ */
+chol_status chol_potrs(chol_dtype dtype, int64_t n, int64_t nrhs,
+                       const void *L, int64_t ldl,
+                       const void *B, int64_t ldb,
+                       void *X, int64_t ldx, int64_t nb,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace chol_potrs needs (n x nb tile inverses for n >
+ * CHOL_SMALL_MAX_N, else 0). */
+chol_status chol_potrs_workspace_size(chol_dtype dtype, int64_t n, int64_t nrhs, int64_t nb, size_t *bytes);
+
+/*
+ * chol_potrs_batched -- chol_potrs for `batch` independent systems, n <=
+ * CHOL_SMALL_MAX_N (larger n returns CHOL_ERR_NOT_SUPPORTED), no workspace.
+ * System b uses L + b * strideL, B + b * strideB and X + b * strideX
+ * (elements); in place as in chol_potrs (equal ld and stride).
+ */
+chol_status chol_potrs_batched(chol_dtype dtype, int64_t n, int64_t nrhs, int64_t batch,
+                               const void *L, int64_t ldl, int64_t strideL,
+                               const void *B, int64_t ldb, int64_t strideB,
+                               void *X, int64_t ldx, int64_t strideX, void *stream);
+
+/*
+ * chol_potrs_adjoint -- reverse-mode adjoint of X = chol_potrs(L, B).  With
+ * A = L L^T, dX = -A^{-1} dA X and dA = dL L^T + L dL^T, so
+ *   adj_B = A^{-1} adj_X                        (the same two solves)
+ *   adj_L = -tril((adj_B X^T + X adj_B^T) L)    (gradient for the lower entries of L)
+ *   L      [in]  device, the factor (lower triangle read).
+ *   X      [in]  device, n x nrhs, the solve's result.
+ *   adjX   [in]  device, n x nrhs, dLoss/dX.
+ *   adjB   [out] device, n x nrhs: written with adj_B (it may be adjX itself,
+ *                same ld; it must not overlap X or adjL).
+ *   adjL   [in/out] device, n x n; its lower triangle receives adj_L:
+ *                accumulate != 0: lower(adjL) += adj_L; == 0: lower(adjL) = adj_L.
+ *                The strict upper triangle is not touched.  adjL must not
+ *                overlap L, X, adjX or adjB.
+ *   nb, workspace, workspace_bytes: as chol_potrs, with the size from
+ *          chol_potrs_adjoint_workspace_size.
+ * The adj_L term is formed as tril(S P + X Q) with S = adj_B, P = X^T L and
+ * Q = S^T L: for n <= CHOL_SMALL_MAX_N one wavefront per matrix; for larger n
+ * [Q; P] = [S | X]^T tril(L) as one split-contraction product and
+ * lower(adj_L) -= [X | S] [Q; P] as one lower-only product of depth 2 nrhs.
+ */
+chol_status chol_potrs_adjoint(chol_dtype dtype, int64_t n, int64_t nrhs,
+                               const void *L, int64_t ldl,
+                               const void *X, int64_t ldx,
+                               const void *adjX, int64_t ldax,
+                               void *adjB, int64_t ldab,
+                               void *adjL, int64_t ldal,
+                               int accumulate, int64_t nb,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace chol_potrs_adjoint needs (0 for n <= CHOL_SMALL_MAX_N). */
+chol_status chol_potrs_adjoint_workspace_size(chol_dtype dtype, int64_t n, int64_t nrhs, int64_t nb,
+                                              size_t *bytes);
+
+/*
+ * chol_potrs_adjoint_batched -- chol_potrs_adjoint for `batch` independent
+ * systems, n <= CHOL_SMALL_MAX_N (larger n returns CHOL_ERR_NOT_SUPPORTED),
+ * no workspace; per-array strides as in chol_potrs_batched.
+ */
+chol_status chol_potrs_adjoint_batched(chol_dtype dtype, int64_t n, int64_t nrhs, int64_t batch,
+                                       const void *L, int64_t ldl, int64_t strideL,
+                                       const void *X, int64_t ldx, int64_t strideX,
+                                       const void *adjX, int64_t ldax, int64_t strideAX,
+                                       void *adjB, int64_t ldab, int64_t strideAB,
+                                       void *adjL, int64_t ldal, int64_t strideAL,
+                                       int accumulate, void *stream);
+
+/*
  * chol_wave_dot_fwd_adj -- diagnostic kernel for the reduction/broadcast
  * pattern the small-tile kernels rely on (Warp issue #1374, "adj_tile_dot is
  * missing a block-wide broadcast of adj_ret": a dot product whose result only
@@ -257,7 +349,10 @@ typedef enum {
     CHOL_K_ADJ_DIAG = 9,         /* adjoint of the factor on a diagonal tile; flops: 2 kb^3 / 3 */
     CHOL_K_ELEMENTWISE = 10,     /* triangle copies, zeroing, accumulation; bytes moved */
     CHOL_K_REDUCE = 11,          /* sums of split partial products into their target; bytes moved */
-    CHOL_K_COUNT = 12
+    CHOL_K_SOLVE = 12,           /* chol_potrs*, and the solve inside chol_potrs_adjoint*, whole
+                                    calls; flops: 2 n^2 nrhs per matrix */
+    CHOL_K_SOLVE_ADJOINT = 13,   /* the adj_L term of chol_potrs_adjoint*; flops: 4 n^2 nrhs per matrix */
+    CHOL_K_COUNT = 14
 } chol_kernel_family;
 
 #define CHOL_PROFILE_ALL 0xffffffffu

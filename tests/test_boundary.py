@@ -174,3 +174,68 @@ def test_hbm_stream_argument_errors():
     assert f(2, P1, ctypes.c_void_p(0x10000000 + 64), 1 << 20, NUL) == INVALID   # overlapping copy
     assert f(0, NUL, P2, 1 << 20, NUL) == INVALID                      # read without a source
     assert f(2, P1, P2, 0, NUL) == OK
+
+
+def test_potrs_argument_errors():
+    n = 100
+    big = ctypes.c_void_p(0x7000000000)
+    ws = ctypes.c_size_t(0)
+    assert lib.chol_potrs_workspace_size(F64, n, 3, 0, ctypes.byref(ws)) == OK and ws.value > 0
+    assert lib.chol_potrs_workspace_size(F64, 64, 3, 0, ctypes.byref(ws)) == OK and ws.value == 0
+    assert lib.chol_potrs_workspace_size(F64, n, 3, 129, ctypes.byref(ws)) == INVALID
+    need = ctypes.c_size_t(0)
+    lib.chol_potrs_workspace_size(F64, n, 3, 0, ctypes.byref(need))
+    need = need.value
+    # empty problems are no-ops
+    assert lib.chol_potrs(F64, 0, 3, NUL, 1, NUL, 3, NUL, 3, 0, NUL, 0, NUL) == OK
+    assert lib.chol_potrs(F64, n, 0, NUL, n, NUL, 1, NUL, 1, 0, NUL, 0, NUL) == OK
+    # bad dtype / sizes / leading dimensions / nulls
+    assert lib.chol_potrs(7, n, 3, P1, n, P2, 3, P3, 3, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, -1, 3, P1, n, P2, 3, P3, 3, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, n, -1, P1, n, P2, 3, P3, 3, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, n, 3, P1, n - 1, P2, 3, P3, 3, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 2, P3, 3, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, P3, 2, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, n, 3, NUL, n, P2, 3, P3, 3, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, P3, 3, 129, big, need, NUL) == INVALID
+    # X partly over B, X over L, in place with another ld
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, ctypes.c_void_p(0x20000000 + 8), 3, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, ctypes.c_void_p(0x10000000 + 80), 3, 0, big, need,
+                          NUL) == INVALID
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, P2, 4, 0, big, need, NUL) == INVALID
+    # workspace missing, short, or over an operand
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, P3, 3, 0, NUL, 0, NUL) == WS
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, P3, 3, 0, big, need - 1, NUL) == WS
+    assert lib.chol_potrs(F64, n, 3, P1, n, P2, 3, P3, 3, 0, P1, need, NUL) == INVALID
+    # batched: n > 64 not supported, stride too small, overlap
+    assert lib.chol_potrs_batched(F32, 65, 1, 2, P1, 65, 65 * 65, P2, 1, 65, P3, 1, 65, NUL) == NOTSUP
+    assert lib.chol_potrs_batched(F32, 8, 2, 2, P1, 8, 63, P2, 2, 16, P3, 2, 16, NUL) == INVALID
+    assert lib.chol_potrs_batched(F32, 8, 2, 2, P1, 8, 64, P2, 2, 15, P3, 2, 16, NUL) == INVALID
+    assert lib.chol_potrs_batched(F32, 8, 2, 2, P1, 8, 64, P2, 2, 16, ctypes.c_void_p(0x20000000 + 4), 2, 16,
+                                  NUL) == INVALID
+    assert lib.chol_potrs_batched(F32, 8, 2, 0, NUL, 8, 64, NUL, 2, 16, NUL, 2, 16, NUL) == OK
+
+
+def test_potrs_adjoint_argument_errors():
+    n, r = 100, 3
+    big = ctypes.c_void_p(0x7000000000)
+    need = ctypes.c_size_t(0)
+    assert lib.chol_potrs_adjoint_workspace_size(F64, n, r, 0, ctypes.byref(need)) == OK and need.value > 0
+    need = need.value
+    P4 = ctypes.c_void_p(0x40000000)
+    P5 = ctypes.c_void_p(0x50000000)
+    ok = (F64, n, r, P1, n, P2, r, P3, r, P4, r, P5, n, 1, 0, big, need, NUL)
+    assert lib.chol_potrs_adjoint(*ok[:-3], NUL, 0, NUL) == WS
+    # adj_B may be adj_X (same ld), not X; adj_L must stay apart from every operand
+    assert lib.chol_potrs_adjoint(F64, n, r, P1, n, P2, r, P3, r, P3, r + 1, P5, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs_adjoint(F64, n, r, P1, n, P2, r, P3, r, P2, r, P5, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs_adjoint(F64, n, r, P1, n, P2, r, P3, r, P4, r, P1, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs_adjoint(F64, n, r, P1, n, P2, r, P3, r, P4, r, P4, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs_adjoint(F64, n, r, P1, n, P2, r, P3, r, P4, r, P5, n - 1, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs_adjoint(F64, n, r, P1, n, NUL, r, P3, r, P4, r, P5, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrs_adjoint(F64, n, r, P1, n, P2, r, P3, r, P4, r, P5, n, 1, 0, P5, need, NUL) == INVALID
+    # no right-hand side: accumulate is a no-op; adj_L is still checked
+    assert lib.chol_potrs_adjoint(F64, n, 0, NUL, n, NUL, 1, NUL, 1, NUL, 1, P5, n, 1, 0, NUL, 0, NUL) == OK
+    assert lib.chol_potrs_adjoint(F64, n, 0, NUL, n, NUL, 1, NUL, 1, NUL, 1, NUL, n, 0, 0, NUL, 0, NUL) == INVALID
+    assert lib.chol_potrs_adjoint_batched(F64, 65, r, 2, P1, 65, 65 * 65, P2, r, 65 * r, P3, r, 65 * r, P4, r,
+                                          65 * r, P5, 65, 65 * 65, 1, NUL) == NOTSUP

@@ -16,6 +16,8 @@ benchmark configuration give; no dataset is involved):
 * ``gram_spd``      -- A = G G^T / n + shift * I, G iid N(0, 1) from a seed.
 * ``batched_spd``   -- A_b = B_b B_b^T / n + I, B iid N(0, 1) from a seed.
 * ``lower_normal``  -- a lower-triangular N(0, 1) upstream gradient adj_L.
+* ``normal_rhs``    -- iid N(0, 1) right-hand sides (and their upstream
+                       gradients) for the solve with the factor.
 * ``spd_condition`` -- A = Q diag(logspace(0, -log10(kappa), n)) Q^T with Q the
                        orthogonal factor of an iid N(0, 1) matrix: condition
                        number exactly kappa (the fp32 tolerance applies to
@@ -108,6 +110,13 @@ def lower_normal(n: int, seed: int = SEED_ADJ, batch: int | None = None, dtype=n
     rng = np.random.default_rng(seed)
     shape = (n, n) if batch is None else (batch, n, n)
     return np.tril(rng.standard_normal(shape)).astype(dtype)
+
+
+def normal_rhs(n: int, nrhs: int, seed: int = SEED_ADJ, batch: int | None = None, dtype=np.float64):
+    """N(0, 1) of shape [n, nrhs] or [batch, n, nrhs]."""
+    rng = np.random.default_rng(seed)
+    shape = (n, nrhs) if batch is None else (batch, n, nrhs)
+    return rng.standard_normal(shape).astype(dtype)
 
 
 def spd_condition(n: int, kappa: float, seed: int = SEED_MATRIX, batch: int | None = None,

@@ -19,6 +19,9 @@ What each function computes, and the pages it follows, is stated in
                           factorisation, used only to cross-check the formula.
 * ``dot`` / ``dot_adjoint`` -- y = a.b and a_bar += y_bar b, b_bar += y_bar a
                           (Warp issue #1374, description and repro).
+* ``potrf_upper`` / ``potrf_adjoint_upper`` -- the upper-factor form A = U^T U
+                          (U = L^T of the same matrix, upper triangle of A
+                          read) and its adjoint (G^T into the upper triangle).
 * ``potrs``            -- X = (L L^T)^{-1} B by forward and back substitution
                           against L (the solve the factor is returned for,
                           jaxmg docs, "Cholesky factorization"; the two
@@ -78,6 +81,10 @@ def _load_path(path: str):
     lib.oracle_potrf_adjoint_batched.restype = i32
     lib.oracle_potrf_adjoint_batched.argtypes = [i64, i64, dp, i64, i64, dp, i64, i64,
                                                  dp, i64, i64, i32]
+    lib.oracle_potrf_upper.restype = i32
+    lib.oracle_potrf_upper.argtypes = [i64, dp, i64, dp, i64]
+    lib.oracle_potrf_adjoint_upper.restype = i32
+    lib.oracle_potrf_adjoint_upper.argtypes = [i64, dp, i64, dp, i64, dp, i64, i32]
     lib.oracle_potrs.restype = None
     lib.oracle_potrs.argtypes = [i64, i64, dp, i64, dp, i64, dp, i64]
     lib.oracle_potrs_adjoint.restype = i32
@@ -235,3 +242,38 @@ def potrs_adjoint(L, X, adjX, adjL=None, accumulate: bool = True):
     if rc != 0:
         raise MemoryError("oracle potrs adjoint could not allocate its scratch matrix")
     return (adjB.reshape(-1) if vec else adjB), out
+
+
+def potrf_upper(A):
+    """Return ``(U, info)``: A = U^T U from A's upper triangle (stacked
+    ``[batch, n, n]`` arrays element by element); U's strict lower triangle is
+    zero."""
+    A = _f64(A)
+    lib = _load()
+    if A.ndim == 3:
+        outs = [potrf_upper(A[b]) for b in range(A.shape[0])]
+        return np.stack([o[0] for o in outs]), np.array([o[1] for o in outs], dtype=np.int32)
+    n = A.shape[0]
+    U = np.zeros_like(A)
+    info = int(lib.oracle_potrf_upper(n, _ptr(A), n, _ptr(U), n))
+    if info < 0:
+        raise MemoryError("oracle upper factor could not allocate its scratch matrices")
+    return U, info
+
+
+def potrf_adjoint_upper(U, adjU, adjA=None, accumulate: bool = True):
+    """Adjoint of the upper form: upper(adj_A) += (or =) G^T; the strict lower
+    triangle of adj_A is returned unchanged (zero if not given)."""
+    U = _f64(U)
+    adjU = _f64(adjU)
+    out = np.zeros_like(U) if adjA is None else _f64(adjA).copy()
+    lib = _load()
+    if U.ndim == 3:
+        for b in range(U.shape[0]):
+            out[b] = potrf_adjoint_upper(U[b], adjU[b], out[b], accumulate)
+        return out
+    n = U.shape[0]
+    rc = lib.oracle_potrf_adjoint_upper(n, _ptr(U), n, _ptr(adjU), n, _ptr(out), n, 1 if accumulate else 0)
+    if rc != 0:
+        raise MemoryError("oracle upper adjoint could not allocate its scratch matrices")
+    return out

@@ -251,6 +251,71 @@ int32_t oracle_potrf_adjoint_batched(int64_t n, int64_t batch,
     return bad ? -1 : 0;
 }
 
+/* Upper-factor form (uplo = U, the layout a column-major caller's lower
+ * factor has in row-major memory): A = U^T U with U upper triangular and
+ * positive diagonal, reading only the upper triangle of A.  By uniqueness of
+ * the factor, U = L^T for the lower factor L of the same symmetric matrix, so
+ * this is the lower factorisation [jaxmg-potrf] applied to A^T (whose lower
+ * triangle is A's upper triangle) and written back transposed.  U's strict
+ * lower triangle is written as zero.  Returns info as oracle_potrf.  A and U
+ * must not overlap. */
+int32_t oracle_potrf_upper(int64_t n, const double *A, int64_t lda, double *U, int64_t ldu)
+{
+    if (n <= 0)
+        return 0;
+    double *At = (double *)malloc((size_t)n * (size_t)n * sizeof(double));
+    double *L = (double *)malloc((size_t)n * (size_t)n * sizeof(double));
+    if (!At || !L) {
+        free(At); free(L);
+        return -1;
+    }
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j <= i; ++j)
+            At[(size_t)i * n + j] = AT(A, lda, j, i);       /* lower of A^T = upper of A */
+    const int32_t info = oracle_potrf(n, At, n, L, n);
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            AT(U, ldu, i, j) = (j >= i) ? L[(size_t)j * n + i] : 0.0;
+    free(At); free(L);
+    return info;
+}
+
+/* Adjoint of the upper form: with U = L^T and adj_L = adj_U^T, the gradient
+ * with respect to A's upper entries is G^T, G the lower-form adjoint
+ * [warp-1316] of (L, adj_L).  Only the upper triangles of U and adj_U are
+ * read; upper(adj_A) += G^T (accumulate != 0) or = G^T; the strict lower
+ * triangle of adj_A is not touched. */
+int32_t oracle_potrf_adjoint_upper(int64_t n, const double *U, int64_t ldu,
+                                   const double *adjU, int64_t ldau,
+                                   double *adjA, int64_t ldaa, int32_t accumulate)
+{
+    if (n <= 0)
+        return 0;
+    const size_t nn = (size_t)n * (size_t)n;
+    double *L = (double *)calloc(nn, sizeof(double));
+    double *aL = (double *)calloc(nn, sizeof(double));
+    double *G = (double *)calloc(nn, sizeof(double));
+    if (!L || !aL || !G) {
+        free(L); free(aL); free(G);
+        return -1;
+    }
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j <= i; ++j) {
+            L[(size_t)i * n + j] = AT(U, ldu, j, i);
+            aL[(size_t)i * n + j] = AT(adjU, ldau, j, i);
+        }
+    int32_t rc = oracle_potrf_adjoint(n, L, n, aL, n, G, n, 0);
+    if (rc == 0)
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t j = i; j < n; ++j) {
+                const double g = G[(size_t)j * n + i];
+                double *dst = &AT(adjA, ldaa, i, j);
+                *dst = accumulate ? *dst + g : g;
+            }
+    free(L); free(aL); free(G);
+    return rc;
+}
+
 /* Solve with the factor: X = A^{-1} B for A = L L^T, B and X n x nrhs
  * (row-major, leading dimensions ldb, ldx).  The factor is returned without a
  * solve [jaxmg-potrf]; this is the solve it is computed for, written as the

@@ -337,3 +337,66 @@ def test_potrs_adjoint_accumulate_and_overwrite():
     assert np.allclose(acc[low], start[low] + g0[low], rtol=0, atol=1e-14)
     assert np.array_equal(ovw[low], g0[low])
     assert np.array_equal(acc[~low], start[~low]) and np.array_equal(ovw[~low], start[~low])
+
+
+# ------------------------------------------------------------ upper factor ----
+# uplo = U: A = U^T U from A's upper triangle, and its adjoint.
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 200])
+def test_upper_factor_against_library_and_residual(n):
+    A = workloads.gram_spd(n, seed=60 + n)
+    U, info = oracle.potrf_upper(A)
+    assert info == 0
+    # the library's lower factor, transposed (a textbook identity: U = L^T)
+    assert np.max(np.abs(U - np.linalg.cholesky(A).T)) <= 1e-12 * np.max(np.abs(U))
+    assert np.all(np.tril(U, -1) == 0.0) and np.all(np.diag(U) > 0)
+    assert np.max(np.abs(U.T @ U - A)) <= 1e-13 * np.max(np.abs(A))
+
+
+def test_upper_factor_closed_form_and_upper_only():
+    A, E = workloads.closed_form(16)
+    U, info = oracle.potrf_upper(A)
+    assert info == 0 and np.max(np.abs(U - E.T)) <= 1e-14
+    Al = A.copy()
+    Al[np.tril_indices(16, -1)] = np.nan               # the lower triangle is never read
+    assert np.array_equal(oracle.potrf_upper(Al)[0], U)
+    bad = A.copy()
+    bad[5, 5] = -1.0                                   # pivot 6 fails, as in the lower form
+    assert oracle.potrf_upper(bad)[1] == 6
+
+
+@pytest.mark.parametrize("n", [1, 3, 5])
+def test_upper_adjoint_central_finite_differences(n):
+    A = workloads.gram_spd(n, seed=70 + n)
+    U, _ = oracle.potrf_upper(A)
+    rng = np.random.default_rng(71)
+    adjU = np.triu(rng.standard_normal((n, n)))
+    G = oracle.potrf_adjoint_upper(U, adjU)
+    f = lambda M: float(np.sum(adjU * oracle.potrf_upper(M)[0]))
+    eps = 1e-6
+    for i in range(n):
+        for j in range(i, n):
+            # perturb the upper entry only: the lower triangle is not read
+            Ap, Am = A.copy(), A.copy()
+            Ap[i, j] += eps
+            Am[i, j] -= eps
+            fd = (f(Ap) - f(Am)) / (2 * eps)
+            assert abs(fd - G[i, j]) <= 1e-7 * max(1.0, abs(fd))
+    assert np.all(np.tril(G, -1) == 0.0)
+
+
+def test_upper_adjoint_ignores_lower_inputs_and_keeps_lower_output():
+    n = 9
+    A = workloads.gram_spd(n, seed=81)
+    U, _ = oracle.potrf_upper(A)
+    rng = np.random.default_rng(82)
+    adjU = np.triu(rng.standard_normal((n, n)))
+    start = rng.standard_normal((n, n))
+    G0 = oracle.potrf_adjoint_upper(U, adjU)
+    Un, aUn = U.copy(), adjU.copy()
+    Un[np.tril_indices(n, -1)] = np.nan
+    aUn[np.tril_indices(n, -1)] = np.nan
+    G = oracle.potrf_adjoint_upper(Un, aUn, adjA=start, accumulate=True)
+    up = np.triu(np.ones((n, n), bool))
+    assert np.allclose(G[up], start[up] + G0[up], rtol=0, atol=1e-14)
+    assert np.array_equal(G[~up], start[~up])

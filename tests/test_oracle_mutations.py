@@ -42,6 +42,14 @@ MUTATIONS = [
      "const double g = (i == j) ? 2.0 * S[(size_t)i * n + i]"),
     ("adj_overwrites_when_accumulating", "AT(adjA, ldaa, i, j) += g;", "AT(adjA, ldaa, i, j) = g;"),
     ("dot_reversed_index", "y += a[k] * b[k];", "y += a[k] * b[n - 1 - k];"),
+    ("upper_reads_lower", "At[(size_t)i * n + j] = AT(A, lda, j, i);",
+     "At[(size_t)i * n + j] = AT(A, lda, i, j);"),
+    ("upper_not_transposed_back", "AT(U, ldu, i, j) = (j >= i) ? L[(size_t)j * n + i] : 0.0;",
+     "AT(U, ldu, i, j) = (j >= i) ? L[(size_t)i * n + j] : 0.0;"),
+    ("upper_adj_not_transposed", "const double g = G[(size_t)j * n + i];",
+     "const double g = G[(size_t)i * n + j];"),
+    ("upper_adj_uses_lower_adjU", "aL[(size_t)i * n + j] = AT(adjU, ldau, j, i);",
+     "aL[(size_t)i * n + j] = AT(adjU, ldau, i, j);"),
     ("potrs_forward_sign", "s -= AT(L, ldl, i, k) * AT(X, ldx, k, c);",
      "s += AT(L, ldl, i, k) * AT(X, ldx, k, c);"),
     ("potrs_back_not_transposed", "s -= AT(L, ldl, k, i) * AT(X, ldx, k, c);",
@@ -75,6 +83,10 @@ PINS = [
     pins.test_potrs_closed_forms,
     lambda: pins.test_potrs_adjoint_central_finite_differences(6, 3),
     pins.test_potrs_adjoint_chained_with_factor_adjoint_matches_matrix_calculus,
+    lambda: pins.test_upper_factor_against_library_and_residual(7),
+    pins.test_upper_factor_closed_form_and_upper_only,
+    lambda: pins.test_upper_adjoint_central_finite_differences(3),
+    pins.test_upper_adjoint_ignores_lower_inputs_and_keeps_lower_output,
 ]
 
 

@@ -20,7 +20,12 @@ from ._lib import (  # noqa: F401
     chol_potrf_adjoint_noalloc,
     chol_potrf_adjoint_workspace_size,
     chol_potrf_batched,
+    chol_potrf_adjoint_upper,
+    chol_potrf_adjoint_upper_batched,
+    chol_potrf_adjoint_upper_workspace_size,
     chol_potrf_plan,
+    chol_potrf_upper,
+    chol_potrf_upper_batched,
     chol_potrs,
     chol_potrs_adjoint,
     chol_potrs_adjoint_batched,

@@ -84,6 +84,17 @@ def _load() -> ctypes.CDLL:
     lib.chol_profile_start.argtypes = [ctypes.c_uint32]
     lib.chol_profile_stop.restype = st
     lib.chol_profile_stop.argtypes = [ctypes.c_int32, vp, vp, vp]
+    lib.chol_potrf_upper.restype = st
+    lib.chol_potrf_upper.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.chol_potrf_upper_batched.restype = st
+    lib.chol_potrf_upper_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp]
+    lib.chol_potrf_adjoint_upper.restype = st
+    lib.chol_potrf_adjoint_upper.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, i32, i64, vp, sz, vp]
+    lib.chol_potrf_adjoint_upper_batched.restype = st
+    lib.chol_potrf_adjoint_upper_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32,
+                                                     vp, sz, vp]
+    lib.chol_potrf_adjoint_upper_workspace_size.restype = st
+    lib.chol_potrf_adjoint_upper_workspace_size.argtypes = [i32, i64, i64, i64, ctypes.POINTER(sz)]
     lib.chol_potrs.restype = st
     lib.chol_potrs.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, i64, vp, sz, vp]
     lib.chol_potrs_workspace_size.restype = st
@@ -248,6 +259,72 @@ def chol_potrf_adjoint_batched(L, adjL, adjA=None, accumulate: bool = True, stre
     pa, lda, sa = _bat(adjA, "adjA")
     _check(lib.chol_potrf_adjoint_batched(_dtype_code(L), L.shape[1], L.shape[0], pl, ldl, sl, pb, ldb, sb,
                                           pa, lda, sa, 1 if accumulate else 0, _stream(stream)))
+    return adjA
+
+
+def chol_potrf_upper(A, U=None, info=None, nb: int = 0, stream=None):
+    """Upper form: returns (U, info) with A = U^T U from A's upper triangle.
+    ``U`` may be ``A`` (in place)."""
+    torch = _torch()
+    if U is None:
+        U = torch.empty_like(A)
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=A.device)
+    pa, lda = _mat(A, "A")
+    pu, ldu = _mat(U, "U")
+    _check(lib.chol_potrf_upper(_dtype_code(A), A.shape[0], pa, lda, pu, ldu, ctypes.c_void_p(info.data_ptr()),
+                                nb, _stream(stream)))
+    return U, info
+
+
+def chol_potrf_upper_batched(A, U=None, info=None, stream=None):
+    torch = _torch()
+    if U is None:
+        U = torch.empty_like(A)
+    if info is None:
+        info = torch.empty(A.shape[0], dtype=torch.int32, device=A.device)
+    pa, lda, sa = _bat(A, "A")
+    pu, ldu, su = _bat(U, "U")
+    _check(lib.chol_potrf_upper_batched(_dtype_code(A), A.shape[1], A.shape[0], pa, lda, sa, pu, ldu, su,
+                                        ctypes.c_void_p(info.data_ptr()), _stream(stream)))
+    return U, info
+
+
+def chol_potrf_adjoint_upper_workspace_size(dtype_code: int, n: int, batch: int = 1, nb: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.chol_potrf_adjoint_upper_workspace_size(dtype_code, n, batch, nb, ctypes.byref(out)))
+    return int(out.value)
+
+
+def chol_potrf_adjoint_upper(U, adjU, adjA=None, accumulate: bool = True, nb: int = 0, workspace=None,
+                             stream=None):
+    """Adjoint of the upper form: upper(adjA) += (or =) G^T.  Returns adjA."""
+    torch = _torch()
+    if adjA is None:
+        adjA = torch.zeros_like(U)
+    pu, ldu = _mat(U, "U")
+    pg, ldg = _mat(adjU, "adjU")
+    pa, lda = _mat(adjA, "adjA")
+    code = _dtype_code(U)
+    n = U.shape[0]
+    _, wptr, wbytes = _workspace(chol_potrf_adjoint_upper_workspace_size(code, n, 1, nb), U.device, workspace)
+    _check(lib.chol_potrf_adjoint_upper(code, n, pu, ldu, pg, ldg, pa, lda, 1 if accumulate else 0, nb, wptr,
+                                        wbytes, _stream(stream)))
+    return adjA
+
+
+def chol_potrf_adjoint_upper_batched(U, adjU, adjA=None, accumulate: bool = True, workspace=None, stream=None):
+    torch = _torch()
+    if adjA is None:
+        adjA = torch.zeros_like(U)
+    pu, ldu, su = _bat(U, "U")
+    pg, ldg, sg = _bat(adjU, "adjU")
+    pa, lda, sa = _bat(adjA, "adjA")
+    code = _dtype_code(U)
+    n, batch = U.shape[1], U.shape[0]
+    _, wptr, wbytes = _workspace(chol_potrf_adjoint_upper_workspace_size(code, n, batch, 0), U.device, workspace)
+    _check(lib.chol_potrf_adjoint_upper_batched(code, n, batch, pu, ldu, su, pg, ldg, sg, pa, lda, sa,
+                                                1 if accumulate else 0, wptr, wbytes, _stream(stream)))
     return adjA
 
 

@@ -50,6 +50,14 @@ chol_status blocked_potrs_adjoint(int64_t n, int64_t nrhs, const T *L, int64_t l
                                   int accumulate, int nb, void *ws, hipStream_t st);
 size_t blocked_solve_workspace(int64_t n, int nb, size_t es);
 chol_status zero_lower_batched(size_t es, int64_t n, int64_t batch, void *p, int64_t ld, int64_t stride, hipStream_t st);
+template <typename T>
+chol_status upper_to_lower(int64_t n, int64_t batch, const T *src, int64_t lds, int64_t ss, T *dst, int64_t ldd,
+                           int64_t sd, hipStream_t st);
+template <typename T>
+chol_status lower_to_upper(int64_t n, int64_t batch, T *p, int64_t ld, int64_t stride, hipStream_t st);
+template <typename T>
+chol_status add_upper_from_lower(int64_t n, int64_t batch, const T *G, int64_t ldg, int64_t sg, T *A, int64_t lda,
+                                 int64_t sa, int accumulate, hipStream_t st);
 size_t blocked_solve_adjoint_workspace(int64_t n, int64_t nrhs, int nb, size_t es);
 chol_status small_load();
 chol_status blocked_load();
@@ -391,6 +399,189 @@ chol_status chol_potrs_adjoint_batched(chol_dtype dt, int64_t n, int64_t nrhs, i
                                             (const float *)X, ldx, strideX, (const float *)adjX, ldax, strideAX,
                                             (float *)adjB, ldab, strideAB, (float *)adjL, ldal, strideAL,
                                             accumulate, st);
+}
+
+// ------------------------------------------------------------ upper form ----
+
+extern "C++" {
+namespace {
+template <typename T>
+chol_status potrf_upper_t(int64_t n, int64_t batch, const T *A, int64_t lda, int64_t sA, T *U, int64_t ldu,
+                          int64_t sU, int32_t *info, int nb, hipStream_t st)
+{
+    chol_status s = chol::upper_to_lower<T>(n, batch, A, lda, sA, U, ldu, sU, st);
+    if (s != CHOL_OK)
+        return s;
+    if (n <= CHOL_SMALL_MAX_N)
+        s = chol::small_potrf<T>((int)n, batch, U, ldu, sU, U, ldu, sU, info, 0, 0, st);
+    else
+        s = chol::blocked_potrf<T>(n, U, ldu, U, ldu, info, nb, st);
+    if (s != CHOL_OK)
+        return s;
+    return chol::lower_to_upper<T>(n, batch, U, ldu, sU, st);
+}
+
+// workspace of the upper adjoint: U^T and adj_U^T (n x n each, per matrix),
+// then the lower-form adjoint's own (single matrix, n > CHOL_SMALL_MAX_N)
+size_t upper_adjoint_workspace(int64_t n, int64_t batch, int nb, size_t es)
+{
+    const size_t mat = ((size_t)batch * n * n * es + 255) & ~(size_t)255;
+    size_t bytes = 2 * mat;
+    if (n > CHOL_SMALL_MAX_N)
+        bytes += chol::blocked_adjoint_workspace(n, nb, es, false);
+    return bytes;
+}
+
+template <typename T>
+chol_status potrf_adjoint_upper_t(int64_t n, int64_t batch, const T *U, int64_t ldu, int64_t sU, const T *adjU,
+                                  int64_t ldau, int64_t sAU, T *adjA, int64_t ldaa, int64_t sAA, int accumulate,
+                                  int nb, void *ws, hipStream_t st)
+{
+    const size_t mat = ((size_t)batch * n * n * sizeof(T) + 255) & ~(size_t)255;
+    T *Lt = (T *)ws;
+    T *Gt = (T *)((char *)ws + mat);
+    void *inner = (char *)ws + 2 * mat;
+    const int64_t nn = n * n;
+    chol_status s = chol::upper_to_lower<T>(n, batch, U, ldu, sU, Lt, n, nn, st);
+    if (s == CHOL_OK)
+        s = chol::upper_to_lower<T>(n, batch, adjU, ldau, sAU, Gt, n, nn, st);
+    if (s != CHOL_OK)
+        return s;
+    // G (lower form) written over adj_L's transposed copy
+    if (n <= CHOL_SMALL_MAX_N)
+        s = chol::small_potrf_adjoint<T>((int)n, batch, Lt, n, nn, Gt, n, nn, Gt, n, nn, 0, st);
+    else
+        s = chol::blocked_adjoint<T>(n, Lt, n, Gt, n, Gt, n, 0, nb, inner, st);
+    if (s != CHOL_OK)
+        return s;
+    return chol::add_upper_from_lower<T>(n, batch, Gt, n, nn, adjA, ldaa, sAA, accumulate, st);
+}
+} // namespace
+} // extern "C++"
+
+chol_status chol_potrf_upper(chol_dtype dt, int64_t n, const void *A, int64_t lda, void *U, int64_t ldu,
+                             int32_t *info, int64_t nb, void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n == 0)
+        return CHOL_OK;
+    if (!A || !U || !ld_ok(lda, n) || !ld_ok(ldu, n))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    if (!alias_ok(A, lda, 0, U, ldu, 0, n, 1, es))
+        return CHOL_ERR_INVALID_VALUE;
+    if (info && overlap(extent(info, 1, 1, 1, 0, 4), extent(U, n, ldu, 1, 0, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    if (dt == CHOL_F64)
+        return potrf_upper_t<double>(n, 1, (const double *)A, lda, 0, (double *)U, ldu, 0, info, b, st);
+    return potrf_upper_t<float>(n, 1, (const float *)A, lda, 0, (float *)U, ldu, 0, info, b, st);
+}
+
+chol_status chol_potrf_upper_batched(chol_dtype dt, int64_t n, int64_t batch, const void *A, int64_t lda,
+                                     int64_t strideA, void *U, int64_t ldu, int64_t strideU, int32_t *info,
+                                     void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || batch < 0)
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > CHOL_SMALL_MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    if (n == 0 || batch == 0)
+        return CHOL_OK;
+    if (!A || !U || !ld_ok(lda, n) || !ld_ok(ldu, n) || !stride_ok(strideA, lda, n, batch) ||
+        !stride_ok(strideU, ldu, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    if (batch > ((int64_t)1 << 31) - 1)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    if (!alias_ok(A, lda, strideA, U, ldu, strideU, n, batch, es))
+        return CHOL_ERR_INVALID_VALUE;
+    if (info && overlap(extent(info, 1, 1, batch, 1, 4), extent(U, n, ldu, batch, strideU, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    if (dt == CHOL_F64)
+        return potrf_upper_t<double>(n, batch, (const double *)A, lda, strideA, (double *)U, ldu, strideU, info,
+                                     DEFAULT_NB, st);
+    return potrf_upper_t<float>(n, batch, (const float *)A, lda, strideA, (float *)U, ldu, strideU, info,
+                                DEFAULT_NB, st);
+}
+
+chol_status chol_potrf_adjoint_upper_workspace_size(chol_dtype dt, int64_t n, int64_t batch, int64_t nb,
+                                                    size_t *bytes)
+{
+    if (!bytes || !valid_dtype(dt) || n < 0 || batch < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    *bytes = 0;
+    if (n == 0 || batch == 0)
+        return CHOL_OK;
+    if (n > MAX_N || (batch > 1 && n > CHOL_SMALL_MAX_N))
+        return CHOL_ERR_NOT_SUPPORTED;
+    *bytes = upper_adjoint_workspace(n, batch, nb ? (int)nb : DEFAULT_NB, esize(dt));
+    return CHOL_OK;
+}
+
+namespace {
+chol_status adjoint_upper_entry(chol_dtype dt, int64_t n, int64_t batch, const void *U, int64_t ldu, int64_t sU,
+                                const void *adjU, int64_t ldau, int64_t sAU, void *adjA, int64_t ldaa, int64_t sAA,
+                                int accumulate, int64_t nb, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || batch < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    if (batch > 1 && n > CHOL_SMALL_MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    if (n == 0 || batch == 0)
+        return CHOL_OK;
+    if (!U || !adjU || !adjA || !ld_ok(ldu, n) || !ld_ok(ldau, n) || !ld_ok(ldaa, n) ||
+        !stride_ok(sU, ldu, n, batch) || !stride_ok(sAU, ldau, n, batch) || !stride_ok(sAA, ldaa, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > MAX_N || batch > ((int64_t)1 << 31) - 1)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t es = esize(dt);
+    // adj_A may be adj_U itself (it is read into the workspace first), not U
+    if (!alias_ok(adjU, ldau, sAU, adjA, ldaa, sAA, n, batch, es) ||
+        overlap(extent(U, n, ldu, batch, sU, es), extent(adjA, n, ldaa, batch, sAA, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    const size_t need = upper_adjoint_workspace(n, batch, b, es);
+    if (!workspace || workspace_bytes < need)
+        return CHOL_ERR_WORKSPACE;
+    const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlap(ws, extent(U, n, ldu, batch, sU, es)) || overlap(ws, extent(adjU, n, ldau, batch, sAU, es)) ||
+        overlap(ws, extent(adjA, n, ldaa, batch, sAA, es)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    if (dt == CHOL_F64)
+        return potrf_adjoint_upper_t<double>(n, batch, (const double *)U, ldu, sU, (const double *)adjU, ldau, sAU,
+                                             (double *)adjA, ldaa, sAA, accumulate, b, workspace, st);
+    return potrf_adjoint_upper_t<float>(n, batch, (const float *)U, ldu, sU, (const float *)adjU, ldau, sAU,
+                                        (float *)adjA, ldaa, sAA, accumulate, b, workspace, st);
+}
+} // namespace
+
+chol_status chol_potrf_adjoint_upper(chol_dtype dt, int64_t n, const void *U, int64_t ldu, const void *adjU,
+                                     int64_t ldau, void *adjA, int64_t ldaa, int accumulate, int64_t nb,
+                                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    return adjoint_upper_entry(dt, n, 1, U, ldu, 0, adjU, ldau, 0, adjA, ldaa, 0, accumulate, nb, workspace,
+                               workspace_bytes, stream);
+}
+
+chol_status chol_potrf_adjoint_upper_batched(chol_dtype dt, int64_t n, int64_t batch, const void *U, int64_t ldu,
+                                             int64_t strideU, const void *adjU, int64_t ldau, int64_t strideAU,
+                                             void *adjA, int64_t ldaa, int64_t strideAA, int accumulate,
+                                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (valid_dtype(dt) && n > CHOL_SMALL_MAX_N && batch >= 0)
+        return CHOL_ERR_NOT_SUPPORTED;
+    return adjoint_upper_entry(dt, n, batch, U, ldu, strideU, adjU, ldau, strideAU, adjA, ldaa, strideAA, accumulate,
+                               0, workspace, workspace_bytes, stream);
 }
 
 int chol_last_hip_error(void) { return chol::g_last_hip_error.load(std::memory_order_relaxed); }

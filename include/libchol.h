@@ -200,6 +200,65 @@ chol_status chol_potrf_adjoint_batched(chol_dtype dtype, int64_t n, int64_t batc
                                        int accumulate, void *stream);
 
 /*
+ * Upper-factor form (uplo = U): A = U^T U with U upper triangular and positive
+ * diagonal, reading only the upper triangle of A; U's strict lower triangle is
+ * written as zero.  This is the row-major image of a column-major caller's
+ * lower factor: U = L^T for the lower factor L of the same matrix (jaxmg
+ * documentation, "Cholesky factorization": the factor of a symmetric
+ * positive-definite matrix is unique), so these calls run the lower-form
+ * kernels on transposed triangles: A's upper triangle is transposed into the
+ * output's lower triangle (in place when U == A), factored there in place,
+ * and transposed back (zeros below).  info as chol_potrf (column j of U is
+ * row j of L).
+ */
+chol_status chol_potrf_upper(chol_dtype dtype, int64_t n,
+                             const void *A, int64_t lda,
+                             void *U, int64_t ldu,
+                             int32_t *info, int64_t nb, void *stream);
+
+/* chol_potrf_upper for `batch` matrices, n <= CHOL_SMALL_MAX_N (strides and
+ * in-place rules as chol_potrf_batched). */
+chol_status chol_potrf_upper_batched(chol_dtype dtype, int64_t n, int64_t batch,
+                                     const void *A, int64_t lda, int64_t strideA,
+                                     void *U, int64_t ldu, int64_t strideU,
+                                     int32_t *info, void *stream);
+
+/*
+ * chol_potrf_adjoint_upper -- adjoint of the upper form.  With L = U^T and
+ * adj_L = adj_U^T, the gradient with respect to A's upper entries is G^T, G
+ * the lower-form adjoint (Warp issue #1316, resolution comment; see
+ * chol_potrf_adjoint).  Only the upper triangles of U and adj_U are read;
+ * upper(adjA) += G^T (accumulate != 0) or = G^T; adjA's strict lower triangle
+ * is not touched.  adjA may be adjU itself (same ld), with either accumulate
+ * (adj_U is copied into the workspace first); it must not overlap U.
+ * workspace: at least chol_potrf_adjoint_upper_workspace_size(dtype, n, 1,
+ * nb) bytes: the transposed copies of U and adj_U (2 n^2 elements) and, for
+ * n > CHOL_SMALL_MAX_N, the lower-form adjoint's workspace.
+ */
+chol_status chol_potrf_adjoint_upper(chol_dtype dtype, int64_t n,
+                                     const void *U, int64_t ldu,
+                                     const void *adjU, int64_t ldau,
+                                     void *adjA, int64_t ldaa,
+                                     int accumulate, int64_t nb,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* chol_potrf_adjoint_upper for `batch` matrices, n <= CHOL_SMALL_MAX_N; the
+ * workspace holds 2 * batch * n^2 elements. */
+chol_status chol_potrf_adjoint_upper_batched(chol_dtype dtype, int64_t n, int64_t batch,
+                                             const void *U, int64_t ldu, int64_t strideU,
+                                             const void *adjU, int64_t ldau, int64_t strideAU,
+                                             void *adjA, int64_t ldaa, int64_t strideAA,
+                                             int accumulate,
+                                             void *workspace, size_t workspace_bytes,
+                                             void *stream);
+
+/* Bytes of workspace the upper adjoint needs for `batch` matrices (batch > 1
+ * only with n <= CHOL_SMALL_MAX_N; larger n returns CHOL_ERR_NOT_SUPPORTED). */
+chol_status chol_potrf_adjoint_upper_workspace_size(chol_dtype dtype, int64_t n, int64_t batch, int64_t nb,
+                                                    size_t *bytes);
+
+/*
  * chol_potrs -- solve with the factor: X = A^{-1} B for A = L L^T, given the
  * lower factor L (for example from chol_potrf).  The factor is returned
  * without a solve (jaxmg documentation, "Cholesky factorization", opening

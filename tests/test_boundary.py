@@ -239,3 +239,31 @@ def test_potrs_adjoint_argument_errors():
     assert lib.chol_potrs_adjoint(F64, n, 0, NUL, n, NUL, 1, NUL, 1, NUL, 1, NUL, n, 0, 0, NUL, 0, NUL) == INVALID
     assert lib.chol_potrs_adjoint_batched(F64, 65, r, 2, P1, 65, 65 * 65, P2, r, 65 * r, P3, r, 65 * r, P4, r,
                                           65 * r, P5, 65, 65 * 65, 1, NUL) == NOTSUP
+
+
+def test_upper_argument_errors():
+    n = 100
+    big = ctypes.c_void_p(0x7000000000)
+    assert lib.chol_potrf_upper(F64, 0, NUL, 0, NUL, 0, NUL, 0, NUL) == OK
+    assert lib.chol_potrf_upper(F64, n, NUL, n, P2, n, NUL, 0, NUL) == INVALID
+    assert lib.chol_potrf_upper(F64, n, P1, n - 1, P2, n, NUL, 0, NUL) == INVALID
+    assert lib.chol_potrf_upper(F64, n, P1, n, ctypes.c_void_p(0x10000000 + 8), n, NUL, 0, NUL) == INVALID
+    assert lib.chol_potrf_upper(F64, n, P1, n, P2, n, NUL, 129, NUL) == INVALID
+    assert lib.chol_potrf_upper_batched(F32, 65, 2, P1, 65, 65 * 65, P2, 65, 65 * 65, NUL, NUL) == NOTSUP
+    assert lib.chol_potrf_upper_batched(F32, 8, 2, P1, 8, 63, P2, 8, 64, NUL, NUL) == INVALID
+    ws = ctypes.c_size_t(0)
+    assert lib.chol_potrf_adjoint_upper_workspace_size(F64, n, 1, 0, ctypes.byref(ws)) == OK
+    need = ws.value
+    assert need >= 2 * n * n * 8
+    assert lib.chol_potrf_adjoint_upper_workspace_size(F64, n, 2, 0, ctypes.byref(ws)) == NOTSUP
+    assert lib.chol_potrf_adjoint_upper_workspace_size(F32, 32, 3, 0, ctypes.byref(ws)) == OK
+    assert ws.value >= 2 * 3 * 32 * 32 * 4
+    assert lib.chol_potrf_adjoint_upper(F64, n, P1, n, P2, n, P3, n, 1, 0, NUL, 0, NUL) == WS
+    assert lib.chol_potrf_adjoint_upper(F64, n, P1, n, P2, n, P3, n, 1, 0, big, need - 1, NUL) == WS
+    assert lib.chol_potrf_adjoint_upper(F64, n, P1, n, P2, n, P3, n, 1, 0, P3, need, NUL) == INVALID
+    # adj_A over U, or partly over adj_U
+    assert lib.chol_potrf_adjoint_upper(F64, n, P1, n, P2, n, P1, n, 1, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrf_adjoint_upper(F64, n, P1, n, P2, n, ctypes.c_void_p(0x20000000 + 8), n, 1, 0, big, need,
+                                        NUL) == INVALID
+    assert lib.chol_potrf_adjoint_upper_batched(F32, 65, 2, P1, 65, 65 * 65, P2, 65, 65 * 65, P3, 65, 65 * 65, 1,
+                                                big, 1 << 30, NUL) == NOTSUP

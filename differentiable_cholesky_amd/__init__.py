@@ -34,6 +34,7 @@ from ._lib import (  # noqa: F401
     chol_potrs_workspace_size,
     chol_status_string,
     chol_wave_dot_fwd_adj,
+    chol_wave_sum_fwd_adj,
     header_entry_points,
     lib,
 )

@@ -84,6 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.chol_profile_start.argtypes = [ctypes.c_uint32]
     lib.chol_profile_stop.restype = st
     lib.chol_profile_stop.argtypes = [ctypes.c_int32, vp, vp, vp]
+    lib.chol_wave_sum_fwd_adj.restype = st
+    lib.chol_wave_sum_fwd_adj.argtypes = [i32, i64, vp, vp, vp, vp, i32, vp]
     lib.chol_potrf_upper.restype = st
     lib.chol_potrf_upper.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.chol_potrf_upper_batched.restype = st
@@ -465,6 +467,18 @@ def chol_wave_dot_fwd_adj(a, b, ybar, abar=None, bbar=None, staging: int = 0, st
     _check(lib.chol_wave_dot_fwd_adj(_dtype_code(a), a.numel(), p(a), p(b), p(y), p(ybar), p(abar), p(bbar),
                                      staging, _stream(stream)))
     return y, abar, bbar
+
+
+def chol_wave_sum_fwd_adj(a, ybar, abar=None, staging: int = 0, stream=None):
+    """Returns (y, abar) of the one-lane-result sum kernel."""
+    torch = _torch()
+    y = torch.empty(1, dtype=a.dtype, device=a.device)
+    if abar is None:
+        abar = torch.zeros_like(a)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    _check(lib.chol_wave_sum_fwd_adj(_dtype_code(a), a.numel(), p(a), p(y), p(ybar), p(abar), staging,
+                                     _stream(stream)))
+    return y, abar
 
 
 HBM_READ_SINK_FLOATS = 2048 * 256

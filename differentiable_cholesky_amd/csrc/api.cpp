@@ -64,6 +64,8 @@ chol_status blocked_load();
 template <typename T>
 chol_status wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar, T *bbar, int staging,
                      hipStream_t st);
+template <typename T>
+chol_status wave_sum(int n, const T *a, T *y, const T *ybar, T *abar, int staging, hipStream_t st);
 } // namespace chol
 
 namespace {
@@ -821,6 +823,22 @@ chol_status chol_wave_dot_fwd_adj(chol_dtype dt, int64_t n, const void *a, const
                                       (const double *)ybar, (double *)abar, (double *)bbar, staging, st);
     return chol::wave_dot<float>((int)n, (const float *)a, (const float *)b, (float *)y, (const float *)ybar,
                                  (float *)abar, (float *)bbar, staging, st);
+}
+
+chol_status chol_wave_sum_fwd_adj(chol_dtype dt, int64_t n, const void *a, void *y, const void *ybar, void *abar,
+                                  int staging, void *stream)
+{
+    if (!valid_dtype(dt) || n < 0 || n > 64 || (staging != 0 && staging != 1))
+        return CHOL_ERR_INVALID_VALUE;
+    if (!y || !ybar || (n > 0 && (!a || !abar)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    if (dt == CHOL_F64)
+        return chol::wave_sum<double>((int)n, (const double *)a, (double *)y, (const double *)ybar, (double *)abar,
+                                      staging, st);
+    return chol::wave_sum<float>((int)n, (const float *)a, (float *)y, (const float *)ybar, (float *)abar, staging,
+                                 st);
 }
 
 } // extern "C"

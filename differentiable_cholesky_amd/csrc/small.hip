@@ -583,6 +583,43 @@ k_wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar, T *bbar,
     }
 }
 
+// The sum reduction with the same ownership: y = sum_k a_k, written by lane
+// 0 only; reverse: a_bar_k += y_bar for every k, with y_bar read by lane 0 and
+// published to every lane first (the tile_sum adjoint's broadcast of the
+// upstream gradient through shared scratch that Warp issue #1374 describes).
+template <typename T>
+__global__ void __launch_bounds__(64)
+k_wave_sum(int n, const T *a, T *y, const T *ybar, T *abar, int staging)
+{
+    __shared__ T sa[64], sy[1];
+    const int l = threadIdx.x;
+    T av = T(0);
+    if (staging) {
+        sa[l] = l < n ? a[l] : T(0);
+        __syncthreads();
+        av = sa[l];
+    } else if (l < n) {
+        av = a[l];
+    }
+    T s = av;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        s += __shfl_xor(s, off, 64);
+    if (l == 0)
+        y[0] = s;
+    T yb = (l == 0) ? ybar[0] : T(0);
+    if (staging) {
+        if (l == 0)
+            sy[0] = yb;
+        __syncthreads();
+        yb = sy[0];
+    } else {
+        yb = __shfl(yb, 0, 64);
+    }
+    if (l < n)
+        abar[l] += yb;
+}
+
 // ------------------------------------------------------------------------
 // Diagonal tile of the blocked factor with its inverse (one 128-edge tile per
 // 256-thread block, lane grid 16 x 16).  The inverse X = L^{-1} is built row
@@ -830,6 +867,14 @@ chol_status wave_dot(int n, const T *a, const T *b, T *y, const T *ybar, T *abar
     return CHOL_OK;
 }
 
+template <typename T>
+chol_status wave_sum(int n, const T *a, T *y, const T *ybar, T *abar, int staging, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_wave_sum<T>), dim3(1), dim3(64), 0, st, n, a, y, ybar, abar, staging);
+    CHOL_LAUNCH_CHECK();
+    return CHOL_OK;
+}
+
 // Loads this file's kernels on the current device (their code object is
 // otherwise loaded on first launch).
 chol_status small_load()
@@ -847,7 +892,8 @@ chol_status small_load()
                                        hipStream_t);                                                      \
     template chol_status small_potrf_adjoint<T>(int, int64_t, const T *, int64_t, int64_t, const T *,     \
                                                 int64_t, int64_t, T *, int64_t, int64_t, int, hipStream_t); \
-    template chol_status wave_dot<T>(int, const T *, const T *, T *, const T *, T *, T *, int, hipStream_t);
+    template chol_status wave_dot<T>(int, const T *, const T *, T *, const T *, T *, T *, int, hipStream_t); \
+    template chol_status wave_sum<T>(int, const T *, T *, const T *, T *, int, hipStream_t);
 CHOL_INST(float)
 CHOL_INST(double)
 #undef CHOL_INST

@@ -368,6 +368,17 @@ chol_status chol_wave_dot_fwd_adj(chol_dtype dtype, int64_t n,
                                   int staging, void *stream);
 
 /*
+ * chol_wave_sum_fwd_adj -- the same ownership pattern for the sum reduction
+ * (Warp issue #1374 holds up the tile_sum adjoint as the model: it broadcasts
+ * the upstream gradient from one thread through shared scratch).  One
+ * wavefront loads a (n <= 64), reduces y = sum_k a_k, and only lane 0 writes
+ * y[0]; in the reverse pass only lane 0 reads ybar[0], which is published to
+ * every lane before abar[k] += ybar.  staging as chol_wave_dot_fwd_adj.
+ */
+chol_status chol_wave_sum_fwd_adj(chol_dtype dtype, int64_t n, const void *a, void *y,
+                                  const void *ybar, void *abar, int staging, void *stream);
+
+/*
  * chol_hbm_stream -- diagnostic: plain streaming kernels that measure the
  * device-memory ceiling the bandwidth-bound kernels are compared with.
  *   mode 0  read `bytes` from src (dst receives CHOL_HBM_READ_SINK_FLOATS

@@ -93,6 +93,10 @@ def _load_path(path: str):
     lib.oracle_dot.argtypes = [i64, dp, dp]
     lib.oracle_dot_adjoint.restype = None
     lib.oracle_dot_adjoint.argtypes = [i64, dp, dp, ctypes.c_double, dp, dp]
+    lib.oracle_sum.restype = ctypes.c_double
+    lib.oracle_sum.argtypes = [i64, dp]
+    lib.oracle_sum_adjoint.restype = None
+    lib.oracle_sum_adjoint.argtypes = [i64, ctypes.c_double, dp]
     lib.oracle_max_threads.restype = i32
     lib.oracle_max_threads.argtypes = []
     _lib = lib
@@ -277,3 +281,17 @@ def potrf_adjoint_upper(U, adjU, adjA=None, accumulate: bool = True):
     if rc != 0:
         raise MemoryError("oracle upper adjoint could not allocate its scratch matrices")
     return out
+
+
+def wsum(a) -> float:
+    """y = sum_k a_k (ascending order)."""
+    a = _f64(a)
+    assert a.ndim == 1
+    return float(_load().oracle_sum(a.size, _ptr(a)))
+
+
+def wsum_adjoint(n: int, ybar: float):
+    """a_bar for y = sum a given y_bar, starting from zero."""
+    abar = np.zeros(n)
+    _load().oracle_sum_adjoint(n, float(ybar), _ptr(abar))
+    return abar

@@ -415,6 +415,23 @@ void oracle_dot_adjoint(int64_t n, const double *a, const double *b, double ybar
     }
 }
 
+/* Sum and its adjoint (the tile_sum reduction [warp-1374] names as the model
+ * for broadcasting the upstream gradient):
+ *   y = sum_k a_k ;   a_bar_k += y_bar. */
+double oracle_sum(int64_t n, const double *a)
+{
+    double y = 0.0;
+    for (int64_t k = 0; k < n; ++k)
+        y += a[k];
+    return y;
+}
+
+void oracle_sum_adjoint(int64_t n, double ybar, double *abar)
+{
+    for (int64_t k = 0; k < n; ++k)
+        abar[k] += ybar;
+}
+
 int32_t oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -267,3 +267,10 @@ def test_upper_argument_errors():
                                         NUL) == INVALID
     assert lib.chol_potrf_adjoint_upper_batched(F32, 65, 2, P1, 65, 65 * 65, P2, 65, 65 * 65, P3, 65, 65 * 65, 1,
                                                 big, 1 << 30, NUL) == NOTSUP
+
+
+def test_wave_sum_argument_errors():
+    assert lib.chol_wave_sum_fwd_adj(F32, 65, P1, P2, P3, P1, 0, NUL) == INVALID
+    assert lib.chol_wave_sum_fwd_adj(F32, 16, P1, P2, P3, P1, 2, NUL) == INVALID
+    assert lib.chol_wave_sum_fwd_adj(F32, 16, NUL, P2, P3, P1, 0, NUL) == INVALID
+    assert lib.chol_wave_sum_fwd_adj(7, 16, P1, P2, P3, P1, 0, NUL) == INVALID

@@ -400,3 +400,18 @@ def test_upper_adjoint_ignores_lower_inputs_and_keeps_lower_output():
     up = np.triu(np.ones((n, n), bool))
     assert np.allclose(G[up], start[up] + G0[up], rtol=0, atol=1e-14)
     assert np.array_equal(G[~up], start[~up])
+
+
+def test_sum_closed_form_and_adjoint():
+    # y = sum a, a_bar = y_bar everywhere; with a = 1..16 (the repro's vector) y = 136
+    a = np.arange(1.0, 17.0)
+    assert oracle.wsum(a) == 136.0
+    assert oracle.wsum(np.array([])) == 0.0
+    assert np.array_equal(oracle.wsum_adjoint(16, 2.5), np.full(16, 2.5))
+    # central differences on a random vector
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(9)
+    g = oracle.wsum_adjoint(9, 1.0)
+    for k in range(9):
+        e = np.zeros(9); e[k] = 1e-3
+        assert abs((oracle.wsum(v + e) - oracle.wsum(v - e)) / 2e-3 - g[k]) <= 1e-12

@@ -63,6 +63,8 @@ MUTATIONS = [
     ("potrs_adj_L_transposed", "g += W[(size_t)i * n + k] * AT(L, ldl, k, j);",
      "g += W[(size_t)i * n + k] * AT(L, ldl, j, k);"),
     ("dot_adjoint_swapped", "abar[k] += ybar * b[k];", "abar[k] += ybar * a[k];"),
+    ("sum_skips_last", "for (int64_t k = 0; k < n; ++k)\n        y += a[k];", "for (int64_t k = 0; k + 1 < n; ++k)\n        y += a[k];"),
+    ("sum_adjoint_halved", "abar[k] += ybar;", "abar[k] += 0.5 * ybar;"),
 ]
 
 PINS = [
@@ -87,6 +89,7 @@ PINS = [
     pins.test_upper_factor_closed_form_and_upper_only,
     lambda: pins.test_upper_adjoint_central_finite_differences(3),
     pins.test_upper_adjoint_ignores_lower_inputs_and_keeps_lower_output,
+    pins.test_sum_closed_form_and_adjoint,
 ]
 
 

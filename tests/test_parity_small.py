@@ -246,3 +246,20 @@ def test_wave_dot_one_lane_result(dtype, staging):
     y, abar2, _ = dc().chol_wave_dot_fwd_adj(a, b, dev(np.array([2.0], dtype=dtype)), abar=abar,
                                              staging=staging)
     assert np.array_equal(host(abar2).astype(np.float64), 3.0 * g["grad_a"])
+
+
+@pytest.mark.parametrize("staging", [0, 1])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_wave_sum_one_lane_result(dtype, staging):
+    # the sum's result is written by one lane; its upstream gradient is read
+    # by one lane and must reach every element's gradient
+    a = np.arange(1.0, 17.0).astype(dtype)
+    y, abar = dc().chol_wave_sum_fwd_adj(dev(a), dev(np.array([2.0], dtype=dtype)), staging=staging)
+    assert float(host(y)[0]) == oracle.wsum(a) == 136.0
+    assert np.array_equal(host(abar).astype(np.float64), oracle.wsum_adjoint(16, 2.0))
+    y, abar = dc().chol_wave_sum_fwd_adj(dev(a), dev(np.array([1.0], dtype=dtype)), abar=abar, staging=staging)
+    assert np.array_equal(host(abar).astype(np.float64), np.full(16, 3.0))
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(61).astype(dtype)
+    y, _ = dc().chol_wave_sum_fwd_adj(dev(v), dev(np.array([1.0], dtype=dtype)), staging=staging)
+    assert abs(float(host(y)[0]) - oracle.wsum(v)) <= (1e-12 if dtype == np.float64 else 1e-5) * np.sum(np.abs(v))

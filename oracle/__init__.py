@@ -22,6 +22,9 @@ What each function computes, and the pages it follows, is stated in
 * ``potrf_upper`` / ``potrf_adjoint_upper`` -- the upper-factor form A = U^T U
                           (U = L^T of the same matrix, upper triangle of A
                           read) and its adjoint (G^T into the upper triangle).
+* ``zpotrf`` / ``zpotrf_adjoint`` -- the Hermitian complex factor A = L L^H
+                          and its adjoint (the same formula with conjugate
+                          transposes; the diagonal's real part in Phi).
 * ``potrs``            -- X = (L L^T)^{-1} B by forward and back substitution
                           against L (the solve the factor is returned for,
                           jaxmg docs, "Cholesky factorization"; the two
@@ -93,6 +96,10 @@ def _load_path(path: str):
     lib.oracle_dot.argtypes = [i64, dp, dp]
     lib.oracle_dot_adjoint.restype = None
     lib.oracle_dot_adjoint.argtypes = [i64, dp, dp, ctypes.c_double, dp, dp]
+    lib.oracle_zpotrf.restype = i32
+    lib.oracle_zpotrf.argtypes = [i64, dp, i64, dp, i64]
+    lib.oracle_zpotrf_adjoint.restype = i32
+    lib.oracle_zpotrf_adjoint.argtypes = [i64, dp, i64, dp, i64, dp, i64, i32]
     lib.oracle_sum.restype = ctypes.c_double
     lib.oracle_sum.argtypes = [i64, dp]
     lib.oracle_sum_adjoint.restype = None
@@ -295,3 +302,37 @@ def wsum_adjoint(n: int, ybar: float):
     abar = np.zeros(n)
     _load().oracle_sum_adjoint(n, float(ybar), _ptr(abar))
     return abar
+
+
+def _c128(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.complex128))
+
+
+def zpotrf(A):
+    """Return ``(L, info)``, A = L L^H (complex128; stacked arrays element by
+    element).  Only the lower triangle of A is read."""
+    A = _c128(A)
+    if A.ndim == 3:
+        outs = [zpotrf(A[b]) for b in range(A.shape[0])]
+        return np.stack([o[0] for o in outs]), np.array([o[1] for o in outs], dtype=np.int32)
+    n = A.shape[0]
+    L = np.zeros_like(A)
+    info = int(_load().oracle_zpotrf(n, _ptr(A), n, _ptr(L), n))
+    return L, info
+
+
+def zpotrf_adjoint(L, adjL, adjA=None, accumulate: bool = True):
+    """Adjoint of the Hermitian factor: lower(adj_A) += (or =) G, gradients as
+    d/dRe + i d/dIm; the strict upper triangle of adj_A is returned unchanged."""
+    L = _c128(L)
+    adjL = _c128(adjL)
+    out = np.zeros_like(L) if adjA is None else _c128(adjA).copy()
+    if L.ndim == 3:
+        for b in range(L.shape[0]):
+            out[b] = zpotrf_adjoint(L[b], adjL[b], out[b], accumulate)
+        return out
+    n = L.shape[0]
+    rc = _load().oracle_zpotrf_adjoint(n, _ptr(L), n, _ptr(adjL), n, _ptr(out), n, 1 if accumulate else 0)
+    if rc != 0:
+        raise MemoryError("oracle complex adjoint could not allocate its scratch matrices")
+    return out

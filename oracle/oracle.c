@@ -42,6 +42,7 @@
  * OpenMP is used only to split independent rows, columns or batch elements
  * over threads; every element is still computed by one plain loop.
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -314,6 +315,107 @@ int32_t oracle_potrf_adjoint_upper(int64_t n, const double *U, int64_t ldu,
             }
     free(L); free(aL); free(G);
     return rc;
+}
+
+/* Hermitian complex factor A = L L^H [jaxmg-potrf: the factor of a symmetric
+ * or Hermitian positive-definite matrix], column by column, complex128 stored
+ * as (re, im) pairs, row-major, leading dimensions in complex elements:
+ *   d      = Re(A_jj) - sum_{k<j} |L_jk|^2 ;  fail unless d > 0
+ *   L_jj   = sqrt(d)                               (real)
+ *   L_ij   = (A_ij - sum_{k<j} L_ik conj(L_jk)) / L_jj   for i > j
+ * Only the lower triangle of A is read; the imaginary part of its diagonal is
+ * ignored (a Hermitian matrix has a real diagonal).  L's strict upper
+ * triangle is written as zero.  info as oracle_potrf. */
+#define ZAT(p, ld, i, j) ((p)[(int64_t)(i) * (ld) + (j)])
+int32_t oracle_zpotrf(int64_t n, const double complex *A, int64_t lda, double complex *L, int64_t ldl)
+{
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = i + 1; j < n; ++j)
+            ZAT(L, ldl, i, j) = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        double d = creal(ZAT(A, lda, j, j));
+        for (int64_t k = 0; k < j; ++k) {
+            const double complex l = ZAT(L, ldl, j, k);
+            d -= creal(l) * creal(l) + cimag(l) * cimag(l);
+        }
+        if (!(d > 0.0))
+            return (int32_t)(j + 1);
+        const double djj = sqrt(d);
+        ZAT(L, ldl, j, j) = djj;
+#pragma omp parallel for schedule(static) if (n - j > 256)
+        for (int64_t i = j + 1; i < n; ++i) {
+            double complex s = ZAT(A, lda, i, j);
+            for (int64_t k = 0; k < j; ++k)
+                s -= ZAT(L, ldl, i, k) * conj(ZAT(L, ldl, j, k));
+            ZAT(L, ldl, i, j) = CMPLX(creal(s) / djj, cimag(s) / djj);
+        }
+    }
+    return 0;
+}
+
+/* Its adjoint: the formula of [warp-1316] with conjugate transposes.  With
+ * gradients taken as adj_X = dloss/dRe(X) + i dloss/dIm(X):
+ *   M = L^H tril(adj_L)                  (lower triangle used)
+ *   P = Phi(M)      Phi: lower triangle, diagonal -> Re(diagonal) / 2
+ *   X = L^{-H} P    (back substitution with L^H)
+ *   S = X L^{-1}    (solve with L from the right)
+ *   G = Phi(S + S^H):  G_ij = S_ij + conj(S_ji) (i > j),  G_ii = Re(S_ii)
+ *   lower(adj_A) += G (accumulate != 0) or = G.
+ * G is the gradient with respect to the entries the factor reads: Re and Im
+ * of A_ij below the diagonal, and the real diagonal. */
+int32_t oracle_zpotrf_adjoint(int64_t n, const double complex *L, int64_t ldl,
+                              const double complex *adjL, int64_t ldal,
+                              double complex *adjA, int64_t ldaa, int32_t accumulate)
+{
+    if (n <= 0)
+        return 0;
+    const size_t nn = (size_t)n * (size_t)n;
+    double complex *M = (double complex *)calloc(nn, sizeof(double complex));
+    double complex *X = (double complex *)calloc(nn, sizeof(double complex));
+    double complex *S = (double complex *)calloc(nn, sizeof(double complex));
+    if (!M || !X || !S) {
+        free(M); free(X); free(S);
+        return -1;
+    }
+    /* M_ij = sum_{k >= i} conj(L_ki) adjL_kj for i >= j */
+#pragma omp parallel for schedule(dynamic, 16) if (n > 64)
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = i; k < n; ++k) {
+            const double complex lki = conj(ZAT(L, ldl, k, i));
+            for (int64_t j = 0; j <= i; ++j)
+                M[(size_t)i * n + j] += lki * ZAT(adjL, ldal, k, j);
+        }
+    for (int64_t i = 0; i < n; ++i)
+        M[(size_t)i * n + i] = 0.5 * creal(M[(size_t)i * n + i]);
+    /* X = L^{-H} P:  X_i = (P_i - sum_{t > i} conj(L_ti) X_t) / L_ii, i = n-1 .. 0 */
+    for (int64_t i = n - 1; i >= 0; --i) {
+        const double lii = creal(ZAT(L, ldl, i, i));
+        for (int64_t c = 0; c < n; ++c) {
+            double complex s = M[(size_t)i * n + c];
+            for (int64_t t = i + 1; t < n; ++t)
+                s -= conj(ZAT(L, ldl, t, i)) * X[(size_t)t * n + c];
+            X[(size_t)i * n + c] = CMPLX(creal(s) / lii, cimag(s) / lii);
+        }
+    }
+    /* S = X L^{-1}:  S_rj = (X_rj - sum_{k > j} S_rk L_kj) / L_jj, j = n-1 .. 0 */
+#pragma omp parallel for schedule(static) if (n > 64)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t j = n - 1; j >= 0; --j) {
+            double complex s = X[(size_t)r * n + j];
+            for (int64_t k = j + 1; k < n; ++k)
+                s -= S[(size_t)r * n + k] * ZAT(L, ldl, k, j);
+            const double ljj = creal(ZAT(L, ldl, j, j));
+            S[(size_t)r * n + j] = CMPLX(creal(s) / ljj, cimag(s) / ljj);
+        }
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j <= i; ++j) {
+            const double complex g = (i == j) ? (double complex)creal(S[(size_t)i * n + i])
+                                              : S[(size_t)i * n + j] + conj(S[(size_t)j * n + i]);
+            double complex *dst = &ZAT(adjA, ldaa, i, j);
+            *dst = accumulate ? *dst + g : g;
+        }
+    free(M); free(X); free(S);
+    return 0;
 }
 
 /* Solve with the factor: X = A^{-1} B for A = L L^T, B and X n x nrhs

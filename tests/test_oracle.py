@@ -415,3 +415,89 @@ def test_sum_closed_form_and_adjoint():
     for k in range(9):
         e = np.zeros(9); e[k] = 1e-3
         assert abs((oracle.wsum(v + e) - oracle.wsum(v - e)) / 2e-3 - g[k]) <= 1e-12
+
+
+# ------------------------------------------------------- Hermitian complex ----
+# A = L L^H (complex128) and its adjoint, gradients as d/dRe + i d/dIm.
+
+def _herm(n, seed):
+    rng = np.random.default_rng(seed)
+    G = rng.standard_normal((n, n)) + 1j * rng.standard_normal((n, n))
+    A = G @ G.conj().T / n + np.eye(n)
+    return rng, (A + A.conj().T) / 2
+
+
+@pytest.mark.parametrize("n", [1, 2, 9, 100])
+def test_complex_factor_against_library(n):
+    rng, A = _herm(n, 90 + n)
+    L, info = oracle.zpotrf(A)
+    assert info == 0
+    assert np.max(np.abs(L - np.linalg.cholesky(A))) <= 1e-12 * np.max(np.abs(L))
+    assert np.all(np.triu(L, 1) == 0) and np.all(np.diag(L).imag == 0) and np.all(np.diag(L).real > 0)
+    assert np.max(np.abs(L @ L.conj().T - A)) <= 1e-13 * np.max(np.abs(A))
+
+
+def test_complex_factor_special_cases():
+    # a closed form: A = E E^H with E lower, real positive diagonal, complex subdiagonal
+    n = 12
+    E = np.diag(np.linspace(1.0, 2.0, n)).astype(complex)
+    E[np.arange(1, n), np.arange(n - 1)] = 0.5 - 0.25j
+    L, info = oracle.zpotrf(E @ E.conj().T)
+    assert info == 0 and np.max(np.abs(L - E)) <= 1e-14
+    # real input: exactly the real factor
+    _, A = _herm(8, 3)
+    Ar = A.real.copy()
+    Ar = (Ar + Ar.T) / 2 + 0 * np.eye(8)
+    Lr, _ = oracle.potrf(Ar)
+    assert np.array_equal(oracle.zpotrf(Ar.astype(complex))[0], Lr.astype(complex))
+    # only the lower triangle and the real part of the diagonal are read
+    Ap = A.copy()
+    Ap[np.triu_indices(8, 1)] = np.nan
+    Ap[np.diag_indices(8)] += 5j
+    assert np.array_equal(oracle.zpotrf(Ap)[0], oracle.zpotrf(A)[0])
+    bad = A.copy()
+    bad[4, 4] = -1.0
+    assert oracle.zpotrf(bad)[1] == 5
+
+
+@pytest.mark.parametrize("n", [1, 3, 5])
+def test_complex_adjoint_central_finite_differences(n):
+    rng, A = _herm(n, 95 + n)
+    L, _ = oracle.zpotrf(A)
+    aL = np.tril(rng.standard_normal((n, n)) + 1j * rng.standard_normal((n, n)))
+    G = oracle.zpotrf_adjoint(L, aL)
+    f = lambda M: float(np.real(np.sum(np.conj(aL) * oracle.zpotrf(M)[0])))
+    eps = 1e-6
+    for i in range(n):
+        for j in range(i + 1):
+            for part in ((1.0,) if i == j else (1.0, 1j)):
+                Ap, Am = A.copy(), A.copy()
+                Ap[i, j] += eps * part
+                Am[i, j] -= eps * part
+                fd = (f(Ap) - f(Am)) / (2 * eps)
+                got = G[i, j].real if part == 1.0 else G[i, j].imag
+                assert abs(fd - got) <= 1e-7 * max(1.0, abs(fd)), (i, j, part)
+    assert np.all(np.diag(G).imag == 0) and np.all(np.triu(G, 1) == 0)
+
+
+def test_complex_adjoint_invariants():
+    rng, A = _herm(10, 97)
+    L, _ = oracle.zpotrf(A)
+    # adj_L = L gives half the identity, as in the real case
+    assert np.max(np.abs(oracle.zpotrf_adjoint(L, L) - 0.5 * np.eye(10))) <= 1e-14
+    # real factor and real adj_L: the real adjoint
+    Ar = A.real.copy()
+    Lr, _ = oracle.potrf((Ar + Ar.T) / 2)
+    aL = np.tril(rng.standard_normal((10, 10)))
+    assert np.max(np.abs(oracle.zpotrf_adjoint(Lr, aL) - oracle.potrf_adjoint(Lr, aL))) <= 1e-14
+    # linear in adj_L over the reals, and accumulate / overwrite
+    aL1 = np.tril(rng.standard_normal((10, 10)) + 1j * rng.standard_normal((10, 10)))
+    aL2 = np.tril(rng.standard_normal((10, 10)) + 1j * rng.standard_normal((10, 10)))
+    g1, g2 = oracle.zpotrf_adjoint(L, aL1), oracle.zpotrf_adjoint(L, aL2)
+    assert np.max(np.abs(oracle.zpotrf_adjoint(L, 2 * aL1 - aL2) - (2 * g1 - g2))) <= 1e-13
+    start = rng.standard_normal((10, 10)) + 1j * rng.standard_normal((10, 10))
+    acc = oracle.zpotrf_adjoint(L, aL1, adjA=start, accumulate=True)
+    ovw = oracle.zpotrf_adjoint(L, aL1, adjA=start, accumulate=False)
+    low = np.tril(np.ones((10, 10), bool))
+    assert np.allclose(acc[low], start[low] + g1[low], rtol=0, atol=1e-14)
+    assert np.array_equal(ovw[low], g1[low]) and np.array_equal(acc[~low], start[~low])

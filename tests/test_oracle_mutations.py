@@ -50,6 +50,16 @@ MUTATIONS = [
      "const double g = G[(size_t)i * n + j];"),
     ("upper_adj_uses_lower_adjU", "aL[(size_t)i * n + j] = AT(adjU, ldau, j, i);",
      "aL[(size_t)i * n + j] = AT(adjU, ldau, i, j);"),
+    ("zpotrf_no_conj", "s -= ZAT(L, ldl, i, k) * conj(ZAT(L, ldl, j, k));",
+     "s -= ZAT(L, ldl, i, k) * ZAT(L, ldl, j, k);"),
+    ("zadj_M_no_conj", "const double complex lki = conj(ZAT(L, ldl, k, i));",
+     "const double complex lki = ZAT(L, ldl, k, i);"),
+    ("zadj_phi_no_halving", "M[(size_t)i * n + i] = 0.5 * creal(M[(size_t)i * n + i]);",
+     "M[(size_t)i * n + i] = creal(M[(size_t)i * n + i]);"),
+    ("zadj_solve1_no_conj", "s -= conj(ZAT(L, ldl, t, i)) * X[(size_t)t * n + c];",
+     "s -= ZAT(L, ldl, t, i) * X[(size_t)t * n + c];"),
+    ("zadj_sym_no_conj", ": S[(size_t)i * n + j] + conj(S[(size_t)j * n + i]);",
+     ": S[(size_t)i * n + j] + S[(size_t)j * n + i];"),
     ("potrs_forward_sign", "s -= AT(L, ldl, i, k) * AT(X, ldx, k, c);",
      "s += AT(L, ldl, i, k) * AT(X, ldx, k, c);"),
     ("potrs_back_not_transposed", "s -= AT(L, ldl, k, i) * AT(X, ldx, k, c);",
@@ -90,6 +100,10 @@ PINS = [
     lambda: pins.test_upper_adjoint_central_finite_differences(3),
     pins.test_upper_adjoint_ignores_lower_inputs_and_keeps_lower_output,
     pins.test_sum_closed_form_and_adjoint,
+    lambda: pins.test_complex_factor_against_library(9),
+    pins.test_complex_factor_special_cases,
+    lambda: pins.test_complex_adjoint_central_finite_differences(5),
+    pins.test_complex_adjoint_invariants,
 ]
 
 

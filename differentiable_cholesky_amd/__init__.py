@@ -6,6 +6,8 @@ builds it (``build``).  Importing the package loads ``libchol.so`` and fails
 loudly if it has not been built.
 """
 from ._lib import (  # noqa: F401
+    CHOL_C64,
+    CHOL_C128,
     CHOL_F32,
     CHOL_F64,
     CholError,
@@ -17,9 +19,14 @@ from ._lib import (  # noqa: F401
     chol_potrf,
     chol_potrf_adjoint,
     chol_potrf_adjoint_batched,
+    chol_potrf_adjoint_hermitian,
+    chol_potrf_adjoint_hermitian_batched,
     chol_potrf_adjoint_noalloc,
     chol_potrf_adjoint_workspace_size,
     chol_potrf_batched,
+    chol_potrf_hermitian,
+    chol_potrf_hermitian_batched,
+    chol_potrf_hermitian_workspace_size,
     chol_potrf_adjoint_upper,
     chol_potrf_adjoint_upper_batched,
     chol_potrf_adjoint_upper_workspace_size,

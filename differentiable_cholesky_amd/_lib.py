@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libchol.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "libchol.h")
 
-CHOL_F32, CHOL_F64 = 0, 1
+CHOL_F32, CHOL_F64, CHOL_C64, CHOL_C128 = 0, 1, 2, 3
 CHOL_OK, CHOL_ERR_INVALID_VALUE, CHOL_ERR_NOT_SUPPORTED, CHOL_ERR_WORKSPACE, CHOL_ERR_HIP = range(5)
 SMALL_MAX_N = 64
 MAX_NB = 128
@@ -84,6 +84,17 @@ def _load() -> ctypes.CDLL:
     lib.chol_profile_start.argtypes = [ctypes.c_uint32]
     lib.chol_profile_stop.restype = st
     lib.chol_profile_stop.argtypes = [ctypes.c_int32, vp, vp, vp]
+    lib.chol_potrf_hermitian.restype = st
+    lib.chol_potrf_hermitian.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, vp, sz, vp]
+    lib.chol_potrf_hermitian_batched.restype = st
+    lib.chol_potrf_hermitian_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, sz, vp]
+    lib.chol_potrf_adjoint_hermitian.restype = st
+    lib.chol_potrf_adjoint_hermitian.argtypes = [i32, i64, vp, i64, vp, i64, vp, i64, i32, i64, vp, sz, vp]
+    lib.chol_potrf_adjoint_hermitian_batched.restype = st
+    lib.chol_potrf_adjoint_hermitian_batched.argtypes = [i32, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                                         i32, vp, sz, vp]
+    lib.chol_potrf_hermitian_workspace_size.restype = st
+    lib.chol_potrf_hermitian_workspace_size.argtypes = [i32, i64, i64, i64, i32, ctypes.POINTER(sz)]
     lib.chol_wave_sum_fwd_adj.restype = st
     lib.chol_wave_sum_fwd_adj.argtypes = [i32, i64, vp, vp, vp, vp, i32, vp]
     lib.chol_potrf_upper.restype = st
@@ -261,6 +272,88 @@ def chol_potrf_adjoint_batched(L, adjL, adjA=None, accumulate: bool = True, stre
     pa, lda, sa = _bat(adjA, "adjA")
     _check(lib.chol_potrf_adjoint_batched(_dtype_code(L), L.shape[1], L.shape[0], pl, ldl, sl, pb, ldb, sb,
                                           pa, lda, sa, 1 if accumulate else 0, _stream(stream)))
+    return adjA
+
+
+def _cdtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.complex64:
+        return CHOL_C64
+    if t.dtype == torch.complex128:
+        return CHOL_C128
+    raise TypeError(f"the Hermitian factor takes complex64 or complex128, got {t.dtype}")
+
+
+def chol_potrf_hermitian_workspace_size(dtype_code: int, n: int, batch: int = 1, nb: int = 0,
+                                        adjoint: bool = False) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.chol_potrf_hermitian_workspace_size(dtype_code, n, batch, nb, 1 if adjoint else 0, ctypes.byref(out)))
+    return int(out.value)
+
+
+def chol_potrf_hermitian(A, L=None, info=None, nb: int = 0, workspace=None, stream=None):
+    """Hermitian complex factor A = L L^H: returns (L, info); ``L`` may be ``A``."""
+    torch = _torch()
+    if L is None:
+        L = torch.empty_like(A)
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=A.device)
+    pa, lda = _mat(A, "A")
+    pl, ldl = _mat(L, "L")
+    code = _cdtype_code(A)
+    n = A.shape[0]
+    _, wptr, wbytes = _workspace(chol_potrf_hermitian_workspace_size(code, n, 1, nb), A.device, workspace)
+    _check(lib.chol_potrf_hermitian(code, n, pa, lda, pl, ldl, ctypes.c_void_p(info.data_ptr()), nb, wptr, wbytes,
+                                    _stream(stream)))
+    return L, info
+
+
+def chol_potrf_hermitian_batched(A, L=None, info=None, workspace=None, stream=None):
+    torch = _torch()
+    if L is None:
+        L = torch.empty_like(A)
+    if info is None:
+        info = torch.empty(A.shape[0], dtype=torch.int32, device=A.device)
+    pa, lda, sa = _bat(A, "A")
+    pl, ldl, sl = _bat(L, "L")
+    code = _cdtype_code(A)
+    n, batch = A.shape[1], A.shape[0]
+    _, wptr, wbytes = _workspace(chol_potrf_hermitian_workspace_size(code, n, batch, 0), A.device, workspace)
+    _check(lib.chol_potrf_hermitian_batched(code, n, batch, pa, lda, sa, pl, ldl, sl,
+                                            ctypes.c_void_p(info.data_ptr()), wptr, wbytes, _stream(stream)))
+    return L, info
+
+
+def chol_potrf_adjoint_hermitian(L, adjL, adjA=None, accumulate: bool = True, nb: int = 0, workspace=None,
+                                 stream=None):
+    """Adjoint of the Hermitian factor: lower(adjA) += (or =) G.  Returns adjA."""
+    torch = _torch()
+    if adjA is None:
+        adjA = torch.zeros_like(L)
+    pl, ldl = _mat(L, "L")
+    pg, ldg = _mat(adjL, "adjL")
+    pa, lda = _mat(adjA, "adjA")
+    code = _cdtype_code(L)
+    n = L.shape[0]
+    _, wptr, wbytes = _workspace(chol_potrf_hermitian_workspace_size(code, n, 1, nb, True), L.device, workspace)
+    _check(lib.chol_potrf_adjoint_hermitian(code, n, pl, ldl, pg, ldg, pa, lda, 1 if accumulate else 0, nb, wptr,
+                                            wbytes, _stream(stream)))
+    return adjA
+
+
+def chol_potrf_adjoint_hermitian_batched(L, adjL, adjA=None, accumulate: bool = True, workspace=None,
+                                         stream=None):
+    torch = _torch()
+    if adjA is None:
+        adjA = torch.zeros_like(L)
+    pl, ldl, sl = _bat(L, "L")
+    pg, ldg, sg = _bat(adjL, "adjL")
+    pa, lda, sa = _bat(adjA, "adjA")
+    code = _cdtype_code(L)
+    n, batch = L.shape[1], L.shape[0]
+    _, wptr, wbytes = _workspace(chol_potrf_hermitian_workspace_size(code, n, batch, 0, True), L.device, workspace)
+    _check(lib.chol_potrf_adjoint_hermitian_batched(code, n, batch, pl, ldl, sl, pg, ldg, sg, pa, lda, sa,
+                                                    1 if accumulate else 0, wptr, wbytes, _stream(stream)))
     return adjA
 
 

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libchol.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["small.hip", "blocked.hip", "api.cpp", "profile.cpp", "side.cpp", "plan.cpp", "stream.hip", "solve.hip", "upper.hip"]
+SOURCES = ["small.hip", "blocked.hip", "api.cpp", "profile.cpp", "side.cpp", "plan.cpp", "stream.hip", "solve.hip", "upper.hip", "complex.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

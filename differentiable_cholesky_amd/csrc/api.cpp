@@ -51,6 +51,19 @@ chol_status blocked_potrs_adjoint(int64_t n, int64_t nrhs, const T *L, int64_t l
 size_t blocked_solve_workspace(int64_t n, int nb, size_t es);
 chol_status zero_lower_batched(size_t es, int64_t n, int64_t batch, void *p, int64_t ld, int64_t stride, hipStream_t st);
 template <typename T>
+chol_status herm_embed(int64_t n, int64_t batch, const T *A, int64_t lda, int64_t sA, T *M, int64_t ldm, int64_t sM,
+                       hipStream_t st);
+template <typename T>
+chol_status herm_embed_adjoint(int64_t n, int64_t batch, const T *adjL, int64_t ldal, int64_t sAL, T *M,
+                               int64_t ldm, int64_t sM, hipStream_t st);
+template <typename T>
+chol_status herm_read_back(int64_t n, int64_t batch, const T *E, int64_t lde, int64_t sE, T *L, int64_t ldl,
+                           int64_t sL, hipStream_t st);
+template <typename T>
+chol_status herm_fold(int64_t n, int64_t batch, const T *GM, int64_t ldg, int64_t sG, T *adjA, int64_t lda,
+                      int64_t sA, int accumulate, hipStream_t st);
+chol_status herm_info(int64_t batch, int32_t *info, hipStream_t st);
+template <typename T>
 chol_status upper_to_lower(int64_t n, int64_t batch, const T *src, int64_t lds, int64_t ss, T *dst, int64_t ldd,
                            int64_t sd, hipStream_t st);
 template <typename T>
@@ -584,6 +597,214 @@ chol_status chol_potrf_adjoint_upper_batched(chol_dtype dt, int64_t n, int64_t b
         return CHOL_ERR_NOT_SUPPORTED;
     return adjoint_upper_entry(dt, n, batch, U, ldu, strideU, adjU, ldau, strideAU, adjA, ldaa, strideAA, accumulate,
                                0, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------ Hermitian complex ----
+
+extern "C++" {
+namespace {
+bool complex_dtype(chol_dtype dt) { return dt == CHOL_C64 || dt == CHOL_C128; }
+size_t real_esize(chol_dtype dt) { return dt == CHOL_C128 ? 8 : 4; }
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// the real 2n x 2n embedding of each matrix (per matrix 4 n^2 reals)
+size_t herm_embedding_bytes(int64_t n, int64_t batch, size_t res)
+{
+    return align_up((size_t)batch * 4 * n * n * res);
+}
+
+template <typename T>
+chol_status herm_potrf_t(int64_t n, int64_t batch, const T *A, int64_t lda, int64_t sA, T *L, int64_t ldl,
+                         int64_t sL, int32_t *info, int nb, void *ws, hipStream_t st)
+{
+    T *M = (T *)ws;
+    const int64_t m = 2 * n, mm = m * m;
+    chol_status s = chol::herm_embed<T>(n, batch, A, lda, sA, M, m, mm, st);
+    if (s != CHOL_OK)
+        return s;
+    if (m <= CHOL_SMALL_MAX_N)
+        s = chol::small_potrf<T>((int)m, batch, M, m, mm, M, m, mm, info, 0, 0, st);
+    else
+        s = chol::blocked_potrf<T>(m, M, m, M, m, info, nb, st);
+    if (s == CHOL_OK)
+        s = chol::herm_read_back<T>(n, batch, M, m, mm, L, ldl, sL, st);
+    if (s == CHOL_OK)
+        s = chol::herm_info(batch, info, st);
+    return s;
+}
+
+size_t herm_adjoint_bytes(int64_t n, int64_t batch, int nb, size_t res)
+{
+    size_t bytes = 2 * herm_embedding_bytes(n, batch, res);
+    if (2 * n > CHOL_SMALL_MAX_N)
+        bytes += chol::blocked_adjoint_workspace(2 * n, nb, res, false);
+    return bytes;
+}
+
+template <typename T>
+chol_status herm_adjoint_t(int64_t n, int64_t batch, const T *L, int64_t ldl, int64_t sL, const T *adjL, int64_t ldal,
+                           int64_t sAL, T *adjA, int64_t ldaa, int64_t sAA, int accumulate, int nb, void *ws,
+                           hipStream_t st)
+{
+    const size_t emb = herm_embedding_bytes(n, batch, sizeof(T));
+    T *E = (T *)ws;
+    T *aE = (T *)((char *)ws + emb);
+    void *inner = (char *)ws + 2 * emb;
+    const int64_t m = 2 * n, mm = m * m;
+    chol_status s = chol::herm_embed<T>(n, batch, L, ldl, sL, E, m, mm, st);
+    if (s == CHOL_OK)
+        s = chol::herm_embed_adjoint<T>(n, batch, adjL, ldal, sAL, aE, m, mm, st);
+    if (s != CHOL_OK)
+        return s;
+    // the real gradient of M's lower entries, written over adj_E
+    if (m <= CHOL_SMALL_MAX_N)
+        s = chol::small_potrf_adjoint<T>((int)m, batch, E, m, mm, aE, m, mm, aE, m, mm, 0, st);
+    else
+        s = chol::blocked_adjoint<T>(m, E, m, aE, m, aE, m, 0, nb, inner, st);
+    if (s != CHOL_OK)
+        return s;
+    return chol::herm_fold<T>(n, batch, aE, m, mm, adjA, ldaa, sAA, accumulate, st);
+}
+
+// argument checks shared by the Hermitian entry points (sizes in complex
+// elements); CHOL_OK with *noop for empty problems
+chol_status herm_args(chol_dtype dt, int64_t n, int64_t batch, const void *X, int64_t ldx, int64_t sX, const void *Y,
+                      int64_t ldy, int64_t sY, bool *noop)
+{
+    *noop = false;
+    if (!complex_dtype(dt) || n < 0 || batch < 0)
+        return CHOL_ERR_INVALID_VALUE;
+    if (n == 0 || batch == 0) {
+        *noop = true;
+        return CHOL_OK;
+    }
+    if (!X || !Y || !ld_ok(ldx, n) || !ld_ok(ldy, n) || !stride_ok(sX, ldx, n, batch) || !stride_ok(sY, ldy, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    if (n > MAX_N / 2 || batch > ((int64_t)1 << 31) - 1)
+        return CHOL_ERR_NOT_SUPPORTED;
+    return CHOL_OK;
+}
+} // namespace
+} // extern "C++"
+
+chol_status chol_potrf_hermitian_workspace_size(chol_dtype dt, int64_t n, int64_t batch, int64_t nb, int adjoint,
+                                                size_t *bytes)
+{
+    if (!bytes || !complex_dtype(dt) || n < 0 || batch < 0 || !nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    *bytes = 0;
+    if (n == 0 || batch == 0)
+        return CHOL_OK;
+    if (n > MAX_N / 2 || (batch > 1 && 2 * n > CHOL_SMALL_MAX_N))
+        return CHOL_ERR_NOT_SUPPORTED;
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    *bytes = adjoint ? herm_adjoint_bytes(n, batch, b, real_esize(dt)) : herm_embedding_bytes(n, batch, real_esize(dt));
+    return CHOL_OK;
+}
+
+namespace {
+chol_status herm_potrf_entry(chol_dtype dt, int64_t n, int64_t batch, const void *A, int64_t lda, int64_t sA, void *L,
+                             int64_t ldl, int64_t sL, int32_t *info, int64_t nb, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    if (!nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    bool noop;
+    chol_status s = herm_args(dt, n, batch, A, lda, sA, L, ldl, sL, &noop);
+    if (s != CHOL_OK || noop)
+        return s;
+    if (batch > 1 && 2 * n > CHOL_SMALL_MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t ce = 2 * real_esize(dt);
+    if (!alias_ok(A, lda, sA, L, ldl, sL, n, batch, ce))
+        return CHOL_ERR_INVALID_VALUE;
+    if (info && overlap(extent(info, 1, 1, batch, 1, 4), extent(L, n, ldl, batch, sL, ce)))
+        return CHOL_ERR_INVALID_VALUE;
+    const size_t need = herm_embedding_bytes(n, batch, real_esize(dt));
+    if (!workspace || workspace_bytes < need)
+        return CHOL_ERR_WORKSPACE;
+    const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlap(ws, extent(A, n, lda, batch, sA, ce)) || overlap(ws, extent(L, n, ldl, batch, sL, ce)) ||
+        (info && overlap(ws, extent(info, 1, 1, batch, 1, 4))))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    if (dt == CHOL_C128)
+        return herm_potrf_t<double>(n, batch, (const double *)A, lda, sA, (double *)L, ldl, sL, info, b, workspace, st);
+    return herm_potrf_t<float>(n, batch, (const float *)A, lda, sA, (float *)L, ldl, sL, info, b, workspace, st);
+}
+
+chol_status herm_adjoint_entry(chol_dtype dt, int64_t n, int64_t batch, const void *L, int64_t ldl, int64_t sL,
+                               const void *adjL, int64_t ldal, int64_t sAL, void *adjA, int64_t ldaa, int64_t sAA,
+                               int accumulate, int64_t nb, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!nb_ok(nb))
+        return CHOL_ERR_INVALID_VALUE;
+    bool noop;
+    chol_status s = herm_args(dt, n, batch, L, ldl, sL, adjL, ldal, sAL, &noop);
+    if (s != CHOL_OK || noop)
+        return s;
+    if (!adjA || !ld_ok(ldaa, n) || !stride_ok(sAA, ldaa, n, batch))
+        return CHOL_ERR_INVALID_VALUE;
+    if (batch > 1 && 2 * n > CHOL_SMALL_MAX_N)
+        return CHOL_ERR_NOT_SUPPORTED;
+    const size_t ce = 2 * real_esize(dt);
+    // adj_A may be adj_L itself (adj_L is embedded first), not L
+    if (!alias_ok(adjL, ldal, sAL, adjA, ldaa, sAA, n, batch, ce) ||
+        overlap(extent(L, n, ldl, batch, sL, ce), extent(adjA, n, ldaa, batch, sAA, ce)))
+        return CHOL_ERR_INVALID_VALUE;
+    const int b = nb ? (int)nb : DEFAULT_NB;
+    const size_t need = herm_adjoint_bytes(n, batch, b, real_esize(dt));
+    if (!workspace || workspace_bytes < need)
+        return CHOL_ERR_WORKSPACE;
+    const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlap(ws, extent(L, n, ldl, batch, sL, ce)) || overlap(ws, extent(adjL, n, ldal, batch, sAL, ce)) ||
+        overlap(ws, extent(adjA, n, ldaa, batch, sAA, ce)))
+        return CHOL_ERR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    clear_stale_status();
+    if (dt == CHOL_C128)
+        return herm_adjoint_t<double>(n, batch, (const double *)L, ldl, sL, (const double *)adjL, ldal, sAL,
+                                      (double *)adjA, ldaa, sAA, accumulate, b, workspace, st);
+    return herm_adjoint_t<float>(n, batch, (const float *)L, ldl, sL, (const float *)adjL, ldal, sAL, (float *)adjA,
+                                 ldaa, sAA, accumulate, b, workspace, st);
+}
+} // namespace
+
+chol_status chol_potrf_hermitian(chol_dtype dt, int64_t n, const void *A, int64_t lda, void *L, int64_t ldl,
+                                 int32_t *info, int64_t nb, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return herm_potrf_entry(dt, n, 1, A, lda, 0, L, ldl, 0, info, nb, workspace, workspace_bytes, stream);
+}
+
+chol_status chol_potrf_hermitian_batched(chol_dtype dt, int64_t n, int64_t batch, const void *A, int64_t lda,
+                                         int64_t strideA, void *L, int64_t ldl, int64_t strideL, int32_t *info,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (complex_dtype(dt) && 2 * n > CHOL_SMALL_MAX_N && batch >= 0)
+        return CHOL_ERR_NOT_SUPPORTED;
+    return herm_potrf_entry(dt, n, batch, A, lda, strideA, L, ldl, strideL, info, 0, workspace, workspace_bytes,
+                            stream);
+}
+
+chol_status chol_potrf_adjoint_hermitian(chol_dtype dt, int64_t n, const void *L, int64_t ldl, const void *adjL,
+                                         int64_t ldal, void *adjA, int64_t ldaa, int accumulate, int64_t nb,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    return herm_adjoint_entry(dt, n, 1, L, ldl, 0, adjL, ldal, 0, adjA, ldaa, 0, accumulate, nb, workspace,
+                              workspace_bytes, stream);
+}
+
+chol_status chol_potrf_adjoint_hermitian_batched(chol_dtype dt, int64_t n, int64_t batch, const void *L, int64_t ldl,
+                                                 int64_t strideL, const void *adjL, int64_t ldal, int64_t strideAL,
+                                                 void *adjA, int64_t ldaa, int64_t strideAA, int accumulate,
+                                                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (complex_dtype(dt) && 2 * n > CHOL_SMALL_MAX_N && batch >= 0)
+        return CHOL_ERR_NOT_SUPPORTED;
+    return herm_adjoint_entry(dt, n, batch, L, ldl, strideL, adjL, ldal, strideAL, adjA, ldaa, strideAA, accumulate,
+                              0, workspace, workspace_bytes, stream);
 }
 
 int chol_last_hip_error(void) { return chol::g_last_hip_error.load(std::memory_order_relaxed); }

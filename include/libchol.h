@@ -78,7 +78,10 @@ extern "C" {
  * lengthen the serial chain of diagonal factors that the updates hide. */
 #define CHOL_MAX_NB 128
 
-typedef enum { CHOL_F32 = 0, CHOL_F64 = 1 } chol_dtype;
+/* Real types for every entry point; the complex types (interleaved real and
+ * imaginary parts, complex64 = 2 x fp32, complex128 = 2 x fp64) only for the
+ * chol_potrf_hermitian* family. */
+typedef enum { CHOL_F32 = 0, CHOL_F64 = 1, CHOL_C64 = 2, CHOL_C128 = 3 } chol_dtype;
 
 typedef enum {
     CHOL_OK = 0,
@@ -257,6 +260,67 @@ chol_status chol_potrf_adjoint_upper_batched(chol_dtype dtype, int64_t n, int64_
  * only with n <= CHOL_SMALL_MAX_N; larger n returns CHOL_ERR_NOT_SUPPORTED). */
 chol_status chol_potrf_adjoint_upper_workspace_size(chol_dtype dtype, int64_t n, int64_t batch, int64_t nb,
                                                     size_t *bytes);
+
+/*
+ * Hermitian complex factor A = L L^H (jaxmg documentation, "Cholesky
+ * factorization": the factor of a symmetric or Hermitian positive-definite
+ * matrix) and its adjoint, dtype CHOL_C64 or CHOL_C128.  Complex arrays hold
+ * interleaved (re, im) pairs; leading dimensions and strides count complex
+ * elements.  Only the lower triangle of A is read, and of its diagonal only
+ * the real part; L has a real positive diagonal and zeros above it.
+ * Gradients are taken as d/dRe + i d/dIm.  The adjoint is the real one with
+ * conjugate transposes: M = L^H tril(adj_L), Phi keeps the lower triangle
+ * and the real part of the diagonal halved, S = L^{-H} Phi(M) L^{-1}, and
+ * G_ij = S_ij + conj(S_ji) below the diagonal, G_ii = Re S_ii (so the
+ * imaginary part of adj_L's diagonal does not enter).
+ * Both run the real kernels on the real embedding: each entry x + iy becomes
+ * the 2 x 2 block [[x, -y], [y, x]], the Hermitian A a symmetric 2n x 2n
+ * matrix whose real factor is the embedding of L (read back from the first
+ * column of each block), and the adjoint folds the real gradient of the
+ * embedding's lower entries back onto the complex ones.  This costs twice
+ * the flops of a native complex factor.
+ *   workspace  device scratch of chol_potrf_hermitian_workspace_size bytes
+ *              (adjoint = 0 for the factor, 1 for the adjoint): the 2n x 2n
+ *              embeddings (4 n^2 reals per matrix, twice for the adjoint) and,
+ *              for 2n > CHOL_SMALL_MAX_N, the real adjoint's workspace.  It
+ *              must not overlap the operands.
+ *   L == A (same ld and stride) factors in place; adjA may be adjL (it is
+ *   read into the workspace first), with either accumulate; adjA must not
+ *   overlap L.  lower(adjA) += G (accumulate != 0) or = G.
+ * info as chol_potrf, in complex columns.  The batched forms take n <= 32
+ * (the embedding's 2n <= CHOL_SMALL_MAX_N); larger n returns
+ * CHOL_ERR_NOT_SUPPORTED.
+ */
+chol_status chol_potrf_hermitian(chol_dtype dtype, int64_t n,
+                                 const void *A, int64_t lda,
+                                 void *L, int64_t ldl,
+                                 int32_t *info, int64_t nb,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+chol_status chol_potrf_hermitian_batched(chol_dtype dtype, int64_t n, int64_t batch,
+                                         const void *A, int64_t lda, int64_t strideA,
+                                         void *L, int64_t ldl, int64_t strideL,
+                                         int32_t *info,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
+chol_status chol_potrf_adjoint_hermitian(chol_dtype dtype, int64_t n,
+                                         const void *L, int64_t ldl,
+                                         const void *adjL, int64_t ldal,
+                                         void *adjA, int64_t ldaa,
+                                         int accumulate, int64_t nb,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
+chol_status chol_potrf_adjoint_hermitian_batched(chol_dtype dtype, int64_t n, int64_t batch,
+                                                 const void *L, int64_t ldl, int64_t strideL,
+                                                 const void *adjL, int64_t ldal, int64_t strideAL,
+                                                 void *adjA, int64_t ldaa, int64_t strideAA,
+                                                 int accumulate,
+                                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of the Hermitian factor (adjoint == 0) or its adjoint
+ * (adjoint != 0) for `batch` matrices. */
+chol_status chol_potrf_hermitian_workspace_size(chol_dtype dtype, int64_t n, int64_t batch, int64_t nb,
+                                                int adjoint, size_t *bytes);
 
 /*
  * chol_potrs -- solve with the factor: X = A^{-1} B for A = L L^T, given the

@@ -274,3 +274,36 @@ def test_wave_sum_argument_errors():
     assert lib.chol_wave_sum_fwd_adj(F32, 16, P1, P2, P3, P1, 2, NUL) == INVALID
     assert lib.chol_wave_sum_fwd_adj(F32, 16, NUL, P2, P3, P1, 0, NUL) == INVALID
     assert lib.chol_wave_sum_fwd_adj(7, 16, P1, P2, P3, P1, 0, NUL) == INVALID
+
+
+def test_hermitian_argument_errors():
+    C64, C128 = _lib.CHOL_C64, _lib.CHOL_C128
+    n = 100
+    big = ctypes.c_void_p(0x7000000000)
+    ws = ctypes.c_size_t(0)
+    assert lib.chol_potrf_hermitian_workspace_size(C128, n, 1, 0, 0, ctypes.byref(ws)) == OK
+    assert ws.value >= 4 * n * n * 8
+    need = ws.value
+    assert lib.chol_potrf_hermitian_workspace_size(C128, n, 1, 0, 1, ctypes.byref(ws)) == OK
+    assert ws.value >= 2 * 4 * n * n * 8
+    need_adj = ws.value
+    assert lib.chol_potrf_hermitian_workspace_size(F64, n, 1, 0, 0, ctypes.byref(ws)) == INVALID
+    assert lib.chol_potrf_hermitian_workspace_size(C64, 33, 2, 0, 0, ctypes.byref(ws)) == NOTSUP
+    # real dtypes are rejected by the Hermitian entry points and complex ones by the real ones
+    assert lib.chol_potrf_hermitian(F64, n, P1, n, P2, n, NUL, 0, big, need, NUL) == INVALID
+    assert lib.chol_potrf(C128, n, P1, n, P2, n, NUL, 0, NUL) == INVALID
+    assert lib.chol_potrf_hermitian(C128, 0, NUL, 0, NUL, 0, NUL, 0, NUL, 0, NUL) == OK
+    assert lib.chol_potrf_hermitian(C128, n, P1, n, P2, n, NUL, 0, NUL, 0, NUL) == WS
+    assert lib.chol_potrf_hermitian(C128, n, P1, n, P2, n, NUL, 0, big, need - 1, NUL) == WS
+    assert lib.chol_potrf_hermitian(C128, n, P1, n - 1, P2, n, NUL, 0, big, need, NUL) == INVALID
+    # L partly over A (complex elements are 16 bytes), workspace over an operand
+    assert lib.chol_potrf_hermitian(C128, n, P1, n, ctypes.c_void_p(0x10000000 + 16), n, NUL, 0, big, need,
+                                    NUL) == INVALID
+    assert lib.chol_potrf_hermitian(C128, n, P1, n, P2, n, NUL, 0, P2, need, NUL) == INVALID
+    assert lib.chol_potrf_hermitian_batched(C64, 33, 2, P1, 33, 33 * 33, P2, 33, 33 * 33, NUL, big, 1 << 30,
+                                            NUL) == NOTSUP
+    # adjoint: adjA over L, missing workspace
+    assert lib.chol_potrf_adjoint_hermitian(C128, n, P1, n, P2, n, P1, n, 1, 0, big, need_adj, NUL) == INVALID
+    assert lib.chol_potrf_adjoint_hermitian(C128, n, P1, n, P2, n, P3, n, 1, 0, NUL, 0, NUL) == WS
+    assert lib.chol_potrf_adjoint_hermitian_batched(C64, 33, 2, P1, 33, 33 * 33, P2, 33, 33 * 33, P3, 33, 33 * 33,
+                                                    1, big, 1 << 30, NUL) == NOTSUP

@@ -195,6 +195,132 @@ def sampled_residual(L, A, rows):
     return worst
 
 
+def _timed(torch, fn, reps: int, warm: int = 1) -> float:
+    """Average ms of fn() over reps calls on the current stream (events
+    recorded around the whole batch of calls, after warm untimed calls)."""
+    for _ in range(warm):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def extra_rows(dc, workloads, torch, args):
+    """The entry points beyond the headline path, timed at benchmark sizes
+    (inputs resident in device memory), each with a sampled check of its
+    result; one JSON line per entry point."""
+    dev = "cuda"
+    n, nb = args.n, args.nb
+    reps = max(1, args.steps)
+    HBM = 8000.0
+    log(f"rows: building inputs (n={n})")
+    A = workloads.gram_spd(n, seed=workloads.SEED_MATRIX, shift=0.1, device=dev)
+    L, info = dc.chol_potrf(A, nb=nb)
+    torch.cuda.synchronize()
+    rows = [int(r) for r in np.linspace(0, n - 1, 6)]
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    # solve with the factor, fp64, 16 right-hand sides: bound by reading the
+    # lower triangle of L once per sweep
+    nrhs = 16
+    B = torch.from_numpy(workloads.normal_rhs(n, nrhs, seed=3)).to(dev)
+    X = torch.empty_like(B)
+    ws = torch.empty(dc.chol_potrs_workspace_size(dc.CHOL_F64, n, nrhs, nb), dtype=torch.uint8, device=dev)
+    ms = _timed(torch, lambda: dc.chol_potrs(L, B, X=X, nb=nb, workspace=ws), reps)
+    res = float(torch.linalg.norm(A[rows] @ X - B[rows]) / torch.linalg.norm(B[rows]))
+    byts = 2 * (n * (n + 1) / 2) * 8 + 4 * n * nrhs * 8
+    emit({"row": "potrs", "dtype": "f64", "n": n, "nrhs": nrhs, "ms": round(ms, 3),
+          "bound": "hbm", "algorithmic_bytes": byts, "achieved_GBs": round(byts / (ms * 1e-3) / 1e9, 1),
+          "frac": round(byts / (ms * 1e-3) / 1e9 / HBM, 4), "sampled_residual": res})
+    # its adjoint: the same solve, then [Q; P] = [S|X]^T tril(L) and the
+    # lower-only product into adj_L (read + write of its lower triangle)
+    gX = torch.from_numpy(workloads.normal_rhs(n, nrhs, seed=4)).to(dev)
+    gB = torch.empty_like(gX)
+    gL = torch.zeros_like(A)
+    wsa = torch.empty(dc.chol_potrs_adjoint_workspace_size(dc.CHOL_F64, n, nrhs, nb), dtype=torch.uint8,
+                      device=dev)
+    ms = _timed(torch, lambda: dc.chol_potrs_adjoint(L, X, gX, adjB=gB, adjL=gL, accumulate=False, nb=nb,
+                                                      workspace=wsa), reps)
+    byts = 5 * (n * (n + 1) / 2) * 8 + 8 * n * nrhs * 8
+    emit({"row": "potrs_adjoint", "dtype": "f64", "n": n, "nrhs": nrhs, "ms": round(ms, 3),
+          "bound": "hbm", "algorithmic_bytes": byts, "achieved_GBs": round(byts / (ms * 1e-3) / 1e9, 1),
+          "frac": round(byts / (ms * 1e-3) / 1e9 / HBM, 4)})
+    del gL, wsa, gX, gB, ws, X, B
+
+    # batched solve, fp32, 65536 systems of 32 with one right-hand side
+    bt, bn = args.batch, args.batch_n
+    Ab = torch.from_numpy(workloads.batched_spd(bt, bn, dtype=np.float32)).to(dev)
+    Lb, _ = dc.chol_potrf_batched(Ab)
+    bb = torch.from_numpy(workloads.normal_rhs(bn, 1, seed=5, batch=bt, dtype=np.float32)).to(dev)
+    xb = torch.empty_like(bb)
+    ms = _timed(torch, lambda: dc.chol_potrs_batched(Lb, bb, X=xb), reps * 4)
+    res = float((torch.linalg.norm(Ab[:64] @ xb[:64] - bb[:64]) / torch.linalg.norm(bb[:64])))
+    byts = bt * ((bn * (bn + 1) / 2) + 2 * bn) * 4
+    emit({"row": "potrs_batched", "dtype": "f32", "batch": bt, "n": bn, "nrhs": 1, "ms": round(ms, 4),
+          "matrices_per_s": round(bt / (ms * 1e-3), 1), "bound": "hbm", "algorithmic_bytes": byts,
+          "achieved_GBs": round(byts / (ms * 1e-3) / 1e9, 1), "frac": round(byts / (ms * 1e-3) / 1e9 / HBM, 4),
+          "sampled_residual": res})
+    del Ab, Lb, bb, xb
+
+    # upper form, fp64: the lower factor on transposed triangles (two extra
+    # triangle transpositions); U must be exactly the lower factor transposed
+    U = torch.empty_like(A)
+    ms = _timed(torch, lambda: dc.chol_potrf_upper(A, U=U, nb=nb), reps)
+    same = bool(torch.equal(U[rows], L.t()[rows]))
+    emit({"row": "potrf_upper", "dtype": "f64", "n": n, "ms": round(ms, 3), "bound": "mfma",
+          "flops": n ** 3 / 3, "achieved_TFs": round(n ** 3 / 3 / (ms * 1e-3) / 1e12, 2),
+          "frac": round(n ** 3 / 3 / (ms * 1e-3) / 1e12 / 78.6, 4), "equals_lower_transposed": same})
+    gU = torch.triu(torch.from_numpy(workloads.lower_normal(n, seed=6).T.copy()).to(dev))
+    gA = torch.zeros_like(A)
+    wsu = torch.empty(dc.chol_potrf_adjoint_upper_workspace_size(dc.CHOL_F64, n, 1, nb), dtype=torch.uint8,
+                      device=dev)
+    ms = _timed(torch, lambda: dc.chol_potrf_adjoint_upper(U, gU, adjA=gA, accumulate=False, nb=nb,
+                                                            workspace=wsu), reps)
+    emit({"row": "potrf_adjoint_upper", "dtype": "f64", "n": n, "ms": round(ms, 3), "bound": "mfma",
+          "flops": 2 * n ** 3 / 3, "achieved_TFs": round(2 * n ** 3 / 3 / (ms * 1e-3) / 1e12, 2),
+          "frac": round(2 * n ** 3 / 3 / (ms * 1e-3) / 1e12 / 78.6, 4)})
+    del U, gU, gA, wsu, L, A
+    torch.cuda.empty_cache()
+
+    # Hermitian complex128 at n/2 (the real embedding is n x n): complex flops
+    # 4 (n/2)^3 / 3 for the factor, twice that for the adjoint
+    m = n // 2
+    rng = np.random.default_rng(7)
+    G = torch.complex(torch.from_numpy(rng.standard_normal((m, m))), torch.from_numpy(rng.standard_normal((m, m))))
+    G = G.to(dev)
+    Ac = G @ G.conj().t() / m
+    Ac = (Ac + Ac.conj().t()) / 2 + torch.eye(m, dtype=Ac.dtype, device=dev)
+    del G
+    Lc = torch.empty_like(Ac)
+    wsh = torch.empty(dc.chol_potrf_hermitian_workspace_size(dc.CHOL_C128, m, 1, nb), dtype=torch.uint8,
+                      device=dev)
+    ms = _timed(torch, lambda: dc.chol_potrf_hermitian(Ac, L=Lc, nb=nb, workspace=wsh), reps)
+    rr = [int(r) for r in np.linspace(0, m - 1, 6)]
+    res = float(torch.linalg.norm(Lc[rr] @ Lc.conj().t() - Ac[rr]) / torch.linalg.norm(Ac[rr]))
+    cfl = 4 * m ** 3 / 3
+    emit({"row": "potrf_hermitian", "dtype": "c128", "n": m, "ms": round(ms, 3), "bound": "mfma",
+          "complex_flops": cfl, "achieved_TFs": round(cfl / (ms * 1e-3) / 1e12, 2),
+          "real_embedding_flops": (2 * m) ** 3 / 3,
+          "frac": round(cfl / (ms * 1e-3) / 1e12 / 78.6, 4), "sampled_residual": res})
+    del wsh
+    gLc = torch.tril(torch.complex(torch.randn(m, m, dtype=torch.float64, device=dev),
+                                   torch.randn(m, m, dtype=torch.float64, device=dev)))
+    gAc = torch.zeros_like(Ac)
+    wsh = torch.empty(dc.chol_potrf_hermitian_workspace_size(dc.CHOL_C128, m, 1, nb, True), dtype=torch.uint8,
+                      device=dev)
+    ms = _timed(torch, lambda: dc.chol_potrf_adjoint_hermitian(Lc, gLc, adjA=gAc, accumulate=False, nb=nb,
+                                                                workspace=wsh), reps)
+    emit({"row": "potrf_adjoint_hermitian", "dtype": "c128", "n": m, "ms": round(ms, 3), "bound": "mfma",
+          "complex_flops": 2 * cfl, "achieved_TFs": round(2 * cfl / (ms * 1e-3) / 1e12, 2),
+          "frac": round(2 * cfl / (ms * 1e-3) / 1e12 / 78.6, 4)})
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +332,9 @@ def main():
     ap.add_argument("--batch-n", type=int, default=32)
     ap.add_argument("--cpu-sample-n", type=int, default=5632)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", action="store_true",
+                    help="only time the entry points beyond the headline path (solve and its adjoint, upper "
+                         "form, Hermitian complex form) at benchmark sizes, one JSON line each, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the library's streaming kernels on 1 GiB (read, write, copy: the HBM "
                          "ceiling, and the reference for the HBM byte counters) and exit")
@@ -249,6 +378,10 @@ def main():
 
     import differentiable_cholesky_amd as dc
     import workloads
+
+    if args.rows:
+        extra_rows(dc, workloads, torch, args)
+        return
 
     torch.cuda.set_device(0)
     dev = "cuda"

@@ -48,7 +48,7 @@ template <typename T>
 chol_status blocked_potrs_adjoint(int64_t n, int64_t nrhs, const T *L, int64_t ldl, const T *X, int64_t ldx,
                                   const T *adjX, int64_t ldax, T *adjB, int64_t ldab, T *adjL, int64_t ldal,
                                   int accumulate, int nb, void *ws, hipStream_t st);
-size_t blocked_solve_workspace(int64_t n, int nb, size_t es);
+size_t blocked_solve_workspace(int64_t n, int64_t nrhs, int nb, size_t es);
 chol_status zero_lower_batched(size_t es, int64_t n, int64_t batch, void *p, int64_t ld, int64_t stride, hipStream_t st);
 template <typename T>
 chol_status herm_embed(int64_t n, int64_t batch, const T *A, int64_t lda, int64_t sA, T *M, int64_t ldm, int64_t sM,
@@ -228,7 +228,7 @@ chol_status chol_potrs_workspace_size(chol_dtype dt, int64_t n, int64_t nrhs, in
         return CHOL_OK;
     if (n > MAX_N)
         return CHOL_ERR_NOT_SUPPORTED;
-    *bytes = chol::blocked_solve_workspace(n, nb ? (int)nb : DEFAULT_NB, esize(dt));
+    *bytes = chol::blocked_solve_workspace(n, nrhs, nb ? (int)nb : DEFAULT_NB, esize(dt));
     return CHOL_OK;
 }
 
@@ -253,7 +253,7 @@ chol_status chol_potrs(chol_dtype dt, int64_t n, int64_t nrhs, const void *L, in
                                         (float *)X, ldx, 0, st);
     }
     const int b = nb ? (int)nb : DEFAULT_NB;
-    const size_t need = chol::blocked_solve_workspace(n, b, es);
+    const size_t need = chol::blocked_solve_workspace(n, nrhs, b, es);
     if (!workspace || workspace_bytes < need)
         return CHOL_ERR_WORKSPACE;
     const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};

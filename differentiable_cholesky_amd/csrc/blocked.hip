@@ -855,6 +855,122 @@ k_splitk_sum(int M, int N, int splits, const T *part, T *c, int64_t ldc)
 
 static int64_t solve_tiles(int64_t n, int nb) { return (n + nb - 1) / nb; }
 
+// The solve's per-tile products for few right-hand sides (nrhs <= SK_N):
+// C (M x N) = or -= A (M x K) B (K x N) with K <= 128 (one tile).  With N
+// small each product is short, and the matrix-core loop, which has one
+// 16-deep chunk in flight at a time, would wait for memory once per chunk;
+// here a block loads its whole 32-row slab of A and all of B into LDS with
+// one wait, then forms its outputs on the vector ALUs.  A is row-major
+// (A_KM = 0: A(m, t) = a[m * lda + t]) or k-major (A_KM = 1: a[t * lda + m]).
+constexpr int SK_ROWS = 32, SK_K = 128, SK_N = 64;
+template <typename T, int A_KM, bool SUB>
+__global__ void __launch_bounds__(256)
+k_solve_skinny(int M, int N, int K, const T *a, int64_t lda, const T *b, int64_t ldb, T *c, int64_t ldc)
+{
+    __shared__ T sa[SK_ROWS * (SK_K + 1)];
+    __shared__ T sb[SK_K * SK_N];
+    const int r0 = blockIdx.x * SK_ROWS, c0 = blockIdx.y * SK_N;
+    const int rows = min(SK_ROWS, M - r0), cols = min(SK_N, N - c0);
+    const int tid = threadIdx.x;
+    // every load of the thread is issued before the first LDS write, so the
+    // block waits for memory once
+    constexpr int PA = SK_ROWS * SK_K / 256, PB = SK_K * SK_N / 256;
+    T va[PA], vb[PB];
+#pragma unroll
+    for (int q = 0; q < PA; ++q) {
+        const int e = tid + 256 * q;
+        const int i = A_KM ? e % SK_ROWS : e / SK_K, t = A_KM ? e / SK_ROWS : e % SK_K;
+        va[q] = T(0);
+        if (i < rows && t < K)
+            va[q] = A_KM ? a[(int64_t)t * lda + r0 + i] : a[(int64_t)(r0 + i) * lda + t];
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+        const int e = tid + 256 * q, t = e / SK_N, j = e % SK_N;
+        vb[q] = (j < cols && t < K) ? b[(int64_t)t * ldb + c0 + j] : T(0);
+    }
+#pragma unroll
+    for (int q = 0; q < PA; ++q) {
+        const int e = tid + 256 * q;
+        const int i = A_KM ? e % SK_ROWS : e / SK_K, t = A_KM ? e / SK_ROWS : e % SK_K;
+        sa[i * (SK_K + 1) + t] = va[q];
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q)
+        sb[tid + 256 * q] = vb[q];
+    __syncthreads();
+    for (int o = tid; o < rows * cols; o += 256) {
+        const int i = o / cols, j = o % cols;
+        const T *ai = sa + i * (SK_K + 1);
+        T acc0 = T(0), acc1 = T(0), acc2 = T(0), acc3 = T(0);
+        int t = 0;
+        for (; t + 4 <= K; t += 4) {
+            acc0 += ai[t] * sb[t * SK_N + j];
+            acc1 += ai[t + 1] * sb[(t + 1) * SK_N + j];
+            acc2 += ai[t + 2] * sb[(t + 2) * SK_N + j];
+            acc3 += ai[t + 3] * sb[(t + 3) * SK_N + j];
+        }
+        for (; t < K; ++t)
+            acc0 += ai[t] * sb[t * SK_N + j];
+        const T acc = (acc0 + acc1) + (acc2 + acc3);
+        T *dst = c + (int64_t)(r0 + i) * ldc + c0 + j;
+        if (SUB)
+            *dst -= acc;
+        else
+            *dst = acc;
+    }
+}
+
+template <typename T, int A_KM, bool SUB>
+static chol_status solve_skinny(int M, int N, int K, const T *a, int64_t lda, const T *b, int64_t ldb, T *c,
+                                int64_t ldc, hipStream_t st)
+{
+    if (M <= 0 || N <= 0)
+        return CHOL_OK;
+    if (K > SK_K)
+        return CHOL_ERR_INVALID_VALUE;
+    const dim3 grid((unsigned)((M + SK_ROWS - 1) / SK_ROWS), (unsigned)((N + SK_N - 1) / SK_N));
+    hipLaunchKernelGGL((k_solve_skinny<T, A_KM, SUB>), grid, dim3(256), 0, st, M, N, K, a, lda, b, ldb, c, ldc);
+    CHOL_LAUNCH_CHECK();
+    return CHOL_OK;
+}
+
+// Few right-hand sides: both sweeps with the short products above, out of
+// place so that no product reads what another block of it writes.  The
+// forward sweep leaves Y = L^{-1} X (tile k: Y_k = Linv_kk X_k, then
+// X[r0:] -= L[r0:, k] Y_k); the backward sweep writes the solution into X
+// (X_k = Linv_kk^T Y_k, then Y[:k0] -= L[k, :k0]^T X_k).
+template <typename T>
+static chol_status blocked_solve_skinny(int64_t n, int64_t nrhs, const T *L, int64_t ldl, T *X, int64_t ldx, int nb,
+                                        const T *inv, T *Y, hipStream_t st)
+{
+    const int64_t K = solve_tiles(n, nb);
+    const int N = (int)nrhs;
+    chol_status s;
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t k0 = k * nb;
+        const int kb = (int)std::min<int64_t>(nb, n - k0);
+        const int64_t r0 = k0 + kb;
+        const T *invk = inv + k * (int64_t)nb * nb;
+        if ((s = solve_skinny<T, 0, false>(kb, N, kb, invk, nb, X + k0 * ldx, ldx, Y + k0 * nrhs, nrhs, st)) != CHOL_OK)
+            return s;
+        if ((s = solve_skinny<T, 0, true>((int)(n - r0), N, kb, L + r0 * ldl + k0, ldl, Y + k0 * nrhs, nrhs,
+                                          X + r0 * ldx, ldx, st)) != CHOL_OK)
+            return s;
+    }
+    for (int64_t k = K - 1; k >= 0; --k) {
+        const int64_t k0 = k * nb;
+        const int kb = (int)std::min<int64_t>(nb, n - k0);
+        const T *invk = inv + k * (int64_t)nb * nb;
+        if ((s = solve_skinny<T, 1, false>(kb, N, kb, invk, nb, Y + k0 * nrhs, nrhs, X + k0 * ldx, ldx, st)) != CHOL_OK)
+            return s;
+        if ((s = solve_skinny<T, 1, true>((int)k0, N, kb, L + k0 * ldl, ldl, X + k0 * ldx, ldx, Y, nrhs, st)) !=
+            CHOL_OK)
+            return s;
+    }
+    return CHOL_OK;
+}
+
 template <typename T>
 static chol_status blocked_solve_on(int64_t n, int64_t nrhs, const T *L, int64_t ldl, T *X, int64_t ldx, int nb,
                                     const T *inv, hipStream_t st)
@@ -923,15 +1039,31 @@ static int solve_adj_splits(int64_t n, int64_t nrhs)
     return (int)std::max<int64_t>(1, std::min<int64_t>(32, std::min<int64_t>(want, n / 256 + 1)));
 }
 
-size_t blocked_solve_workspace(int64_t n, int nb, size_t es)
+// tile inverses, then (few right-hand sides) the forward sweep's n x nrhs result
+size_t blocked_solve_workspace(int64_t n, int64_t nrhs, int nb, size_t es)
 {
-    return align256((size_t)solve_tiles(n, nb) * nb * nb * es);
+    size_t bytes = align256((size_t)solve_tiles(n, nb) * nb * nb * es);
+    if (nrhs <= SK_N)
+        bytes += align256((size_t)n * nrhs * es);
+    return bytes;
+}
+
+template <typename T>
+static chol_status solve_sweeps(int64_t n, int64_t nrhs, const T *L, int64_t ldl, T *X, int64_t ldx, int nb,
+                                void *ws, hipStream_t st)
+{
+    const T *inv = (const T *)ws;
+    if (nrhs <= SK_N) {
+        T *Y = (T *)((char *)ws + align256((size_t)solve_tiles(n, nb) * nb * nb * sizeof(T)));
+        return blocked_solve_skinny<T>(n, nrhs, L, ldl, X, ldx, nb, inv, Y, st);
+    }
+    return blocked_solve_on<T>(n, nrhs, L, ldl, X, ldx, nb, inv, st);
 }
 
 size_t blocked_solve_adjoint_workspace(int64_t n, int64_t nrhs, int nb, size_t es)
 {
     const int sp = solve_adj_splits(n, nrhs);
-    return blocked_solve_workspace(n, nb, es) + 2 * align256((size_t)n * 2 * nrhs * es) +
+    return blocked_solve_workspace(n, nrhs, nb, es) + 2 * align256((size_t)n * 2 * nrhs * es) +
            align256((size_t)2 * nrhs * n * es) + (sp > 1 ? align256((size_t)sp * 2 * nrhs * n * es) : 0);
 }
 
@@ -946,7 +1078,7 @@ chol_status blocked_potrs(int64_t n, int64_t nrhs, const T *L, int64_t ldl, cons
         s = copy2d<T>(n, nrhs, B, ldb, X, ldx, st);
     if (s != CHOL_OK)
         return s;
-    return blocked_solve_on<T>(n, nrhs, L, ldl, X, ldx, nb, inv, st);
+    return solve_sweeps<T>(n, nrhs, L, ldl, X, ldx, nb, ws, st);
 }
 
 // adj_B = (L L^T)^{-1} adj_X; lower(adj_L) (+)= -tril((adj_B X^T + X adj_B^T) L).
@@ -960,7 +1092,8 @@ chol_status blocked_potrs_adjoint(int64_t n, int64_t nrhs, const T *L, int64_t l
 {
     char *w = (char *)ws;
     T *inv = (T *)w;
-    w += blocked_solve_workspace(n, nb, sizeof(T));
+    void *solve_ws = w;
+    w += blocked_solve_workspace(n, nrhs, nb, sizeof(T));
     T *sx = (T *)w;                       // [S | X], n x 2 nrhs
     w += align256((size_t)n * 2 * nrhs * sizeof(T));
     T *xs = (T *)w;                       // [X | S]
@@ -977,7 +1110,7 @@ chol_status blocked_potrs_adjoint(int64_t n, int64_t nrhs, const T *L, int64_t l
         if (s == CHOL_OK && adjB != adjX)
             s = copy2d<T>(n, nrhs, adjX, ldax, adjB, ldab, st);
         if (s == CHOL_OK)
-            s = blocked_solve_on<T>(n, nrhs, L, ldl, adjB, ldab, nb, inv, st);
+            s = solve_sweeps<T>(n, nrhs, L, ldl, adjB, ldab, nb, solve_ws, st);
     }
     prof::Scope ps(CHOL_K_SOLVE_ADJOINT, st, 4.0 * n * n * nrhs);
     if (s == CHOL_OK)

@@ -108,7 +108,7 @@ def test_single_small_solve_through_potrs(dt):
 
 @pytest.mark.parametrize("dt", [np.float64, np.float32])
 @pytest.mark.parametrize("n,nrhs,nb", [(65, 1, 0), (100, 3, 32), (129, 1, 0), (300, 7, 64), (520, 130, 96),
-                                       (1000, 16, 0), (1030, 1, 128)])
+                                       (1000, 16, 0), (1030, 1, 128), (400, 64, 0), (400, 65, 0)])
 def test_blocked_solve_and_adjoint(n, nrhs, nb, dt):
     L = _factor(n, 200 + n, dt)
     B = workloads.normal_rhs(n, nrhs, seed=11, dtype=dt)

@@ -297,11 +297,21 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         }
         prof::Scope ps(CHOL_K_TRAILING_UPDATE, sx, flops);
         // the narrow updates of single panels (128 deep) and those with few
-        // 128 x 128 tiles take 64 x 64 tiles: a 128-deep 128 x 128 tile is
+        // 128 x 128 tiles take 64 x 128 tiles: a 128-deep 128 x 128 tile is
         // ~20 us of one CU's matrix cores, and a short launch is as long as
-        // its slowest tile
-        const int64_t tiles128 = ((M + 127) / 128) * ((w + 127) / 128);
-        if (!tri && (Kd <= 128 || tiles128 < 256))
+        // its slowest tile (up to 3 x 256 of the smaller tiles are resident
+        // at once, three per CU: nothing runs beside these launches)
+        if (!tri) {
+            const int64_t tiles128 = ((M + 127) / 128) * ((w + 127) / 128);
+            if (Kd <= 128 || tiles128 <= 384)
+                return gemm<T, OP_MK, OP_MK, C_SUB_LOWER, 64>(p, 1, sx);
+            return gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx);
+        }
+        // a far-triangle part of at most half a round of the persistent grid
+        // runs as the halves (64 x 128) of its tiles: one round of items half
+        // as long, on the same slots (two per CU, so a CU with one of them
+        // still has room for the diagonal factor beside it)
+        if (2 * (int64_t)tn <= cap_x)
             return gemm<T, OP_MK, OP_MK, C_SUB_LOWER, 64>(p, 1, sx);
         return gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx);
     };

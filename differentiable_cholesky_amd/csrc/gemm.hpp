@@ -410,8 +410,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
     // so the epilogue is a plain store and no accumulator has to leave the
     // matrix-core registers for a read-modify-write.
     constexpr bool FROM_C = (CM == C_SUB || CM == C_SUB_LOWER);
-    // a lower-only update has nothing to do on a tile above the diagonal
-    if (CM == C_SUB_LOWER && r0 + TM - 1 < c0)
+    // a lower-only update has nothing to do on a tile above the diagonal (nor
+    // on the lower half of a short last triangular tile that lies past M)
+    if ((CM == C_SUB_LOWER && r0 + TM - 1 < c0) || r0 >= p.M)
         return;
     // a tile inside M x N needs no per-entry bounds test: its loads of C and
     // its stores are issued back to back, without a branch around each one
@@ -559,8 +560,11 @@ k_gemm(GemmArgs<T> p)
     __shared__ T lds[LDS_ELEMS<T, TM>];
     // tile grid: TM-row by 128-column tiles (the lower-triangular grid only
     // with square tiles, TM = 128)
-    const int TI = (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
-    const int nt = p.tn ? p.tn : (p.tri ? TI * (TI + 1) / 2 : TI * TJ);
+    // a triangular grid counts 128 x 128 tiles; with 64-row tiles each of
+    // them is two items (its upper and lower half), dynamic schedule only
+    constexpr int HALVES = TM == 64 ? 2 : 1;
+    const int TI = p.tri ? (p.M + 127) / 128 : (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
+    const int nt = (p.tn ? p.tn : (p.tri ? TI * (TI + 1) / 2 : TI * TJ)) * (p.tri ? HALVES : 1);
 
     if (SCHED == SCHED_STATIC || (SCHED == SCHED_BOTH && !p.sched)) {
         // static: one tile per block, tiles spread over the XCDs in contiguous ranges
@@ -585,11 +589,18 @@ k_gemm(GemmArgs<T> p)
             s_item = atomicAdd(p.sched, 1);
         __syncthreads();
         const int it = s_item;
+        __syncthreads();                  // every thread holds the item before s_item is rewritten
         if (it >= items)
             break;
         const int split = it / nt;
         int I, J;
-        tile_of(p.t0 + it % nt, p.tri, TJ, I, J);
+        if (HALVES == 2 && p.tri) {
+            const int t = it % nt;
+            tile_of(p.t0 + t / 2, 1, TJ, I, J);
+            I = 2 * I + (t & 1);
+        } else {
+            tile_of(p.t0 + it % nt, p.tri, TJ, I, J);
+        }
         int kbeg = 0, kend = p.K;
         if (CM == C_PARTIAL) {
             kbeg = split * p.kchunk;
@@ -627,8 +638,8 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     using namespace gemm_detail;
     if (p.M <= 0 || p.N <= 0)
         return CHOL_OK;
-    if (TM != BM && p.tri)
-        return CHOL_ERR_INVALID_VALUE;           // the triangular tile grid needs square tiles
+    if (TM != BM && p.tri && !p.sched)
+        return CHOL_ERR_INVALID_VALUE;           // halves of triangular tiles: dynamic schedule only
     p.vec = (aligned16(p.a, p.lda) ? 1 : 0) | (aligned16(p.b, p.ldb) ? 2 : 0);
     p.splits = splits;
     if constexpr (AOP == OP_SYM) {
@@ -640,7 +651,7 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         if (p.dg && p.vec == 3 && p.M % BM == 0 && (p.excl == 0 || p.excl == BM) && ((uintptr_t)p.dg % 16) == 0)
             return gemm<T, OP_SYM_DG, BOP, CM, TM>(p, splits, st);
     }
-    const int TI = (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
+    const int TI = p.tri ? (p.M + BM - 1) / BM : (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
     const int nt_all = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
     if (p.t0 < 0 || p.tn < 0 || p.t0 + (p.tn ? p.tn : nt_all) > nt_all)
         return CHOL_ERR_INVALID_VALUE;
@@ -650,7 +661,7 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     const dim3 sgrid((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1));
     if (p.sched) {
         // persistent blocks, all resident at once (two per CU the stream may use)
-        const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1);
+        const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1) * (TM != BM && p.tri ? 2 : 1);
         const unsigned dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
         if (CM == C_SUB_LOWER)
             hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN, TM>), dim3(dgrid), dim3(NT), 0, st, p);

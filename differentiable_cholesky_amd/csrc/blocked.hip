@@ -485,142 +485,127 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
     return CHOL_OK;
 }
 
-// Adjoint of chol on one kb x kb diagonal tile (kb <= 128), in place on the
-// lower triangle of Wb, from the tile's factor L and its inverse Linv (stored
-// with its zeros, kb x kb, leading dimension ldi):
-//   M = L^T tril(Wb)          Psi = Phi(M) + Phi(M)^T (lower part of M mirrored,
-//                             diagonal M_ii), written whole into scratch s1
-//   V = Psi Linv              into s2
-//   Z = Linv^T V              G = Phi(Z) into Wb (lower); Z is symmetric, and
-//                             Sym(G) = G + G^T (lower part of Z mirrored) goes
-//                             whole into sg (the tile's dense copy, which the
-//                             symmetric products of later tile columns read
-//                             as their diagonal block)
-// and, when `slot` is given, the one term of the previous tile column's
-// trailing-update adjoint that needs G:  slot = Sym(G) Lnext  (kb x nj, row
-// major), with Lnext = L[this tile's rows, previous tile column].
-// Each stage is one 128 x 128 x 128 matrix-core product of the whole block;
-// between stages the block's global writes are made visible by the barrier.
-// Only the first stage reads masked triangles (of the caller's L and Wb); the
-// others read plain whole operands and take the pipelined K loop.
 template <typename T>
 __device__ __forceinline__ int vec_ok(const T *p, int64_t ld)
 {
     return ((uintptr_t)p % 16 == 0) && (ld % (16 / (int64_t)sizeof(T)) == 0);
 }
 
-// At most 256 registers per wave: the kernel has to fit on a CU beside a
-// block of the persistent trailing product (which holds the other half).
-template <typename T>
+// Adjoint of chol on one kb x kb diagonal tile (kb <= 128), in place on the
+// lower triangle of Wb, from the tile's factor L and its inverse Linv (stored
+// with its zeros, kb x kb, leading dimension ldi), as four stages, each one
+// kb x kb x kb matrix-core product:
+//   stage 0: M = L^T tril(Wb); Psi = Phi(M) + Phi(M)^T (the lower part of M
+//            mirrored, diagonal M_ii) whole into the scratch s1
+//   stage 1: V = Psi Linv into the scratch s2
+//   stage 2: Z = Linv^T V (symmetric); G = Phi(Z) into Wb (lower), and
+//            Sym(G) = G + G^T (the lower part of Z mirrored) whole into sg,
+//            the tile's dense copy that the symmetric products of later tile
+//            columns read as their diagonal block
+//   stage 3: when `slot` is given, the one term of the previous tile column's
+//            trailing-update adjoint that needs G: slot = Sym(G) Lnext (kb x
+//            nj, row major), Lnext = L[this tile's rows, previous tile column]
+// Each stage is a launch of two blocks, one per 64-row half of its product,
+// so that the chain of tile adjoints, which sets the pace of the sweep while
+// the trailing blocks are small, runs on two CUs (a one-block kernel doing
+// all four stages took 90 us per tile, the four launches about 65 us).  The
+// stream orders the stages, so each reads what the one before wrote.  A
+// block writes the entries (r, c), c <= r, of its own rows r and their
+// mirrors (c, r) above the diagonal, which are never entries the other block
+// writes.  Only stage 0 reads masked triangles (of the caller's L and Wb);
+// the others read plain whole operands.
+template <typename T, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-k_tile_adjoint(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv, int64_t ldi, T *s1, T *s2,
-               int64_t lds_scr, const T *Lnext, int nj, T *slot, T *sg, int64_t ldsg)
+k_tile_adjoint_stage(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv, int64_t ldi, T *s1,
+                     T *s2, int64_t lds_scr, const T *Lnext, int nj, T *slot, T *sg, int64_t ldsg)
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
-    // this one-block kernel is on the critical path of the sweep and shares
-    // its CU with blocks of the trailing product: its waves win instruction
-    // arbitration on their SIMDs
+    constexpr int TM = 64;
     __builtin_amdgcn_s_setprio(3);
-    __shared__ T lds[LDS_ELEMS<T>];
-    acc_t acc[4][4];
-    auto zero = [&]() {
+    __shared__ T lds[LDS_ELEMS<T, TM>];
+    const int r0 = (int)blockIdx.x * TM;
+    if (r0 >= kb)
+        return;
+    AccTile<T, TM> acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WaveTile<TM>::FRM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = acc_t{0, 0, 0, 0};
-    };
-    // the lower part of the accumulated (symmetric) block mirrored whole into
-    // dst (leading dimension ldd)
-    auto mirror_to = [&](T *dst, int64_t ldd) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    int r, c;
-                    acc_pos<T>(i, j, v, r, c);
-                    if (r < kb && c <= r) {
-                        dst[(int64_t)r * ldd + c] = acc[i][j][v];
-                        dst[(int64_t)c * ldd + r] = acc[i][j][v];
-                    }
-                }
-    };
+        for (int j = 0; j < WaveTile<TM>::FRN; ++j)
+            acc[i][j] = acc_t{0, 0, 0, 0};
     const int vs = vec_ok(s1, lds_scr) && vec_ok(s2, lds_scr);
     const int vi = vec_ok(inv, ldi);
-    // stage 1: M = L^T tril(Wb); A(r, t) = L[t][r] (t >= r), B(t, c) = Wb[t][c] (t >= c)
-    zero();
-    {
-        Operand<T, OP_KM_LOWER> A{L, ldl, 0, kb, vec_ok(L, ldl)};
+    if (STAGE == 0) {
+        Operand<T, OP_KM_LOWER, TM> A{L, ldl, r0, kb, vec_ok(L, ldl)};
         Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, vec_ok(Wb, ldw)};
-        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false>(acc, A, B, 0, kb, lds);
-    }
-    mirror_to(s1, lds_scr);
-    __threadfence_block();
-    __syncthreads();
-    // stage 2: V = Psi Linv; A(r, t) = Psi[r][t], B(t, c) = Linv[t][c]
-    zero();
-    {
-        Operand<T, OP_MK> A{s1, lds_scr, 0, kb, vs};
+        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, false, false, TM>(acc, A, B, 0, kb, lds);
+    } else if (STAGE == 1) {
+        Operand<T, OP_MK, TM> A{s1, lds_scr, r0, kb, vs};
         Operand<T, OP_KM> B{inv, ldi, 0, kb, vs && vi};
-        tile_mma<T, OP_MK, OP_KM, false>(acc, A, B, 0, kb, lds);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                int r, c;
-                acc_pos<T>(i, j, v, r, c);
-                if (r < kb && c < kb)
-                    s2[(int64_t)r * lds_scr + c] = acc[i][j][v];
-            }
-    __threadfence_block();
-    __syncthreads();
-    // stage 3: Z = Linv^T V; A(r, t) = Linv[t][r], B(t, c) = V[t][c]
-    zero();
-    {
-        Operand<T, OP_KM> A{inv, ldi, 0, kb, vs && vi};
+        tile_mma<T, OP_MK, OP_KM, false, false, false, TM>(acc, A, B, 0, kb, lds);
+    } else if (STAGE == 2) {
+        Operand<T, OP_KM, TM> A{inv, ldi, r0, kb, vs && vi};
         Operand<T, OP_KM> B{s2, lds_scr, 0, kb, vs && vi};
-        tile_mma<T, OP_KM, OP_KM, false>(acc, A, B, 0, kb, lds);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                int r, c;
-                acc_pos<T>(i, j, v, r, c);
-                if (r < kb && c <= r)
-                    Wb[(int64_t)r * ldw + c] = (r == c) ? T(0.5) * acc[i][j][v] : acc[i][j][v];
-            }
-    if (!slot)
-        return;
-    mirror_to(sg, ldsg);
-    __threadfence_block();
-    __syncthreads();
-    // stage 4: slot = Sym(G) Lnext; A(r, t) = Sym(G)[r][t], B(t, c) = Lnext[t][c]
-    zero();
-    {
-        Operand<T, OP_MK> A{sg, ldsg, 0, kb, vec_ok(sg, ldsg)};
+        tile_mma<T, OP_KM, OP_KM, false, false, false, TM>(acc, A, B, 0, kb, lds);
+    } else {
+        Operand<T, OP_MK, TM> A{sg, ldsg, r0, kb, vec_ok(sg, ldsg)};
         Operand<T, OP_KM> B{Lnext, ldl, 0, nj, vs && vec_ok(Lnext, ldl)};
-        tile_mma<T, OP_MK, OP_KM, false>(acc, A, B, 0, kb, lds);
+        tile_mma<T, OP_MK, OP_KM, false, false, false, TM>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WaveTile<TM>::FRM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < WaveTile<TM>::FRN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int r, c;
-                acc_pos<T>(i, j, v, r, c);
-                if (r < kb && c < nj)
-                    slot[(int64_t)r * nj + c] = acc[i][j][v];
+                acc_pos<T, TM>(i, j, v, r, c);
+                r += r0;
+                const T x = acc[i][j][v];
+                if (STAGE == 0) {
+                    if (r < kb && c <= r) {
+                        s1[(int64_t)r * lds_scr + c] = x;
+                        s1[(int64_t)c * lds_scr + r] = x;
+                    }
+                } else if (STAGE == 1) {
+                    if (r < kb && c < kb)
+                        s2[(int64_t)r * lds_scr + c] = x;
+                } else if (STAGE == 2) {
+                    if (r < kb && c <= r) {
+                        Wb[(int64_t)r * ldw + c] = (r == c) ? T(0.5) * x : x;
+                        if (sg) {
+                            sg[(int64_t)r * ldsg + c] = x;
+                            sg[(int64_t)c * ldsg + r] = x;
+                        }
+                    }
+                } else {
+                    if (r < kb && c < nj)
+                        slot[(int64_t)r * nj + c] = x;
+                }
             }
+}
+
+template <typename T>
+static chol_status tile_adjoint_stages(hipStream_t st, int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw,
+                                       const T *inv, int64_t ldi, T *s1, T *s2, int64_t lds_scr, const T *Lnext,
+                                       int nj, T *slot, T *sg, int64_t ldsg)
+{
+    const dim3 grid((unsigned)((kb + 63) / 64));
+    hipLaunchKernelGGL((k_tile_adjoint_stage<T, 0>), grid, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1, s2,
+                       lds_scr, Lnext, nj, slot, sg, ldsg);
+    CHOL_LAUNCH_CHECK();
+    hipLaunchKernelGGL((k_tile_adjoint_stage<T, 1>), grid, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1, s2,
+                       lds_scr, Lnext, nj, slot, sg, ldsg);
+    CHOL_LAUNCH_CHECK();
+    hipLaunchKernelGGL((k_tile_adjoint_stage<T, 2>), grid, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1, s2,
+                       lds_scr, Lnext, nj, slot, slot ? sg : (T *)nullptr, ldsg);
+    CHOL_LAUNCH_CHECK();
+    if (slot) {
+        hipLaunchKernelGGL((k_tile_adjoint_stage<T, 3>), grid, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1,
+                           s2, lds_scr, Lnext, nj, slot, sg, ldsg);
+        CHOL_LAUNCH_CHECK();
+    }
+    return CHOL_OK;
 }
 
 // Reverse sweep over the tile columns with depth-1 look-ahead.  Tile column
@@ -746,10 +731,10 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
             prof::Scope ps(CHOL_K_ADJ_DIAG, sc, 2.0 * kb * kb * kb / 3 + (k >= 1 ? 2.0 * kb * kb * nb : 0.0));
             const T *Lnext = (k >= 1) ? L + k0 * ldl + j0 : nullptr;
             T *sg = dense ? dense + k * nb * nb : part_c;
-            hipLaunchKernelGGL((k_tile_adjoint<T>), dim3(1), dim3(256), 0, sc, kb, Lkk, ldl, Wkk, ldw, invk,
-                               (int64_t)nb, part_c, part_c + (int64_t)nb * nb, (int64_t)nb, Lnext, nb,
-                               k >= 1 ? slot : (T *)nullptr, sg, (int64_t)nb);
-            CHOL_LAUNCH_CHECK();
+            if ((s = tile_adjoint_stages<T>(sc, kb, Lkk, ldl, Wkk, ldw, invk, (int64_t)nb, part_c,
+                                            part_c + (int64_t)nb * nb, (int64_t)nb, Lnext, nb,
+                                            k >= 1 ? slot : (T *)nullptr, sg, (int64_t)nb)) != CHOL_OK)
+                return s;
         }
         // first term of tile column k-1: rows and columns from tile column k on,
         // the block Wb_kk left out

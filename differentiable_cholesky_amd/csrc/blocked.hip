@@ -608,6 +608,11 @@ static chol_status tile_adjoint_stages(hipStream_t st, int kb, const T *L, int64
     return CHOL_OK;
 }
 
+// Below this many trailing rows the sum of a tile column's second term and
+// its panel adjoint run on the chain stream (the symmetric product beside a
+// tile adjoint is then shorter than the chain, about 90 us at 3840 rows).
+constexpr int64_t ADJ_CHAIN_PANEL_ROWS = 3840;
+
 // Reverse sweep over the tile columns with depth-1 look-ahead.  Tile column
 // j's adjoint of the trailing update, Wb_panel(j) -= Sym(Wb22(j)) L_panel(j),
 // with Wb22(j) starting at tile column k = j+1, is split as
@@ -675,15 +680,30 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         const T *invk = inv + k * nb * nb;
         const T *Lp = L + r0 * ldl + k0;       // L_panel, m x kb
         T *Wp = Wb + r0 * ldw + k0;            // Wb_panel, m x kb
-        if (m > 0) {
-            // the second term of this tile column (from tile column k+1's tile
-            // adjoint on sc) lands in the first kn rows of Wb_panel
-            if (stream_join(sx, sc, e_tile) != hipSuccess)
+        // Where the trailing block is short, the chain of tile adjoints paces
+        // the sweep: the two launches that start tile column k (the sum of its
+        // second term and the panel adjoint) then run on sc as well, so the
+        // chain goes from one tile adjoint to the next with no wait on sx in
+        // between (what they need from sx, the symmetric product of tile
+        // column k, ran beside the previous tile adjoint and is long done).
+        // Further on, sx's symmetric products are the longer path and the two
+        // launches stay on sx, where they follow the product directly.
+        const bool on_chain = m <= ADJ_CHAIN_PANEL_ROWS;
+        hipStream_t sp = on_chain ? sc : sx;
+        // on sc, these launches need everything sx has done so far (the copy of
+        // adj_L, the tile inverses, the symmetric product of this tile column);
+        // on sx, the second term from tile column k+1's tile adjoint on sc
+        if (on_chain || m > 0) {
+            if (stream_join(on_chain ? sc : sx, on_chain ? sx : sc, e_tile) != hipSuccess)
                 return CHOL_ERR_HIP;
+        }
+        if (m > 0) {
+            // the second term of this tile column lands in the first kn rows
+            // of Wb_panel
             {
                 const int64_t tot = (int64_t)kn * kb;
-                prof::Scope ps(CHOL_K_REDUCE, sx, 3.0 * tot * sizeof(T));
-                hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, sx,
+                prof::Scope ps(CHOL_K_REDUCE, sp, 3.0 * tot * sizeof(T));
+                hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, sp,
                                    kn, kb, 1, (const T *)slot, Wp, ldw);
                 CHOL_LAUNCH_CHECK();
             }
@@ -695,16 +715,17 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 p.a = Wp; p.lda = ldw;
                 p.b = invk; p.ldb = nb;
                 p.c = Wp; p.ldc = ldw;
-                prof::Scope ps(CHOL_K_ADJ_PANEL, sx, (double)m * kb * kb);
-                if ((s = gemm<T, OP_MK, OP_KM, C_STORE, 64>(p, 1, sx)) != CHOL_OK)
+                prof::Scope ps(CHOL_K_ADJ_PANEL, sp, (double)m * kb * kb);
+                if ((s = gemm<T, OP_MK, OP_KM, C_STORE, 64>(p, 1, sp)) != CHOL_OK)
                     return s;
             }
         }
         // from here on sc: R2b (it only feeds the tile adjoint), then the tile
         // adjoint of tile column k, whose last stage is the second term of
-        // tile column k-1; meanwhile sx goes on with the symmetric product
+        // tile column k-1; meanwhile sx goes on with the symmetric product,
+        // which needs the panel adjoint
         const int64_t j0 = k0 - nb;                 // previous tile column (if k >= 1)
-        if (stream_join(sc, sx, e_wide) != hipSuccess)
+        if (stream_join(on_chain ? sx : sc, on_chain ? sc : sx, e_wide) != hipSuccess)
             return CHOL_ERR_HIP;
         if (m > 0) {
             // R2b: Wb_kk -= tril(X^T L_panel), split over the m rows into

@@ -505,15 +505,17 @@ __device__ __forceinline__ int vec_ok(const T *p, int64_t ld)
 //   stage 3: when `slot` is given, the one term of the previous tile column's
 //            trailing-update adjoint that needs G: slot = Sym(G) Lnext (kb x
 //            nj, row major), Lnext = L[this tile's rows, previous tile column]
-// Each stage is a launch of two blocks, one per 64-row half of its product,
-// so that the chain of tile adjoints, which sets the pace of the sweep while
-// the trailing blocks are small, runs on two CUs (a one-block kernel doing
-// all four stages took 90 us per tile, the four launches about 65 us).  The
-// stream orders the stages, so each reads what the one before wrote.  A
-// block writes the entries (r, c), c <= r, of its own rows r and their
-// mirrors (c, r) above the diagonal, which are never entries the other block
-// writes.  Only stage 0 reads masked triangles (of the caller's L and Wb);
-// the others read plain whole operands.
+// Each stage is a launch of one block per 64 x 64 quadrant of its product
+// (stages 0 and 2 skip the quadrant above the diagonal), so that the chain of
+// tile adjoints, which sets the pace of the sweep while the trailing blocks
+// are small, runs on three or four CUs (a one-block kernel doing all four
+// stages took 90 us per tile).  The stream orders the stages, so each reads
+// what the one before wrote.  In stages 0 and 2 a block writes the entries
+// (r, c), c <= r, of its quadrant and their mirrors (c, r): the mirrors of a
+// quadrant below the diagonal land in the skipped one, those of a diagonal
+// quadrant in its own upper part, so no two blocks write the same entry.
+// Only stage 0 reads masked triangles (of the caller's L and Wb); the others
+// read plain whole operands.
 template <typename T, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_tile_adjoint_stage(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv, int64_t ldi, T *s1,
@@ -521,46 +523,49 @@ k_tile_adjoint_stage(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const 
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
-    constexpr int TM = 64;
+    constexpr int TM = 64, TN = 64;
     __builtin_amdgcn_s_setprio(3);
     __shared__ T lds[LDS_ELEMS<T, TM>];
-    const int r0 = (int)blockIdx.x * TM;
-    if (r0 >= kb)
+    const int r0 = (int)blockIdx.x * TM, c0 = (int)blockIdx.y * TN;
+    // stages 0 and 2 keep only the lower part of their (symmetric) result
+    const bool lower_only = STAGE == 0 || STAGE == 2;
+    if (r0 >= kb || c0 >= (STAGE == 3 ? nj : kb) || (lower_only && r0 + TM <= c0))
         return;
-    AccTile<T, TM> acc;
+    AccTile<T, TM, TN> acc;
 #pragma unroll
-    for (int i = 0; i < WaveTile<TM>::FRM; ++i)
+    for (int i = 0; i < WaveTile<TM, TN>::FRM; ++i)
 #pragma unroll
-        for (int j = 0; j < WaveTile<TM>::FRN; ++j)
+        for (int j = 0; j < WaveTile<TM, TN>::FRN; ++j)
             acc[i][j] = acc_t{0, 0, 0, 0};
     const int vs = vec_ok(s1, lds_scr) && vec_ok(s2, lds_scr);
     const int vi = vec_ok(inv, ldi);
     if (STAGE == 0) {
         Operand<T, OP_KM_LOWER, TM> A{L, ldl, r0, kb, vec_ok(L, ldl)};
-        Operand<T, OP_KM_LOWER> B{Wb, ldw, 0, kb, vec_ok(Wb, ldw)};
-        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, false, false, TM>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_KM_LOWER, TN> B{Wb, ldw, c0, kb, vec_ok(Wb, ldw)};
+        tile_mma<T, OP_KM_LOWER, OP_KM_LOWER, false, false, false, TM, TN>(acc, A, B, 0, kb, lds);
     } else if (STAGE == 1) {
         Operand<T, OP_MK, TM> A{s1, lds_scr, r0, kb, vs};
-        Operand<T, OP_KM> B{inv, ldi, 0, kb, vs && vi};
-        tile_mma<T, OP_MK, OP_KM, false, false, false, TM>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_KM, TN> B{inv, ldi, c0, kb, vs && vi};
+        tile_mma<T, OP_MK, OP_KM, false, false, false, TM, TN>(acc, A, B, 0, kb, lds);
     } else if (STAGE == 2) {
         Operand<T, OP_KM, TM> A{inv, ldi, r0, kb, vs && vi};
-        Operand<T, OP_KM> B{s2, lds_scr, 0, kb, vs && vi};
-        tile_mma<T, OP_KM, OP_KM, false, false, false, TM>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_KM, TN> B{s2, lds_scr, c0, kb, vs && vi};
+        tile_mma<T, OP_KM, OP_KM, false, false, false, TM, TN>(acc, A, B, 0, kb, lds);
     } else {
         Operand<T, OP_MK, TM> A{sg, ldsg, r0, kb, vec_ok(sg, ldsg)};
-        Operand<T, OP_KM> B{Lnext, ldl, 0, nj, vs && vec_ok(Lnext, ldl)};
-        tile_mma<T, OP_MK, OP_KM, false, false, false, TM>(acc, A, B, 0, kb, lds);
+        Operand<T, OP_KM, TN> B{Lnext, ldl, c0, nj, vs && vec_ok(Lnext, ldl)};
+        tile_mma<T, OP_MK, OP_KM, false, false, false, TM, TN>(acc, A, B, 0, kb, lds);
     }
 #pragma unroll
-    for (int i = 0; i < WaveTile<TM>::FRM; ++i)
+    for (int i = 0; i < WaveTile<TM, TN>::FRM; ++i)
 #pragma unroll
-        for (int j = 0; j < WaveTile<TM>::FRN; ++j)
+        for (int j = 0; j < WaveTile<TM, TN>::FRN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int r, c;
-                acc_pos<T, TM>(i, j, v, r, c);
+                acc_pos<T, TM, TN>(i, j, v, r, c);
                 r += r0;
+                c += c0;
                 const T x = acc[i][j][v];
                 if (STAGE == 0) {
                     if (r < kb && c <= r) {
@@ -590,7 +595,8 @@ static chol_status tile_adjoint_stages(hipStream_t st, int kb, const T *L, int64
                                        const T *inv, int64_t ldi, T *s1, T *s2, int64_t lds_scr, const T *Lnext,
                                        int nj, T *slot, T *sg, int64_t ldsg)
 {
-    const dim3 grid((unsigned)((kb + 63) / 64));
+    const unsigned q = (unsigned)((kb + 63) / 64);
+    const dim3 grid(q, q), grid3(q, (unsigned)((nj + 63) / 64));
     hipLaunchKernelGGL((k_tile_adjoint_stage<T, 0>), grid, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1, s2,
                        lds_scr, Lnext, nj, slot, sg, ldsg);
     CHOL_LAUNCH_CHECK();
@@ -601,7 +607,7 @@ static chol_status tile_adjoint_stages(hipStream_t st, int kb, const T *L, int64
                        lds_scr, Lnext, nj, slot, slot ? sg : (T *)nullptr, ldsg);
     CHOL_LAUNCH_CHECK();
     if (slot) {
-        hipLaunchKernelGGL((k_tile_adjoint_stage<T, 3>), grid, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1,
+        hipLaunchKernelGGL((k_tile_adjoint_stage<T, 3>), grid3, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1,
                            s2, lds_scr, Lnext, nj, slot, sg, ldsg);
         CHOL_LAUNCH_CHECK();
     }

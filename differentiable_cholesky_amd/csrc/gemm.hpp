@@ -95,13 +95,15 @@ template <typename T, int TE = 128> struct Stage {
     static constexpr int GEN = TILE / NT;              // elements per thread on the per-element path
     static constexpr int DPW = TE / 32;                // direct-load instructions per wave per chunk
 };
-template <int TM> struct WaveTile {
+template <int TM, int TN = 128> struct WaveTile {
     static constexpr int WM = TM / 2;                  // wave tile rows
     static constexpr int FRM = TM / 32;                // MFMA tiles along the wave tile's rows
-    static constexpr int WN = 64, FRN = 4;
+    static constexpr int WN = TN / 2;                  // wave tile columns
+    static constexpr int FRN = TN / 32;
 };
 // a wave's accumulators: FRM x FRN MFMA result tiles
-template <typename T, int TM> using AccTile = typename Acc<T>::type[WaveTile<TM>::FRM][WaveTile<TM>::FRN];
+template <typename T, int TM, int TN = 128>
+using AccTile = typename Acc<T>::type[WaveTile<TM, TN>::FRM][WaveTile<TM, TN>::FRN];
 
 // LDS a product needs: two buffers of A's (TM x BK) and B's (128 x BK) chunks
 // (64 KB for 128-row tiles, 48 KB for 64-row tiles)
@@ -267,12 +269,13 @@ __device__ __forceinline__ int xcd_tile(int b, int nt)
 }
 
 // acc += (NEG ? -A : A) B over one chunk at k0 staged at SA (A) and SB (B)
-template <typename T, int AOP, int BOP, bool NEG, int TM>
-__device__ __forceinline__ void chunk_mma(AccTile<T, TM> &acc, const Operand<T, AOP, TM> &A,
-                                          const Operand<T, BOP, 128> &B, int k0, const T *SA, const T *SB)
+template <typename T, int AOP, int BOP, bool NEG, int TM, int TN = 128>
+__device__ __forceinline__ void chunk_mma(AccTile<T, TM, TN> &acc, const Operand<T, AOP, TM> &A,
+                                          const Operand<T, BOP, TN> &B, int k0, const T *SA, const T *SB)
 {
     constexpr int BK = Stage<T, TM>::BK;
-    constexpr int FRM = WaveTile<TM>::FRM, FRN = WaveTile<TM>::FRN, WM = WaveTile<TM>::WM, WN = WaveTile<TM>::WN;
+    constexpr int FRM = WaveTile<TM, TN>::FRM, FRN = WaveTile<TM, TN>::FRN;
+    constexpr int WM = WaveTile<TM, TN>::WM, WN = WaveTile<TM, TN>::WN;
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
     const int wm = wave / 2, wn = wave % 2;
 #pragma unroll
@@ -312,12 +315,13 @@ __device__ __forceinline__ void chunk_mma(AccTile<T, TM> &acc, const Operand<T, 
 // chunk leaves that one load in flight.  (A second LDS buffer set for a
 // two-chunk lookahead would take the block to 80 KB of LDS, and two blocks no
 // longer fit a CU.)
-template <typename T, int AOP, int BOP, bool NEG, bool BOOST = false, bool TOUCH = false, int TM = 128>
-__device__ __forceinline__ void tile_mma(gemm_detail::AccTile<T, TM> &acc, const gemm_detail::Operand<T, AOP, TM> &A,
-                                         const gemm_detail::Operand<T, BOP, 128> &B, int kbeg, int kend, T *lds)
+template <typename T, int AOP, int BOP, bool NEG, bool BOOST = false, bool TOUCH = false, int TM = 128, int TN = 128>
+__device__ __forceinline__ void tile_mma(gemm_detail::AccTile<T, TM, TN> &acc,
+                                         const gemm_detail::Operand<T, AOP, TM> &A,
+                                         const gemm_detail::Operand<T, BOP, TN> &B, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
-    constexpr int BK = Stage<T, TM>::BK, TA = Stage<T, TM>::TILE, SZ = TA + Stage<T, 128>::TILE;
+    constexpr int BK = Stage<T, TM>::BK, TA = Stage<T, TM>::TILE, SZ = TA + Stage<T, TN>::TILE;
     if (kend <= kbeg)
         return;
     const int nc = (kend - kbeg + BK - 1) / BK;
@@ -342,7 +346,7 @@ __device__ __forceinline__ void tile_mma(gemm_detail::AccTile<T, TM> &acc, const
         T tnext = T(0);
         if (touch)
             tnext = A.touch(k0 + 2 * BK);
-        chunk_mma<T, AOP, BOP, NEG, TM>(acc, A, B, k0, S, S + TA);
+        chunk_mma<T, AOP, BOP, NEG, TM, TN>(acc, A, B, k0, S, S + TA);
         if (BOOST)
             __builtin_amdgcn_s_setprio(0);
         if (touch)
@@ -388,12 +392,12 @@ __device__ __forceinline__ void tile_mma_serial(gemm_detail::AccTile<T, TM> &acc
 }
 
 // Position of accumulator element (i, j, v) of this thread inside the TM x 128 tile.
-template <typename T, int TM = 128>
+template <typename T, int TM = 128, int TN = 128>
 __device__ __forceinline__ void acc_pos(int i, int j, int v, int &row, int &col)
 {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    row = (wave / 2) * gemm_detail::WaveTile<TM>::WM + i * 16 + Acc<T>::row(lane, v);
-    col = (wave % 2) * gemm_detail::WaveTile<TM>::WN + j * 16 + lane % 16;
+    row = (wave / 2) * gemm_detail::WaveTile<TM, TN>::WM + i * 16 + Acc<T>::row(lane, v);
+    col = (wave % 2) * gemm_detail::WaveTile<TM, TN>::WN + j * 16 + lane % 16;
 }
 
 // One TM x 128 output tile (I, J) over the contraction range [kbeg, kend).

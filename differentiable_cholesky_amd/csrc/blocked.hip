@@ -303,8 +303,12 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
         // at once, three per CU: nothing runs beside these launches)
         if (!tri) {
             const int64_t tiles128 = ((M + 127) / 128) * ((w + 127) / 128);
-            if (Kd <= 128 || tiles128 <= 384)
+            if (Kd <= 128 || tiles128 <= 384) {
+                // fewer 64 x 128 tiles than CUs: 64 x 64 tiles, twice as many
+                if (2 * tiles128 < 256)
+                    return gemm<T, OP_MK, OP_MK, C_SUB_LOWER, 64, 64>(p, 1, sx);
                 return gemm<T, OP_MK, OP_MK, C_SUB_LOWER, 64>(p, 1, sx);
+            }
             return gemm<T, OP_MK, OP_MK, C_SUB_LOWER>(p, 1, sx);
         }
         // a far-triangle part of at most half a round of the persistent grid

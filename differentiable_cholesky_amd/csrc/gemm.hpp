@@ -401,13 +401,13 @@ __device__ __forceinline__ void acc_pos(int i, int j, int v, int &row, int &col)
 }
 
 // One TM x 128 output tile (I, J) over the contraction range [kbeg, kend).
-template <typename T, int AOP, int BOP, int CM, bool BOOST = false, int TM = 128>
+template <typename T, int AOP, int BOP, int CM, bool BOOST = false, int TM = 128, int TN = 128>
 __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, int split, int kbeg, int kend, T *lds)
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
-    constexpr int FRM = WaveTile<TM>::FRM, FRN = WaveTile<TM>::FRN, TN = 128;
-    static_assert(TM == BM || (AOP != OP_SYM && AOP != OP_SYM_DG), "the symmetric operand takes 128 tiles");
+    constexpr int FRM = WaveTile<TM, TN>::FRM, FRN = WaveTile<TM, TN>::FRN;
+    static_assert((TM == BM && TN == BM) || (AOP != OP_SYM && AOP != OP_SYM_DG), "the symmetric operand takes 128 tiles");
     const int r0 = I * TM, c0 = J * TN;
 
     // C -= AB runs as acc = C, acc += (-A) B: the accumulators start from C,
@@ -432,7 +432,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     int row, col;
-                    acc_pos<T, TM>(i, j, v, row, col);
+                    acc_pos<T, TM, TN>(i, j, v, row, col);
                     acc[i][j][v] = cin[(int64_t)(row + r0) * ldcin + col + c0];
                 }
     } else {
@@ -445,7 +445,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
                     T x = T(0);
                     if (FROM_C) {
                         int row, col;
-                        acc_pos<T, TM>(i, j, v, row, col);
+                        acc_pos<T, TM, TN>(i, j, v, row, col);
                         row += r0;
                         col += c0;
                         if (row < p.M && col < p.N)
@@ -486,7 +486,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
             tile_mma<T, OP_KM, BOP, FROM_C, BOOST, true>(acc, Aa, B, a0, kend, lds);
         }
     } else {
-        tile_mma<T, AOP, BOP, FROM_C, BOOST, false, TM>(acc, A, B, kbeg, kend, lds);
+        tile_mma<T, AOP, BOP, FROM_C, BOOST, false, TM, TN>(acc, A, B, kbeg, kend, lds);
     }
 
     if (interior && (CM != C_SUB_LOWER || r0 >= c0 + TN - 1)) {
@@ -497,7 +497,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     int row, col;
-                    acc_pos<T, TM>(i, j, v, row, col);
+                    acc_pos<T, TM, TN>(i, j, v, row, col);
                     row += r0;
                     col += c0;
                     if (CM == C_PARTIAL)
@@ -514,7 +514,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<T> &p, int I, int J, in
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int row, col;
-                acc_pos<T, TM>(i, j, v, row, col);
+                acc_pos<T, TM, TN>(i, j, v, row, col);
                 row += r0;
                 col += c0;
                 if (row >= p.M || col >= p.N)
@@ -556,7 +556,7 @@ enum { SCHED_BOTH = 0, SCHED_DYN = 1, SCHED_STATIC = 2 };
 // (half the accumulators, 48 KB of LDS).
 template <int TM> constexpr int gemm_waves() { return TM == 128 ? 2 : 3; }
 
-template <typename T, int AOP, int BOP, int CM, int SCHED, int TM>
+template <typename T, int AOP, int BOP, int CM, int SCHED, int TM, int TN = 128>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gemm_waves<TM>(), gemm_waves<TM>())))
 k_gemm(GemmArgs<T> p)
 {
@@ -567,7 +567,7 @@ k_gemm(GemmArgs<T> p)
     // a triangular grid counts 128 x 128 tiles; with 64-row tiles each of
     // them is two items (its upper and lower half), dynamic schedule only
     constexpr int HALVES = TM == 64 ? 2 : 1;
-    const int TI = p.tri ? (p.M + 127) / 128 : (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
+    const int TI = p.tri ? (p.M + 127) / 128 : (p.M + TM - 1) / TM, TJ = (p.N + TN - 1) / TN;
     const int nt = (p.tn ? p.tn : (p.tri ? TI * (TI + 1) / 2 : TI * TJ)) * (p.tri ? HALVES : 1);
 
     if (SCHED == SCHED_STATIC || (SCHED == SCHED_BOTH && !p.sched)) {
@@ -579,7 +579,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = blockIdx.y * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM, true, TM>(p, I, J, blockIdx.y, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, true, TM, TN>(p, I, J, blockIdx.y, kbeg, kend, lds);
         return;
     }
 
@@ -610,7 +610,7 @@ k_gemm(GemmArgs<T> p)
             kbeg = split * p.kchunk;
             kend = min(p.K, kbeg + p.kchunk);
         }
-        gemm_tile<T, AOP, BOP, CM, true, TM>(p, I, J, split, kbeg, kend, lds);
+        gemm_tile<T, AOP, BOP, CM, true, TM, TN>(p, I, J, split, kbeg, kend, lds);
     }
     // the last block to finish returns the counters to zero for the next launch
     if (threadIdx.x == 0) {
@@ -636,7 +636,7 @@ static inline bool aligned16(const T *p, int64_t ld)
 // C op= A B on the stream; TM: output tile rows (128, or 64 for short
 // products whose 128 x 128 tiles would be too few, or too long each, to
 // spread over the device; tiles are always 128 columns wide)
-template <typename T, int AOP, int BOP, int CM, int TM = 128>
+template <typename T, int AOP, int BOP, int CM, int TM = 128, int TN = 128>
 static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
 {
     using namespace gemm_detail;
@@ -644,10 +644,12 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         return CHOL_OK;
     if (TM != BM && p.tri && !p.sched)
         return CHOL_ERR_INVALID_VALUE;           // halves of triangular tiles: dynamic schedule only
+    if (TN != BM && (p.tri || p.sched))
+        return CHOL_ERR_INVALID_VALUE;           // 64-column tiles: static rectangular grids only
     p.vec = (aligned16(p.a, p.lda) ? 1 : 0) | (aligned16(p.b, p.ldb) ? 2 : 0);
     p.splits = splits;
     if constexpr (AOP == OP_SYM) {
-        static_assert(TM == BM, "the symmetric operand takes 128 tiles");
+        static_assert(TM == BM && TN == BM, "the symmetric operand takes 128 tiles");
         // the excluded block is at most one tile; with a dense copy of every
         // diagonal block the product meets, the kernel reads them from it
         if (p.excl < 0 || p.excl > BM)
@@ -655,7 +657,7 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         if (p.dg && p.vec == 3 && p.M % BM == 0 && (p.excl == 0 || p.excl == BM) && ((uintptr_t)p.dg % 16) == 0)
             return gemm<T, OP_SYM_DG, BOP, CM, TM>(p, splits, st);
     }
-    const int TI = p.tri ? (p.M + BM - 1) / BM : (p.M + TM - 1) / TM, TJ = (p.N + 127) / 128;
+    const int TI = p.tri ? (p.M + BM - 1) / BM : (p.M + TM - 1) / TM, TJ = (p.N + TN - 1) / TN;
     const int nt_all = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
     if (p.t0 < 0 || p.tn < 0 || p.t0 + (p.tn ? p.tn : nt_all) > nt_all)
         return CHOL_ERR_INVALID_VALUE;
@@ -668,11 +670,11 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1) * (TM != BM && p.tri ? 2 : 1);
         const unsigned dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
         if (CM == C_SUB_LOWER)
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN, TM>), dim3(dgrid), dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN, TM, TN>), dim3(dgrid), dim3(NT), 0, st, p);
         else
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM>), dim3(dgrid), dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM, TN>), dim3(dgrid), dim3(NT), 0, st, p);
     } else {
-        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM>), sgrid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM, TN>), sgrid, dim3(NT), 0, st, p);
     }
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;

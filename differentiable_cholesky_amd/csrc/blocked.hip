@@ -235,6 +235,26 @@ k_splitk_reduce(int M, int N, int splits, const T *part, T *c, int64_t ldc)
     c[(int64_t)r * ldc + col] -= s;
 }
 
+// The sums of a piece-scheduled product (GemmArgs::piece): tile t (128 x 128,
+// TJ per row of tiles) holds one partial per piece that touched it, slots
+// 0 .. count-1 in contraction order, summed in that order into c (c -= sum).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_splitk_reduce_pieces(int M, int N, int TJ, int64_t nku, int64_t piece, const T *part, T *c, int64_t ldc)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t tot = (int64_t)M * N;
+    if (idx >= tot)
+        return;
+    const int r = (int)(idx / N), col = (int)(idx % N);
+    const int64_t t = (int64_t)(r / 128) * TJ + col / 128;
+    const int cnt = (int)(((t + 1) * nku - 1) / piece - (t * nku) / piece + 1);
+    T s = T(0);
+    for (int q = 0; q < cnt; ++q)
+        s += part[(int64_t)q * tot + idx];
+    c[(int64_t)r * ldc + col] -= s;
+}
+
 // contraction length per split: a whole number of fp32 chunks (32), which is
 // also a whole number of fp64 chunks (16)
 static inline int split_chunk(int64_t K, int splits)
@@ -468,7 +488,28 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
             kchunk = c;
         }
     }
+    // Pieces instead: the tiles' contractions laid end to end and cut into
+    // equal pieces, so that r rounds of the grid hold exactly the work (equal
+    // splits leave part of the last round idle); a tile then sums a partial
+    // per piece that touched it (at most ceil(units / piece) + 1)
+    const int64_t nku = ((int64_t)K + SK_UNIT - 1) / SK_UNIT, W = tiles * nku;
+    const int64_t min_units = std::max<int64_t>(1, min_chunk / SK_UNIT);
+    int64_t piece = 0;
+    for (int r = 1; r <= 64; ++r) {
+        const int64_t P = (W + (int64_t)cap * r - 1) / ((int64_t)cap * r);
+        if (P < min_units)
+            break;
+        if ((nku + P - 1) / P + 1 > max_splits)
+            continue;
+        const int64_t items = (W + P - 1) / P;
+        const double t = (double)((items + cap - 1) / cap) * P * SK_UNIT + per_split * ((double)items / tiles + 1);
+        if (t < best_t) {
+            best_t = t;
+            piece = P;
+        }
+    }
     p.kchunk = kchunk;
+    p.piece = (int)piece;
     const int used = (K + p.kchunk - 1) / p.kchunk;
     p.part = part;
     p.sched = sched;
@@ -482,9 +523,16 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
             return s;
     }
     const int64_t tot = (int64_t)M * N;
-    prof::Scope ps(CHOL_K_REDUCE, st, (double)tot * (used + 2) * sizeof(T));
-    hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N, used,
-                       (const T *)part, C, ldc);
+    if (piece > 0) {
+        const double slots = (double)((W + piece - 1) / piece) / tiles + 1;
+        prof::Scope ps(CHOL_K_REDUCE, st, (double)tot * (slots + 2) * sizeof(T));
+        hipLaunchKernelGGL((k_splitk_reduce_pieces<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N,
+                           (N + 127) / 128, nku, piece, (const T *)part, C, ldc);
+    } else {
+        prof::Scope ps(CHOL_K_REDUCE, st, (double)tot * (used + 2) * sizeof(T));
+        hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N,
+                           used, (const T *)part, C, ldc);
+    }
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;
 }

@@ -46,6 +46,10 @@
 namespace chol {
 
 enum { OP_MK = 0, OP_KM = 1, OP_SYM = 2, OP_KM_LOWER = 3, OP_SYM_DG = 4 };
+// contraction unit of the piece schedule: a whole number of fp32 (32) and
+// fp64 (16) chunks
+constexpr int SK_UNIT = 32;
+
 enum { C_SUB = 0,        // C -= AB
        C_SUB_LOWER = 1,  // C -= AB where row >= col
        C_STORE = 2,      // C  = AB
@@ -71,6 +75,13 @@ template <typename T> struct GemmArgs {
     int *sched;          // non-null: blocks take (split, tile) items from this
                          // device counter pair (item, finished blocks), which
                          // must be zero at launch and is zero again afterwards
+    int piece;           // C_PARTIAL with `sched`, optional: the tiles' contractions
+                         // laid end to end in units of SK_UNIT elements and cut
+                         // into pieces of `piece` units, one item each (a piece
+                         // may end one tile's contraction and start the next
+                         // one's); partial slot of a piece on a tile = the
+                         // piece's index minus that of the first piece on the
+                         // tile.  0: `splits` equal splits per tile
     const T *dg;         // OP_SYM A operand, optional: the symmetric 128 x 128
                          // diagonal blocks written whole (block I at dg + I*128*128,
                          // row-major), read by direct loads instead of
@@ -587,7 +598,9 @@ k_gemm(GemmArgs<T> p)
     // block that shares its CU with other work simply takes fewer items
     __shared__ int s_item;
     const int splits = (CM == C_PARTIAL) ? p.splits : 1;
-    const int items = nt * splits;
+    const int64_t nku = (p.K + SK_UNIT - 1) / SK_UNIT;            // units per tile (piece schedule)
+    const bool pieces = CM == C_PARTIAL && p.piece > 0;
+    const int items = pieces ? (int)(((int64_t)nt * nku + p.piece - 1) / p.piece) : nt * splits;
     for (;;) {
         if (threadIdx.x == 0)
             s_item = atomicAdd(p.sched, 1);
@@ -596,6 +609,22 @@ k_gemm(GemmArgs<T> p)
         __syncthreads();                  // every thread holds the item before s_item is rewritten
         if (it >= items)
             break;
+        if (pieces) {
+            // piece it: units [lo, hi) of the contractions laid end to end,
+            // over one tile or the end of one and the start of the next
+            const int64_t total = (int64_t)nt * nku, lo = (int64_t)it * p.piece;
+            const int64_t hi = lo + p.piece < total ? lo + p.piece : total;
+            for (int64_t t = lo / nku; t * nku < hi; ++t) {
+                const int64_t t0u = t * nku, t1u = t0u + nku;
+                const int64_t a = (lo > t0u ? lo : t0u) - t0u, b = (hi < t1u ? hi : t1u) - t0u;
+                const int slot = it - (int)(t0u / p.piece);
+                const int64_t kend = b * SK_UNIT < p.K ? b * SK_UNIT : p.K;
+                int I, J;
+                tile_of(p.t0 + (int)t, p.tri, TJ, I, J);
+                gemm_tile<T, AOP, BOP, CM, true, TM, TN>(p, I, J, slot, (int)(a * SK_UNIT), (int)kend, lds);
+            }
+            continue;
+        }
         const int split = it / nt;
         int I, J;
         if (HALVES == 2 && p.tri) {
@@ -646,6 +675,8 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         return CHOL_ERR_INVALID_VALUE;           // halves of triangular tiles: dynamic schedule only
     if (TN != BM && (p.tri || p.sched))
         return CHOL_ERR_INVALID_VALUE;           // 64-column tiles: static rectangular grids only
+    if (p.piece < 0 || (p.piece > 0 && (CM != C_PARTIAL || !p.sched)))
+        return CHOL_ERR_INVALID_VALUE;           // pieces: persistent split-contraction products only
     p.vec = (aligned16(p.a, p.lda) ? 1 : 0) | (aligned16(p.b, p.ldb) ? 2 : 0);
     p.splits = splits;
     if constexpr (AOP == OP_SYM) {
@@ -667,7 +698,10 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
     const dim3 sgrid((unsigned)nt, (unsigned)(CM == C_PARTIAL ? splits : 1));
     if (p.sched) {
         // persistent blocks, all resident at once (two per CU the stream may use)
-        const int64_t items = (int64_t)nt * (CM == C_PARTIAL ? splits : 1) * (TM != BM && p.tri ? 2 : 1);
+        const int64_t nku = (p.K + SK_UNIT - 1) / SK_UNIT;
+        const int64_t items = (CM == C_PARTIAL && p.piece > 0)
+                                  ? ((int64_t)nt * nku + p.piece - 1) / p.piece
+                                  : (int64_t)nt * (CM == C_PARTIAL ? splits : 1) * (TM != BM && p.tri ? 2 : 1);
         const unsigned dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
         if (CM == C_SUB_LOWER)
             hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN, TM, TN>), dim3(dgrid), dim3(NT), 0, st, p);

@@ -797,7 +797,12 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
             const int splits = (int)((m + 127) / 128);
             {
                 prof::Scope ps(CHOL_K_ADJ_DIAG_UPDATE, sc, 2.0 * m * kb * kb);
-                if ((s = gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sc)) != CHOL_OK)
+                // on the critical chain (short trailing block) as 64 x 64
+                // tiles, four times the blocks; beside the large symmetric
+                // products the 128 x 128 tiles, which leave them the CUs
+                s = on_chain ? gemm<T, OP_KM, OP_KM, C_PARTIAL, 64, 64>(p, splits, sc)
+                             : gemm<T, OP_KM, OP_KM, C_PARTIAL>(p, splits, sc);
+                if (s != CHOL_OK)
                     return s;
             }
             const int64_t tot = (int64_t)kb * kb;

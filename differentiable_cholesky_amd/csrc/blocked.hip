@@ -670,6 +670,12 @@ static chol_status tile_adjoint_stages(hipStream_t st, int kb, const T *L, int64
 // its panel adjoint run on the chain stream (the symmetric product beside a
 // tile adjoint is then shorter than the chain, about 90 us at 3840 rows).
 constexpr int64_t ADJ_CHAIN_PANEL_ROWS = 3840;
+// adj_L is copied into the running gradient as the last ADJ_COPY_FIRST tile
+// columns up front and the rest in bands of ADJ_COPY_BAND tile columns
+constexpr int64_t ADJ_COPY_FIRST = 8, ADJ_COPY_BAND = 4;
+// tile columns of the gradient added into adj_A per iteration, beyond its own,
+// once the chain no longer sets the pace
+constexpr int64_t ADJ_ADD_CATCHUP = 2;
 
 // Reverse sweep over the tile columns with depth-1 look-ahead.  Tile column
 // j's adjoint of the trailing update, Wb_panel(j) -= Sym(Wb22(j)) L_panel(j),
@@ -717,8 +723,16 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
     T *dense = nb == 128 ? (T *)w : nullptr;
     T *slot = part_b + panel_tiles(n) * nb * nb;   // Sym(G(k)) L[tile k, tile k-1]
 
-    if ((const T *)Wb != adjL) {
-        if ((s = tri_op<T, TRI_COPY_LOWER>(n, adjL, ldal, Wb, ldw, sx)) != CHOL_OK)
+    // adj_L into the running gradient: the last ADJ_COPY_FIRST tile columns
+    // (all that the first iterations touch) now, the others in bands of
+    // ADJ_COPY_BAND tile columns on sx during the first iterations, where sx
+    // waits for the chain; each band ahead of the iteration that first uses it
+    const bool copy = (const T *)Wb != adjL;
+    const int64_t kc = copy ? std::max<int64_t>(0, K - ADJ_COPY_FIRST) : 0;
+    if (copy) {
+        const int64_t c0 = kc * nb;
+        if ((s = tri_op<T, TRI_COPY_LOWER>(n - c0, adjL + c0 * ldal + c0, ldal, Wb + c0 * ldw + c0, ldw, sx)) !=
+            CHOL_OK)
             return s;
     }
     {
@@ -727,6 +741,14 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                            const_cast<T *>(L), ldl, 1, inv, (int64_t)nb * nb, (int64_t)nb);
         CHOL_LAUNCH_CHECK();
     }
+
+    // tile columns [add_lo, add_hi) are final and not yet added into adj_A
+    int64_t add_lo = K, add_hi = K;
+    auto add_columns = [&](int64_t lo, int64_t hi) {
+        const int64_t c0 = lo * nb;
+        return tri_op<T, TRI_ADD_LOWER>(n - c0, Wb + c0 * ldw + c0, ldw, adjA + c0 * ldaa + c0, ldaa, sc,
+                                        (hi - lo) * nb);
+    };
 
     for (int64_t k = K - 1; k >= 0; --k) {
         const int64_t k0 = k * nb;
@@ -754,6 +776,15 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         if (on_chain || m > 0) {
             if (stream_join(on_chain ? sc : sx, on_chain ? sx : sc, e_tile) != hipSuccess)
                 return CHOL_ERR_HIP;
+        }
+        // the next band of adj_L (tile columns [lo, hi)), first used at
+        // iteration hi - 1 < k
+        if (const int64_t q = K - 1 - k; copy && q * ADJ_COPY_BAND < kc) {
+            const int64_t hi = kc - q * ADJ_COPY_BAND, lo = std::max<int64_t>(0, hi - ADJ_COPY_BAND);
+            const int64_t c0 = lo * nb;
+            if ((s = tri_op<T, TRI_COPY_LOWER>(n - c0, adjL + c0 * ldal + c0, ldal, Wb + c0 * ldw + c0, ldw, sx,
+                                               (hi - lo) * nb)) != CHOL_OK)
+                return s;
         }
         if (m > 0) {
             // the second term of this tile column lands in the first kn rows
@@ -820,6 +851,23 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                                             k >= 1 ? slot : (T *)nullptr, sg, (int64_t)nb)) != CHOL_OK)
                 return s;
         }
+        // tile column k of the gradient is final (its panel since the panel
+        // adjoint, its diagonal tile since the tile adjoint): lower(adj_A) +=
+        // it, on sc.  Where sc carries the chain the columns wait; once the
+        // products are large, sc waits for sx and has the time: there it adds
+        // its own tile column and up to ADJ_ADD_CATCHUP waiting ones.
+        if (need_wb) {
+            if (on_chain) {
+                add_lo = k;
+            } else {
+                if ((s = add_columns(k, k + 1)) != CHOL_OK)
+                    return s;
+                const int64_t lo = std::max(add_lo, add_hi - ADJ_ADD_CATCHUP);
+                if (lo < add_hi && (s = add_columns(lo, add_hi)) != CHOL_OK)
+                    return s;
+                add_hi = lo;
+            }
+        }
         // first term of tile column k-1: rows and columns from tile column k on,
         // the block Wb_kk left out
         if (k >= 1 && m > 0) {
@@ -831,10 +879,10 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 return s;
         }
     }
+    if (need_wb && add_lo < add_hi && (s = add_columns(add_lo, add_hi)) != CHOL_OK)
+        return s;
     if (stream_join(sx, sc, e_tile) != hipSuccess)
         return CHOL_ERR_HIP;
-    if (need_wb)
-        return tri_op<T, TRI_ADD_LOWER>(n, Wb, ldw, adjA, ldaa, sx);
     return CHOL_OK;
 }
 

@@ -517,8 +517,8 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
     p.excl = excl;
     p.dg = dg;
     {
-        prof::Scope ps(CHOL_K_ADJ_TRAILING, st, flops);
-        chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st);
+        prof::LaunchEvents pe(CHOL_K_ADJ_TRAILING, flops);
+        chol_status s = gemm<T, OP_SYM, OP_KM, C_PARTIAL>(p, used, st, pe.a, pe.b);
         if (s != CHOL_OK)
             return s;
     }

@@ -43,6 +43,8 @@
 
 #include "common.hpp"
 
+#include <hip/hip_ext.h>
+
 namespace chol {
 
 enum { OP_MK = 0, OP_KM = 1, OP_SYM = 2, OP_KM_LOWER = 3, OP_SYM_DG = 4 };
@@ -662,11 +664,25 @@ static inline bool aligned16(const T *p, int64_t ld)
     return ((uintptr_t)p % 16 == 0) && (ld % PER == 0) && ld < ((int64_t)1 << 24);
 }
 
+namespace gemm_detail {
+// a launch of the product kernel; with an event pair (a timed launch) the
+// kernel's own start and end are stamped into it
+template <typename T>
+static void launch(void (*kern)(GemmArgs<T>), dim3 grid, hipStream_t st, const GemmArgs<T> &p, hipEvent_t ea,
+                   hipEvent_t eb)
+{
+    if (ea && eb)
+        hipExtLaunchKernelGGL(kern, grid, dim3(NT), 0, st, ea, eb, 0, p);
+    else
+        hipLaunchKernelGGL(kern, grid, dim3(NT), 0, st, p);
+}
+} // namespace gemm_detail
+
 // C op= A B on the stream; TM: output tile rows (128, or 64 for short
 // products whose 128 x 128 tiles would be too few, or too long each, to
 // spread over the device; tiles are always 128 columns wide)
 template <typename T, int AOP, int BOP, int CM, int TM = 128, int TN = 128>
-static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
+static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st, hipEvent_t ea = nullptr, hipEvent_t eb = nullptr)
 {
     using namespace gemm_detail;
     if (p.M <= 0 || p.N <= 0)
@@ -686,7 +702,7 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
         if (p.excl < 0 || p.excl > BM)
             return CHOL_ERR_INVALID_VALUE;
         if (p.dg && p.vec == 3 && p.M % BM == 0 && (p.excl == 0 || p.excl == BM) && ((uintptr_t)p.dg % 16) == 0)
-            return gemm<T, OP_SYM_DG, BOP, CM, TM>(p, splits, st);
+            return gemm<T, OP_SYM_DG, BOP, CM, TM>(p, splits, st, ea, eb);
     }
     const int TI = p.tri ? (p.M + BM - 1) / BM : (p.M + TM - 1) / TM, TJ = (p.N + TN - 1) / TN;
     const int nt_all = p.tri ? TI * (TI + 1) / 2 : TI * TJ;
@@ -704,11 +720,11 @@ static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st)
                                   : (int64_t)nt * (CM == C_PARTIAL ? splits : 1) * (TM != BM && p.tri ? 2 : 1);
         const unsigned dgrid = (unsigned)std::min<int64_t>(items, p.cap > 0 ? p.cap : 2 * 240);
         if (CM == C_SUB_LOWER)
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_DYN, TM, TN>), dim3(dgrid), dim3(NT), 0, st, p);
+            gemm_detail::launch(k_gemm<T, AOP, BOP, CM, SCHED_DYN, TM, TN>, dim3(dgrid), st, p, ea, eb);
         else
-            hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM, TN>), dim3(dgrid), dim3(NT), 0, st, p);
+            gemm_detail::launch(k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM, TN>, dim3(dgrid), st, p, ea, eb);
     } else {
-        hipLaunchKernelGGL((k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM, TN>), sgrid, dim3(NT), 0, st, p);
+        gemm_detail::launch(k_gemm<T, AOP, BOP, CM, SCHED_BOTH, TM, TN>, sgrid, st, p, ea, eb);
     }
     CHOL_LAUNCH_CHECK();
     return CHOL_OK;

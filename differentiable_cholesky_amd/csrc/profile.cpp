@@ -62,6 +62,30 @@ Scope::~Scope()
     g_recs.push_back(Rec{id, a, b, work});
 }
 
+LaunchEvents::LaunchEvents(int id_, double work_) : id(id_), work(work_)
+{
+    if (id < 0 || id >= 32 || !((g_mask.load(std::memory_order_relaxed) >> id) & 1u))
+        return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    a = take();
+    b = take();
+    if (!a || !b) {
+        if (a)
+            g_pool.push_back(a);
+        if (b)
+            g_pool.push_back(b);
+        a = b = nullptr;
+    }
+}
+
+LaunchEvents::~LaunchEvents()
+{
+    if (!a || !b)
+        return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_recs.push_back(Rec{id, a, b, work});
+}
+
 } // namespace prof
 } // namespace chol
 

@@ -22,5 +22,17 @@ struct Scope {
     ~Scope();
 };
 
+// The same timing for one kernel launch that carries the events itself
+// (hipExtLaunchKernel): the pair, when the family is being timed, is handed to
+// the launch, which stamps the kernel's own start and end into it, so that no
+// marker enters the stream between this kernel and its neighbours.
+struct LaunchEvents {
+    int id;
+    double work;
+    hipEvent_t a = nullptr, b = nullptr;
+    LaunchEvents(int id_, double work_);
+    ~LaunchEvents();
+};
+
 } // namespace prof
 } // namespace chol

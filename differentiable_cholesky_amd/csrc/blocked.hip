@@ -557,17 +557,19 @@ __device__ __forceinline__ int vec_ok(const T *p, int64_t ld)
 //   stage 3: when `slot` is given, the one term of the previous tile column's
 //            trailing-update adjoint that needs G: slot = Sym(G) Lnext (kb x
 //            nj, row major), Lnext = L[this tile's rows, previous tile column]
-// Each stage is a launch of one block per 64 x 64 quadrant of its product
-// (stages 0 and 2 skip the quadrant above the diagonal), so that the chain of
-// tile adjoints, which sets the pace of the sweep while the trailing blocks
-// are small, runs on three or four CUs (a one-block kernel doing all four
-// stages took 90 us per tile).  The stream orders the stages, so each reads
-// what the one before wrote.  In stages 0 and 2 a block writes the entries
-// (r, c), c <= r, of its quadrant and their mirrors (c, r): the mirrors of a
-// quadrant below the diagonal land in the skipped one, those of a diagonal
-// quadrant in its own upper part, so no two blocks write the same entry.
-// Only stage 0 reads masked triangles (of the caller's L and Wb); the others
-// read plain whole operands.
+// Each stage is a launch of one block per ADJ_TILE x ADJ_TILE block of its
+// product (stages 0 and 2 skip the blocks above the diagonal), so that the
+// chain of tile adjoints, which sets the pace of the sweep while the trailing
+// blocks are small, is spread over ten to sixteen CUs (a one-block kernel
+// doing all four stages took 90 us per tile; with 64 x 64 blocks a stage took
+// about 10 us, most of it one block's 64-deep share of the matrix cores).
+// The stream orders the stages, so each reads what the one before wrote.  In
+// stages 0 and 2 a block writes the entries (r, c), c <= r, of its block and
+// their mirrors (c, r): the mirrors of a block below the diagonal land in a
+// skipped one, those of a diagonal block in its own upper part, so no two
+// blocks write the same entry.  Only stage 0 reads masked triangles (of the
+// caller's L and Wb); the others read plain whole operands.
+constexpr int ADJ_TILE = 32;
 template <typename T, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_tile_adjoint_stage(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const T *inv, int64_t ldi, T *s1,
@@ -575,7 +577,7 @@ k_tile_adjoint_stage(int kb, const T *L, int64_t ldl, T *Wb, int64_t ldw, const 
 {
     using namespace gemm_detail;
     typedef typename Acc<T>::type acc_t;
-    constexpr int TM = 64, TN = 64;
+    constexpr int TM = ADJ_TILE, TN = ADJ_TILE;
     __builtin_amdgcn_s_setprio(3);
     __shared__ T lds[LDS_ELEMS<T, TM>];
     const int r0 = (int)blockIdx.x * TM, c0 = (int)blockIdx.y * TN;
@@ -647,8 +649,8 @@ static chol_status tile_adjoint_stages(hipStream_t st, int kb, const T *L, int64
                                        const T *inv, int64_t ldi, T *s1, T *s2, int64_t lds_scr, const T *Lnext,
                                        int nj, T *slot, T *sg, int64_t ldsg)
 {
-    const unsigned q = (unsigned)((kb + 63) / 64);
-    const dim3 grid(q, q), grid3(q, (unsigned)((nj + 63) / 64));
+    const unsigned q = (unsigned)((kb + ADJ_TILE - 1) / ADJ_TILE);
+    const dim3 grid(q, q), grid3(q, (unsigned)((nj + ADJ_TILE - 1) / ADJ_TILE));
     hipLaunchKernelGGL((k_tile_adjoint_stage<T, 0>), grid, dim3(256), 0, st, kb, L, ldl, Wb, ldw, inv, ldi, s1, s2,
                        lds_scr, Lnext, nj, slot, sg, ldsg);
     CHOL_LAUNCH_CHECK();

@@ -95,13 +95,14 @@ namespace gemm_detail {
 constexpr int BM = 128;   // the large tile edge (the symmetric operand's diagonal blocks)
 constexpr int NT = 256;
 
-// Chunk geometry of one operand's TE x BK chunk (TE = 128 or 64 rows along
-// m).  An output tile is TM x 128 (TM = 128 or 64): A's chunks have TM rows,
-// B's 128, and the 2 x 2 waves each own TM/2 x 64 of it, an FRM x 4 grid of
-// 16 x 16 MFMA tiles.  (A block always owns whole 128-column spans of its
+// Chunk geometry of one operand's TE x BK chunk (TE = 128, 64 or 32 rows
+// along m).  An output tile is TM x TN (128 x 128, 64 x 128, 64 x 64, or
+// 32 x 32 for the tile-sized products): A's chunks have TM rows, B's TN, and
+// the 2 x 2 waves each own TM/2 x TN/2 of it, an FRM x FRN grid of 16 x 16
+// MFMA tiles.  (A block always owns whole 128-column spans of its
 // rows, so products computed in place over a 128-wide panel stay race-free.)
 template <typename T, int TE = 128> struct Stage {
-    static_assert(TE == 128 || TE == 64, "tile edge 128 or 64");
+    static_assert(TE == 128 || TE == 64 || TE == 32, "tile edge 128, 64 or 32");
     static constexpr int PER = 16 / (int)sizeof(T);   // elements per 16-byte slot
     static constexpr int BK = 8 * PER;                 // chunk depth: 128 bytes of k per m
     static constexpr int TILE = TE * BK;               // elements of one staged operand chunk
@@ -236,17 +237,18 @@ struct Operand {
     __device__ __forceinline__ void stage_elems(int k0, int klim, T *S) const
     {
         constexpr int BK = Stage<T, TS>::BK, GEN = Stage<T, TS>::GEN;
+        constexpr int STEP = GEN < 4 ? GEN : 4;     // a 32-row fp64 chunk has 2 elements per thread
 #pragma unroll 1
-        for (int j0 = 0; j0 < GEN; j0 += 4) {
-            T v[4];
+        for (int j0 = 0; j0 < GEN; j0 += STEP) {
+            T v[STEP];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < STEP; ++j) {
                 const int e = threadIdx.x + NT * (j0 + j);
                 const int m = LAY == LAY_MK ? e / BK : e % TS, k = LAY == LAY_MK ? e % BK : e / TS;
                 v[j] = elem<T, OP>(p, ld, m0 + m, k0 + k, mlim, klim, excl);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < STEP; ++j) {
                 const int e = threadIdx.x + NT * (j0 + j);
                 const int m = LAY == LAY_MK ? e / BK : e % TS, k = LAY == LAY_MK ? e % BK : e / TS;
                 S[lds_index<T, TS>(LAY, m, k)] = v[j];

@@ -368,7 +368,9 @@ static chol_status blocked_potrf_on(int64_t n, const T *A, int64_t lda, T *L, in
             p.b = slot_ptr(o.slot); p.ldb = MAX_TILE;
             p.c = L + r0 * ldl + k0; p.ldc = ldl;
             prof::Scope ps(CHOL_K_PANEL_SOLVE, sx, (double)m * kb * kb);
-            s = gemm<T, OP_MK, OP_MK, C_STORE, 64>(p, 1, sx);
+            // 32-row tiles, each a whole 128-wide row panel (in place): twice
+            // the blocks of 64-row tiles, each half as long a product
+            s = gemm<T, OP_MK, OP_MK, C_STORE, 32>(p, 1, sx);
             break;
         }
         case FWD_UPDATE:
@@ -798,8 +800,9 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                                    kn, kb, 1, (const T *)slot, Wp, ldw);
                 CHOL_LAUNCH_CHECK();
             }
-            // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block;
-            // the stored inverse carries its zeros, so it is a plain operand)
+            // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block,
+            // 32-row tiles; the stored inverse carries its zeros, so it is a
+            // plain operand)
             {
                 GemmArgs<T> p{};
                 p.M = (int)m; p.N = kb; p.K = kb;
@@ -807,7 +810,7 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
                 p.b = invk; p.ldb = nb;
                 p.c = Wp; p.ldc = ldw;
                 prof::Scope ps(CHOL_K_ADJ_PANEL, sp, (double)m * kb * kb);
-                if ((s = gemm<T, OP_MK, OP_KM, C_STORE, 64>(p, 1, sp)) != CHOL_OK)
+                if ((s = gemm<T, OP_MK, OP_KM, C_STORE, 32>(p, 1, sp)) != CHOL_OK)
                     return s;
             }
         }

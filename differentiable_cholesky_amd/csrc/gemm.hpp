@@ -680,9 +680,11 @@ static void launch(void (*kern)(GemmArgs<T>), dim3 grid, hipStream_t st, const G
 }
 } // namespace gemm_detail
 
-// C op= A B on the stream; TM: output tile rows (128, or 64 for short
-// products whose 128 x 128 tiles would be too few, or too long each, to
-// spread over the device; tiles are always 128 columns wide)
+// C op= A B on the stream; TM x TN: output tile (128 x 128; 64 x 128 or
+// 64 x 64 for short products whose 128 x 128 tiles would be too few, or too
+// long each, to spread over the device; 32 x 128 for the in-place panel
+// products, whose blocks must each own whole 128-wide rows; 32 x 32 for
+// tile-sized products)
 template <typename T, int AOP, int BOP, int CM, int TM = 128, int TN = 128>
 static chol_status gemm(GemmArgs<T> p, int splits, hipStream_t st, hipEvent_t ea = nullptr, hipEvent_t eb = nullptr)
 {

@@ -219,40 +219,66 @@ k_splitk_reduce_lower(int n, int splits, const T *part, T *c, int64_t ldc)
         c[(int64_t)r * ldc + col] -= ((sums[0][lane] + sums[1][lane]) + sums[2][lane]) + sums[3][lane];
 }
 
-// C(M x N) -= sum_s part[s] (all entries), part row-major M x N per split
-template <typename T>
-__global__ void __launch_bounds__(256)
-k_splitk_reduce(int M, int N, int splits, const T *part, T *c, int64_t ldc)
-{
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t tot = (int64_t)M * N;
-    if (idx >= tot)
-        return;
-    const int r = (int)(idx / N), col = (int)(idx % N);
-    T s = T(0);
-    for (int q = 0; q < splits; ++q)
-        s += part[(int64_t)q * tot + idx];
-    c[(int64_t)r * ldc + col] -= s;
-}
+// The partial sums a split-contraction product left for its M x N output
+// (C_PARTIAL, row-major M x N per slot): `splits` slots per entry, or with
+// `piece` > 0 the slots of the pieces that touched the entry's 128 x 128 tile
+// (tiles TJ per row of tiles, contraction nku units long, pieces numbered
+// along the tiles' contractions laid end to end); none when part is null.
+template <typename T> struct Partials {
+    const T *part = nullptr;
+    int M = 0, N = 0, splits = 0, TJ = 1;
+    int64_t nku = 0, piece = 0;
+    __host__ __device__ int count(int r, int c) const
+    {
+        if (!part)
+            return 0;
+        if (piece <= 0)
+            return splits;
+        const int64_t t = (int64_t)(r / 128) * TJ + c / 128;
+        return (int)(((t + 1) * nku - 1) / piece - (t * nku) / piece + 1);
+    }
+};
 
-// The sums of a piece-scheduled product (GemmArgs::piece): tile t (128 x 128,
-// TJ per row of tiles) holds one partial per piece that touched it, slots
-// 0 .. count-1 in contraction order, summed in that order into c (c -= sum).
+// C(M x N) -= the sum of the partials (slots in contraction order), then
+// C -= slot in the first kn rows (slot row-major kn x N; null: none): the sums
+// of a split product and of a term computed elsewhere, one pass over C.
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_splitk_reduce_pieces(int M, int N, int TJ, int64_t nku, int64_t piece, const T *part, T *c, int64_t ldc)
+k_splitk_reduce(int M, int N, Partials<T> ps, const T *slot, int kn, T *c, int64_t ldc)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t tot = (int64_t)M * N;
     if (idx >= tot)
         return;
     const int r = (int)(idx / N), col = (int)(idx % N);
-    const int64_t t = (int64_t)(r / 128) * TJ + col / 128;
-    const int cnt = (int)(((t + 1) * nku - 1) / piece - (t * nku) / piece + 1);
+    const int cnt = ps.count(r, col);
     T s = T(0);
     for (int q = 0; q < cnt; ++q)
-        s += part[(int64_t)q * tot + idx];
-    c[(int64_t)r * ldc + col] -= s;
+        s += ps.part[(int64_t)q * tot + idx];
+    T x = c[(int64_t)r * ldc + col] - s;
+    if (slot && r < kn)
+        x -= slot[idx];
+    c[(int64_t)r * ldc + col] = x;
+}
+
+template <typename T>
+static chol_status splitk_reduce(int M, int N, const Partials<T> &ps, const T *slot, int kn, T *c, int64_t ldc,
+                                 hipStream_t st)
+{
+    const int64_t tot = (int64_t)M * N;
+    if (tot <= 0)
+        return CHOL_OK;
+    double slots = ps.part ? ps.splits : 0;
+    if (ps.part && ps.piece > 0) {
+        const int64_t tiles = (int64_t)((M + 127) / 128) * ps.TJ;
+        slots = (double)((tiles * ps.nku + ps.piece - 1) / ps.piece) / tiles + 1;
+    }
+    const double sbytes = slot ? (double)kn * N * sizeof(T) : 0.0;
+    prof::Scope pscope(CHOL_K_REDUCE, st, (double)tot * (slots + 2) * sizeof(T) + sbytes);
+    hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N, ps, slot,
+                       kn, c, ldc);
+    CHOL_LAUNCH_CHECK();
+    return CHOL_OK;
 }
 
 // contraction length per split: a whole number of fp32 chunks (32), which is
@@ -459,7 +485,7 @@ size_t blocked_adjoint_workspace(int64_t n, int nb, size_t esize, bool need_wb, 
 template <typename T>
 static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, const T *B, int64_t ldb, T *C,
                                int64_t ldc, int excl, const T *dg, T *part, int max_splits, int min_chunk,
-                               int *sched, int cap, double flops, hipStream_t st)
+                               int *sched, int cap, double flops, hipStream_t st, Partials<T> *defer = nullptr)
 {
     if (M <= 0 || N <= 0 || K <= 0)
         return CHOL_OK;
@@ -524,19 +550,21 @@ static chol_status sym_product(int M, int N, int K, const T *S, int64_t lds, con
         if (s != CHOL_OK)
             return s;
     }
-    const int64_t tot = (int64_t)M * N;
-    if (piece > 0) {
-        const double slots = (double)((W + piece - 1) / piece) / tiles + 1;
-        prof::Scope ps(CHOL_K_REDUCE, st, (double)tot * (slots + 2) * sizeof(T));
-        hipLaunchKernelGGL((k_splitk_reduce_pieces<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N,
-                           (N + 127) / 128, nku, piece, (const T *)part, C, ldc);
-    } else {
-        prof::Scope ps(CHOL_K_REDUCE, st, (double)tot * (used + 2) * sizeof(T));
-        hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, M, N,
-                           used, (const T *)part, C, ldc);
+    Partials<T> ps;
+    ps.part = part;
+    ps.M = M;
+    ps.N = N;
+    ps.splits = used;
+    ps.TJ = (N + 127) / 128;
+    ps.nku = nku;
+    ps.piece = piece;
+    // C -= the sum of the partials, now or (defer) by the caller's next pass
+    // over C
+    if (defer) {
+        *defer = ps;
+        return CHOL_OK;
     }
-    CHOL_LAUNCH_CHECK();
-    return CHOL_OK;
+    return splitk_reduce<T>(M, N, ps, (const T *)nullptr, 0, C, ldc, st);
 }
 
 template <typename T>
@@ -748,6 +776,9 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
 
     // tile columns [add_lo, add_hi) are final and not yet added into adj_A
     int64_t add_lo = K, add_hi = K;
+    // partials of the last symmetric product not yet summed into the next
+    // tile column's panel
+    Partials<T> pend{};
     auto add_columns = [&](int64_t lo, int64_t hi) {
         const int64_t c0 = lo * nb;
         return tri_op<T, TRI_ADD_LOWER>(n - c0, Wb + c0 * ldw + c0, ldw, adjA + c0 * ldaa + c0, ldaa, sc,
@@ -792,14 +823,16 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         }
         if (m > 0) {
             // the second term of this tile column lands in the first kn rows
-            // of Wb_panel
-            {
-                const int64_t tot = (int64_t)kn * kb;
-                prof::Scope ps(CHOL_K_REDUCE, sp, 3.0 * tot * sizeof(T));
-                hipLaunchKernelGGL((k_splitk_reduce<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, sp,
-                                   kn, kb, 1, (const T *)slot, Wp, ldw);
-                CHOL_LAUNCH_CHECK();
+            // of Wb_panel, in the same pass as the sum of the first term's
+            // partials when the symmetric product left it (where this tile
+            // column's panel adjoint runs on sx, right after that product)
+            if (pend.part) {
+                if ((s = splitk_reduce<T>((int)m, kb, pend, (const T *)slot, kn, Wp, ldw, sp)) != CHOL_OK)
+                    return s;
+            } else if ((s = splitk_reduce<T>(kn, kb, Partials<T>{}, (const T *)slot, kn, Wp, ldw, sp)) != CHOL_OK) {
+                return s;
             }
+            pend = Partials<T>{};
             // R2a: X = Wb_panel L_kk^{-1} (in place, full panel width per block,
             // 32-row tiles; the stored inverse carries its zeros, so it is a
             // plain operand)
@@ -878,9 +911,12 @@ static chol_status blocked_adjoint_on(int64_t n, const T *L, int64_t ldl, const 
         if (k >= 1 && m > 0) {
             const double flops = 2.0 * nb * ((double)(m + kb) * (m + kb) - (double)kb * kb);
             const T *dg = dense ? dense + k * nb * nb : nullptr;   // diagonal tiles from tile k on
+            // the sum of its partials waits for tile column k-1's second term
+            // where that column's panel adjoint runs on sx
+            const bool next_on_chain = m + nb <= ADJ_CHAIN_PANEL_ROWS;
             if ((s = sym_product<T>((int)(m + kb), nb, (int)(m + kb), Wkk, ldw, L + k0 * ldl + j0, ldl,
                                     Wb + k0 * ldw + j0, ldw, kb, dg, part_x, max_splits, 128, sched_x,
-                                    cap_x, flops, sx)) != CHOL_OK)
+                                    cap_x, flops, sx, next_on_chain ? nullptr : &pend)) != CHOL_OK)
                 return s;
         }
     }

@@ -54,7 +54,7 @@ FAMILIES = ["small_factor", "small_adjoint", "diag_factor", "diag_inverse", "pan
 BYTE_FAMILIES = {"small_factor", "small_adjoint", "elementwise", "reduce"}
 # the kernel each matrix-core family launches (names as rocprofv3 lists them)
 FAMILY_KERNEL = {"trailing_update": "k_gemm<double, 0, 0, 1, 1, 128, 128>", "adj_trailing": "k_gemm<double, 4, 1, 3, 0, 128, 128>",
-                 "panel_solve": "k_gemm<double, 0, 0, 2, 0, 64, 128>", "adj_panel": "k_gemm<double, 0, 1, 2, 0, 64, 128>",
+                 "panel_solve": "k_gemm<double, 0, 0, 2, 0, 32, 128>", "adj_panel": "k_gemm<double, 0, 1, 2, 0, 32, 128>",
                  "adj_diag_update": "k_gemm<double, 1, 1, 3, 0, 128, 128>", "adj_diag": "k_tile_adjoint_stage<double, 0..3>"}
 
 
